@@ -1,0 +1,160 @@
+"""Plain fp64 CPU oracle for the exact scaled-dot-product attention forward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links this
+module; only the tests, the smoke check and the CPU-baseline leg of the benchmark do.
+It shares no code, constants or helpers with the HIP library.
+
+What it computes is the definition stated on the page "编译器与内核" (Compilers and
+kernels), section "FlashAttention 围绕 IO 改写算法", first display equation and the
+symbol list under it:
+
+    S = Q K^T / sqrt(d) + C,   m_i = max_j S_ij,   l_i = sum_j exp(S_ij - m_i),
+    P_ij = exp(S_ij - m_i) / l_i,   O = P V,
+
+with Q, K in R^{N x d}, V in R^{N x d_v}, C in (R u {-inf})^{N x N} an additive bias
+or mask where -inf forbids a key, and every query row having at least one allowed key.
+The same page states that the tiled method computes the same mathematical function
+(not the same bits), so the oracle is the definition itself: it materialises S and P
+in float64 and never tiles keys.
+
+Readings taken where the page is silent (each is listed in the design notes):
+  * log-sum-exp: lse_i = m_i + ln(l_i) = ln sum_j exp(S_ij), natural log, over the
+    scaled and biased scores;
+  * d (the Q/K width) sets the scale even when d != d_v;
+  * C is added after scaling and is not itself scaled;
+  * causal means C_ij = -inf for j > i (top-left aligned, square N x N), and a bias
+    and the causal mask add;
+  * a bias tensor may broadcast over batch (stride 0) or over heads;
+  * a row with no allowed key violates the page's precondition; by default the oracle
+    raises, and with ``allow_empty_rows=True`` it returns the convention O = 0,
+    lse = -inf for that row (this convention is not fixed by the page: parity
+    unpinned for that row).
+
+Inputs are taken exactly as the GPU saw them (bf16 or fp32 values) and upcast to
+float64; upcasting bf16 or fp32 to float64 is exact.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = ["sdpa_reference", "sdpa_reference_rows", "EmptyRowError"]
+
+
+class EmptyRowError(ValueError):
+    """A query row has no allowed key (the definition assumes at least one)."""
+
+
+def _as_f64(x) -> np.ndarray:
+    # torch tensors (any dtype, incl. bfloat16) and numpy arrays are both accepted;
+    # a bf16 torch tensor is first widened to fp32 (exact), then to fp64 (exact).
+    if hasattr(x, "detach"):
+        t = x.detach().cpu()
+        if str(t.dtype) in ("torch.bfloat16", "torch.float16"):
+            t = t.float()
+        x = t.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _row_block(qbh, kbh, vbh, c_rows, rows, causal, scale, allow_empty_rows):
+    """Rows `rows` of one (batch, head): the definition, written out in float64.
+
+    c_rows is None or the bias rows already selected ([len(rows), N]).
+    """
+    # S = Q K^T / sqrt(d) + C  (C = bias + causal mask)
+    s = (qbh[rows] @ kbh.T) * scale
+    if c_rows is not None:
+        s = s + c_rows
+    if causal:
+        keys = np.arange(kbh.shape[0])[None, :]
+        s = np.where(keys > rows[:, None], -np.inf, s)
+    # m_i = max_j S_ij
+    m = s.max(axis=1)
+    empty = ~np.isfinite(m) & (m < 0)
+    if empty.any() and not allow_empty_rows:
+        raise EmptyRowError(f"{int(empty.sum())} query row(s) have no allowed key")
+    m_safe = np.where(empty, 0.0, m)
+    # exp(S_ij - m_i), with exp(-inf) = 0
+    e = np.exp(s - m_safe[:, None])
+    # l_i = sum_j exp(S_ij - m_i)
+    ell = e.sum(axis=1)
+    ell_safe = np.where(empty, 1.0, ell)
+    # P_ij = exp(S_ij - m_i) / l_i ;  O = P V
+    p = e / ell_safe[:, None]
+    o = p @ vbh
+    lse = m_safe + np.log(ell_safe)
+    o[empty] = 0.0
+    lse[empty] = -np.inf
+    return o, lse
+
+
+def _bias_slice(bias, b, h):
+    if bias is None:
+        return None
+    # bias broadcasts to [B, H, N, N]
+    bb = bias.shape[0]
+    bh = bias.shape[1]
+    return bias[b if bb > 1 else 0, h if bh > 1 else 0]
+
+
+def sdpa_reference(q, k, v, bias=None, causal=False, *, row_chunk=2048,
+                   allow_empty_rows=False):
+    """Exact attention forward of every (batch, head) in float64.
+
+    q: [B, H, N, d], k: [B, H, N, d], v: [B, H, N, dv] (logical layout; any real
+    dtype, torch or numpy). bias: None or [Bb, Hb, N, N] with Bb in {1, B} and
+    Hb in {1, H}; -inf entries forbid keys. causal: add -inf above the diagonal.
+    Returns (O [B, H, N, dv], lse [B, H, N]) as float64 numpy arrays.
+    Query rows are processed in chunks of `row_chunk`; rows are independent in the
+    definition, so chunking rows changes nothing.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    bias = None if bias is None else _as_f64(bias)
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    if k.shape != (B, H, N, d) or v.shape != (B, H, N, dv):
+        raise ValueError("q, k, v shapes disagree")
+    if bias is not None and (bias.ndim != 4 or bias.shape[2:] != (N, N)
+                             or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H)):
+        raise ValueError("bias must broadcast to [B, H, N, N]")
+    scale = 1.0 / math.sqrt(d)
+    out = np.empty((B, H, N, dv), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            cbh = _bias_slice(bias, b, h)
+            for r0 in range(0, N, row_chunk):
+                rows = np.arange(r0, min(N, r0 + row_chunk))
+                c_rows = None if cbh is None else cbh[rows]
+                o_, l_ = _row_block(q[b, h], k[b, h], v[b, h], c_rows, rows, causal,
+                                    scale, allow_empty_rows)
+                out[b, h, rows] = o_
+                lse[b, h, rows] = l_
+    return out, lse
+
+
+def sdpa_reference_rows(q, k, v, bias, causal, b, h, rows, *, allow_empty_rows=False):
+    """The same definition for selected query rows of one (batch, head).
+
+    Used at sizes where the full N x N problem is too large for the CPU: each
+    sampled row is computed on its own, exactly as in `sdpa_reference`.
+    q, k, v are [B, H, N, *] (torch or numpy, any layout; only the needed slices are
+    converted); bias as in `sdpa_reference`. Returns (O [len(rows), dv], lse [len(rows)]).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    qbh = _as_f64(q[b, h])
+    kbh = _as_f64(k[b, h])
+    vbh = _as_f64(v[b, h])
+    d = qbh.shape[-1]
+    c_rows = None
+    if bias is not None:
+        bb = bias.shape[0]
+        bh = bias.shape[1]
+        sl = bias[b if bb > 1 else 0, h if bh > 1 else 0]
+        c_rows = _as_f64(sl[rows.tolist()])
+    return _row_block(qbh, kbh, vbh, c_rows, rows, causal, 1.0 / math.sqrt(d),
+                      allow_empty_rows)

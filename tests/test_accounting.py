@@ -1,0 +1,51 @@
+"""Pins for the benchmark's FLOP/byte accounting against the pages' printed figures."""
+
+import json
+import os
+
+import pytest
+
+from exact_attention_35_amd import roofline as rf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_single_head_8192_traffic_matches_page():
+    g = json.load(open(os.path.join(GOLDEN, "traffic_single_head_8192.json")))
+    B, H, N, d, dv = g["B"], g["H"], g["N"], g["d"], g["dv"]
+    e = g["qkvo_elem_bytes"]
+    assert B * H * N * d * e == g["each_of_q_k_v_o_bytes"]
+    assert N * N * g["sp_elem_bytes"] == g["each_of_s_p_bytes"]
+    required = rf.min_bytes(B, H, N, d, dv, e, lse_bytes=0)
+    assert required == g["required_bytes"]
+    sp = rf.materialised_sp_bytes(B, H, N, g["sp_elem_bytes"])
+    assert sp == g["materialised_sp_traffic_bytes"]
+    assert sp // required == g["ratio_to_required"]
+
+
+def test_ridge_points_match_page():
+    g = json.load(open(os.path.join(GOLDEN, "ridge_points.json")))
+    a = g["a100"]
+    assert rf.ridge(a["p_max_flops"], a["b_max_bytes_per_s"]) == a["ridge_flop_per_byte"]
+    h = g["h100_block"]
+    # copy/compute time ratio of a block of intensity I on a machine with ridge R is R/I
+    assert abs(h["ridge_flop_per_byte"] / h["flop_per_byte"] - h["copy_over_compute"]) < 0.05
+    assert abs(h["copy_us"] / h["compute_us"] - h["copy_over_compute"]) < 0.05
+
+
+def test_alg_flops_causal_and_dense():
+    # causal N=8192, d=dv=128: 2*(d+dv)*N(N+1)/2
+    assert rf.alg_flops(1, 1, 8192, 128, 128, True) == 17_181_966_336
+    assert rf.alg_flops(2, 16, 2048, 64, 128, False) == 51_539_607_552
+    assert rf.alg_flops(1, 1, 256, 64, 64, False) == 16_777_216
+    # brute count of allowed pairs for a small causal mask
+    n = 13
+    assert rf.allowed_pairs(n, True) == sum(1 for i in range(n) for j in range(n) if j <= i)
+
+
+def test_roofline_bound_two_regimes():
+    p, b = 2.5e15, 8e12
+    attain, t, which = rf.roofline_bound(1e12, 1e9, p, b)      # I = 1000 > ridge 312.5
+    assert which == "compute" and attain == p and t == pytest.approx(1e12 / p)
+    attain, t, which = rf.roofline_bound(1e11, 1e9, p, b)      # I = 100 < ridge
+    assert which == "memory" and attain == pytest.approx(b * 100) and t == pytest.approx(1e9 / b)
