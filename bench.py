@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward on one MI355X.
+
+A step is one fa_fwd call over the headline workload: one bf16 head, N = 8192,
+d = dv = 128, causal (the single-head L = 8192 example of the page
+"AI Infra 第5章图解: 算子与运行时", section "FlashAttention: Softmax 也能逐块算").
+Inputs are drawn once and resident in HBM before timing starts.
+
+Printed: one JSON line with the throughput in algorithmic TFLOP/s
+(2*(d+dv) per allowed query/key pair, softmax not counted), the roofline of the
+dominant kernel (its average launch duration measured with HIP events on the stream
+it is launched on), and the CPU oracle timed on this host as a reported baseline.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+  python bench.py --copy-probe      # plain copy kernel of known size (counter calibration)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s at N=8192,d=128 bf16 causal; % of MI355X MFMA peak"
+DEFAULT_WORKLOAD = "bf16_causal_single_head_n8192_d128"
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_35_amd", "csrc", "fa_fwd_mfma.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"traffic_fwd_mfma_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(steps: int) -> None:
+    """A plain device copy of 256 MiB, `steps` times (for FETCH_SIZE/WRITE_SIZE scale)."""
+    import torch
+
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "steps": steps}))
+
+
+def cpu_baseline(w, inp):
+    """Time the fp64 oracle once over the whole workload on this host's cores."""
+    import numpy as np  # noqa: F401
+
+    from exact_attention_35_amd import roofline as rf
+    from oracle import sdpa_reference
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
+    dt = time.perf_counter() - t0
+    flops = rf.alg_flops(w.B, w.H, w.N, w.d, w.dv, w.causal)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole workload ({w.name}), one call, fp64 numpy, {dt:.2f} s",
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported; this path has no multi-GPU mode", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_probe:
+        copy_probe(args.steps)
+        return 0
+
+    from exact_attention_35_amd import capi, roofline as rf, workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = workloads.make_inputs(w, device="cpu")
+    gpu = {}
+    for n, t in inp.items():
+        if t is None:
+            gpu[n] = None
+        elif w.layout == "bnhd" and n in ("q", "k", "v"):
+            gpu[n] = t.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+        else:
+            gpu[n] = t.to(dev)
+    out = torch.empty(w.B, w.H, w.N, w.dv, dtype=gpu["q"].dtype, device=dev)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+
+    def step():
+        capi.fa_fwd(gpu["q"], gpu["k"], gpu["v"], bias=gpu["bias"], causal=w.causal, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)   # fa_fwd launches on this stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_launch_s = sum(per_launch_ms) / len(per_launch_ms) / 1e3
+    med_launch_s = per_launch_ms[len(per_launch_ms) // 2] / 1e3
+
+    flops = rf.alg_flops(w.B, w.H, w.N, w.d, w.dv, w.causal)
+    elem = 2 if w.dtype == "bf16" else 4
+    bias_bytes = (w.H * w.N * w.N * 4) if w.bias else 0
+    min_b = rf.min_bytes(w.B, w.H, w.N, w.d, w.dv, elem, bias_bytes=bias_bytes)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / avg_launch_s / 1e12
+    if w.dtype == "bf16":
+        peak, bound = rf.MI355X_PEAK_BF16_FLOPS / 1e12, "mfma"
+    else:
+        peak, bound = rf.MI355X_PEAK_F32_FLOPS / 1e12, "mfma"
+    if w.bias:  # the bias stream makes this workload memory-bound at I = F/Q
+        attain, _, which = rf.roofline_bound(flops, min_b, peak * 1e12, rf.MI355X_HBM_BYTES_PER_S)
+        if which == "memory":
+            bound = "hbm"
+    traffic = read_traffic(w.name)
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": min_b / avg_launch_s / 1e9, "peak": 8000.0,
+                "unit": "GB/s", "frac": min_b / avg_launch_s / 8e12, "traffic": traffic}
+    else:
+        roof = {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": traffic}
+    roof.update({"kernel": "fwd_mfma" if w.dtype == "bf16" else "fwd_generic",
+                 "avg_launch_us": avg_launch_s * 1e6, "median_launch_us": med_launch_s * 1e6,
+                 "alg_flops_per_launch": flops, "min_bytes_per_launch": min_b,
+                 "kernel_source_sha256_16": kernel_sha()})
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv,
+                   "causal": w.causal, "bias": w.bias, "layout": w.layout,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": 100.0 * value / (rf.MI355X_PEAK_BF16_FLOPS / 1e12),
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,214 @@
+"""Thin Python binding of the C ABI in include/fa.h (argument marshalling only).
+
+Every function here has the name of the C entry point it wraps. Tensors are torch
+tensors in logical [B, H, N, *] layout with any strides whose innermost axis is
+contiguous; pointers, element strides and torch's current HIP stream are passed
+through unchanged. All arithmetic runs in libfa.so's HIP kernels; if the library is
+not built, every call raises — there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "FaError", "FA_OK", "FA_F32", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
+    "STATUS", "lib", "library_path", "fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size",
+    "fa_workspace_init", "fa_workspace_counter_bytes", "fa_status_string", "fa_version",
+    "fa_shutdown", "make_strides", "FaStrides", "EXPORTED",
+]
+
+FA_OK = 0
+FA_F32 = 0
+FA_BF16 = 1
+FA_MASK_NONE = 0
+FA_MASK_CAUSAL = 1
+STATUS = {
+    "FA_OK": 0, "FA_ERR_NULL": -1, "FA_ERR_SHAPE": -2, "FA_ERR_DTYPE": -3,
+    "FA_ERR_MASK": -4, "FA_ERR_STRIDE": -5, "FA_ERR_ALIGN": -6, "FA_ERR_ALIAS": -7,
+    "FA_ERR_WORKSPACE": -8, "FA_ERR_LAUNCH": -9, "FA_ERR_DEVICE": -10, "FA_ERR_ALLOC": -11,
+}
+
+# every symbol include/fa.h declares
+EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_workspace_init",
+            "fa_workspace_counter_bytes", "fa_status_string", "fa_version", "fa_shutdown")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fa status {status}: {message}")
+        self.status = status
+
+
+class FaStrides(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_int64 * 3), ("k", ctypes.c_int64 * 3), ("v", ctypes.c_int64 * 3),
+                ("out", ctypes.c_int64 * 3), ("bias", ctypes.c_int64 * 3),
+                ("lse", ctypes.c_int64 * 2)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libfa.so (once). Raises if it is missing: the HIP library is the only path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run exact_attention_35_amd.build.build() "
+                           "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(path)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    fwd_args = [vp, vp, vp, vp, ctypes.c_int, vp, vp, i64, i64, i64, i64, i64,
+                ctypes.POINTER(FaStrides), ctypes.c_int, vp]
+    L.fa_fwd.argtypes = fwd_args
+    L.fa_fwd.restype = ctypes.c_int
+    L.fa_fwd_ex.argtypes = fwd_args + [vp, sz]
+    L.fa_fwd_ex.restype = ctypes.c_int
+    L.fa_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    L.fa_fwd_workspace_size.restype = sz
+    L.fa_workspace_init.argtypes = [vp, sz, vp]
+    L.fa_workspace_init.restype = ctypes.c_int
+    L.fa_workspace_counter_bytes.argtypes = []
+    L.fa_workspace_counter_bytes.restype = sz
+    L.fa_status_string.argtypes = [ctypes.c_int]
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_version.argtypes = []
+    L.fa_version.restype = ctypes.c_int
+    L.fa_shutdown.argtypes = []
+    L.fa_shutdown.restype = None
+    _lib = L
+    return L
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def fa_version() -> int:
+    return int(lib().fa_version())
+
+
+def fa_shutdown() -> None:
+    lib().fa_shutdown()
+
+
+def fa_workspace_counter_bytes() -> int:
+    return int(lib().fa_workspace_counter_bytes())
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        raise FaError(status, fa_status_string(status))
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise FaError(STATUS["FA_ERR_DTYPE"], f"unsupported dtype {t.dtype}")
+
+
+def make_strides(q, k, v, out, bias=None, lse=None) -> FaStrides:
+    s = FaStrides()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        st = t.stride()
+        getattr(s, name)[:] = [st[0], st[1], st[2]]
+    if bias is not None:
+        st = bias.stride()
+        s.bias[:] = [st[0], st[1], st[2]]
+    if lse is not None:
+        st = lse.stride()
+        s.lse[:] = [st[0], st[1]]
+    return s
+
+
+def _prepare(q, k, v, bias, causal, out, lse):
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise FaError(STATUS["FA_ERR_SHAPE"], "q, k, v must be 4-D [B, H, N, *]")
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape[:3]) != (B, H, N):
+        raise FaError(STATUS["FA_ERR_SHAPE"], "q, k, v shapes disagree")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise FaError(STATUS["FA_ERR_DTYPE"], "q, k, v dtypes differ")
+    for t in (q, k, v):
+        if t.numel() and t.stride(-1) != 1:
+            raise FaError(STATUS["FA_ERR_STRIDE"], "innermost axis must be contiguous")
+    if bias is not None:
+        if bias.dtype != torch.float32:
+            raise FaError(STATUS["FA_ERR_DTYPE"], "bias must be float32")
+        if bias.dim() == 3:
+            bias = bias.unsqueeze(0)
+        bias = bias.expand(B, H, N, N)
+        if N and bias.stride(-1) != 1:
+            raise FaError(STATUS["FA_ERR_STRIDE"], "bias key axis must be contiguous")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    mask = FA_MASK_CAUSAL if causal else FA_MASK_NONE
+    strides = make_strides(q, k, v, out, bias, lse)
+    return (B, H, N, d, dv, dt, mask, bias, out, lse, strides)
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def fa_fwd(q, k, v, bias=None, causal=False, out=None, lse=None, stream=None):
+    """Attention forward through fa_fwd. Returns (out, lse).
+
+    q, k: [B, H, N, d]; v: [B, H, N, dv]; bf16 or fp32 (same dtype), on one HIP device.
+    bias: None or fp32 broadcastable to [B, H, N, N] (as [B|1, H|1, N, N] or [H, N, N]).
+    out / lse are allocated when not given. Enqueued on `stream` (default: torch's
+    current stream); no synchronisation.
+    """
+    B, H, N, d, dv, dt, mask, bias, out, lse, strides = _prepare(q, k, v, bias, causal, out, lse)
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), mask, _ptr(out), _ptr(lse),
+                      B, H, N, d, dv, ctypes.byref(strides), dt, _stream_handle(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def fa_fwd_workspace_size(B, H, N, d, dv, dtype_code, causal) -> int:
+    return int(lib().fa_fwd_workspace_size(B, H, N, d, dv, dtype_code,
+                                           FA_MASK_CAUSAL if causal else FA_MASK_NONE))
+
+
+def fa_workspace_init(workspace, stream=None) -> None:
+    _check(lib().fa_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream_handle(stream, workspace.device)))
+
+
+def fa_fwd_ex(q, k, v, workspace, bias=None, causal=False, out=None, lse=None, stream=None):
+    """fa_fwd with a caller-provided workspace (a uint8 device tensor, or None)."""
+    B, H, N, d, dv, dt, mask, bias, out, lse, strides = _prepare(q, k, v, bias, causal, out, lse)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), mask, _ptr(out), _ptr(lse),
+                         B, H, N, d, dv, ctypes.byref(strides), dt,
+                         _stream_handle(stream, q.device), _ptr(workspace), nbytes)
+    _check(st)
+    return out, lse

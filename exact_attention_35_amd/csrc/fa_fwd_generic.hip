@@ -1,0 +1,177 @@
+// General attention-forward kernel on the vector ALUs (fp32 and bf16 inputs).
+//
+// It applies the online-softmax recurrence of the page "编译器与内核" (Compilers and
+// kernels), section "FlashAttention 围绕 IO 改写算法", one key block at a time: a
+// workgroup owns 64 query rows; each key block of 32 keys is staged in LDS (converted
+// to fp32), the 32 scores of a row are formed, then the block max b_t, the new
+// running max m_t, the rescale alpha_t = exp(m_{t-1} - m_t), the normaliser l_t and the
+// numerator o_t are updated, and O_i = o_T / l_T is written at the end.
+//
+// Exponentials are taken in base 2: scores are carried as S * log2(e) (the factor is
+// folded into the 1/sqrt(d) scale, and the bias is multiplied by log2(e)), so
+// exp(S - m) = exp2(S*log2e - m*log2e). The hardware v_exp_f32 / v_log_f32
+// instructions supply exp2 and log2.
+//
+// Four lanes share one query row: lane `sub` owns the dims sub, sub+4, sub+8, ... of
+// q and of o, so the four lanes of a row read consecutive LDS words (no bank
+// conflict) and every row of the workgroup reads the same key (an LDS broadcast).
+// This kernel serves the fp32 path, where the problem sizes are small; the bf16 fast
+// path runs on the matrix cores (fa_fwd_mfma.hip).
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }  // RNE
+
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(256) void fwd_generic(Params p) {
+  constexpr int BM = kGenericBM;  // query rows per workgroup
+  constexpr int BK = 32;          // keys per block
+  constexpr int LPR = 4;          // lanes per query row
+  constexpr int DQ = D / LPR;
+  constexpr int DO = DV / LPR;
+  __shared__ float Ks[BK][D];
+  __shared__ float Vs[BK][DV];
+
+  const int tid = threadIdx.x;
+  const int row = tid / LPR;
+  const int sub = tid % LPR;
+  // 1-D grid: block = (b*h) * n_qt + query tile
+  const int n_qt = (p.N + BM - 1) / BM;
+  const int bh = blockIdx.x / n_qt;
+  const int b = bh / p.H;
+  const int h = bh % p.H;
+  const int q0 = (blockIdx.x % n_qt) * BM;
+  const int qi = q0 + row;
+  const bool qvalid = qi < p.N;
+
+  const T* qp = static_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const T* kp = static_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh;
+  const T* vp = static_cast<const T*>(p.v) + b * p.v_sb + h * p.v_sh;
+  const float* bp = p.bias ? p.bias + b * p.b_sb + h * p.b_sh + (int64_t)(qvalid ? qi : 0) * p.b_si
+                           : nullptr;
+
+  float qr[DQ];
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) qr[i] = qvalid ? to_f32<T>(qp[(int64_t)qi * p.q_sn + sub + LPR * i]) : 0.f;
+
+  float o[DO];
+#pragma unroll
+  for (int i = 0; i < DO; ++i) o[i] = 0.f;
+  float m = -INFINITY;  // running max, base-2 units
+  float l = 0.f;        // running normaliser
+
+  const int kv_end = p.causal ? min(p.N, q0 + BM) : p.N;
+  for (int kv0 = 0; kv0 < kv_end; kv0 += BK) {
+    __syncthreads();  // previous block fully consumed
+    for (int idx = tid; idx < BK * D; idx += 256) {
+      const int r = idx / D, c = idx % D;
+      const int key = kv0 + r;
+      Ks[r][c] = key < p.N ? to_f32<T>(kp[(int64_t)key * p.k_sn + c]) : 0.f;
+    }
+    for (int idx = tid; idx < BK * DV; idx += 256) {
+      const int r = idx / DV, c = idx % DV;
+      const int key = kv0 + r;
+      Vs[r][c] = key < p.N ? to_f32<T>(vp[(int64_t)key * p.v_sn + c]) : 0.f;
+    }
+    __syncthreads();
+
+    // scores of this block (base 2) and the block max b_t
+    float s[BK];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < BK; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) acc = fmaf(qr[i], Ks[j][sub + LPR * i], acc);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      const int key = kv0 + j;
+      float x = acc * p.scale_log2;
+      if (bp && key < p.N && qvalid) x = fmaf(bp[key], kLog2e, x);
+      if (key >= p.N || (p.causal && key > qi)) x = -INFINITY;
+      s[j] = x;
+      bmax = fmaxf(bmax, x);
+    }
+    // m_t = max(m_{t-1}, b_t); while no allowed key has been seen (m_t = -inf) the
+    // block adds nothing: using 0 as the reference keeps exp2 away from -inf - -inf.
+    const float m_new = fmaxf(m, bmax);
+    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < BK; ++j) {
+      s[j] = __builtin_amdgcn_exp2f(s[j] - m_ref);
+      psum += s[j];
+    }
+    l = alpha * l + psum;
+#pragma unroll
+    for (int i = 0; i < DO; ++i) {
+      float acc = alpha * o[i];
+#pragma unroll
+      for (int j = 0; j < BK; ++j) acc = fmaf(s[j], Vs[j][sub + LPR * i], acc);
+      o[i] = acc;
+    }
+    m = m_new;
+  }
+
+  if (!qvalid) return;
+  T* op = static_cast<T*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qi * p.o_sn;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int i = 0; i < DO; ++i) op[sub + LPR * i] = from_f32<T>(o[i] * inv);
+  if (p.lse && sub == 0) {
+    p.lse[b * p.l_sb + h * p.l_sh + qi] =
+        l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const Params& p, hipStream_t stream) {
+  dim3 grid((unsigned)(((p.N + kGenericBM - 1) / kGenericBM) * (int64_t)p.B * p.H));
+  dim3 block(256);
+  if (p.d == 64 && p.dv == 64) hipLaunchKernelGGL((fwd_generic<T, 64, 64>), grid, block, 0, stream, p);
+  else if (p.d == 64 && p.dv == 128) hipLaunchKernelGGL((fwd_generic<T, 64, 128>), grid, block, 0, stream, p);
+  else if (p.d == 128 && p.dv == 64) hipLaunchKernelGGL((fwd_generic<T, 128, 64>), grid, block, 0, stream, p);
+  else if (p.d == 128 && p.dv == 128) hipLaunchKernelGGL((fwd_generic<T, 128, 128>), grid, block, 0, stream, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_u32(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_generic(const Params& p, bool is_bf16, hipStream_t stream) {
+  return is_bf16 ? launch_t<__bf16>(p, stream) : launch_t<float>(p, stream);
+}
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  hipLaunchKernelGGL(fill_zero_u32, dim3(blocks), dim3(256), 0, stream, static_cast<uint32_t*>(ptr), n);
+  return hipGetLastError();
+}
+
+}  // namespace fa

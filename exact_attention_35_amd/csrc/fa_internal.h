@@ -1,0 +1,48 @@
+// Internal interface between the host dispatcher (fa_api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Everything a forward kernel needs, passed by value as the kernel argument.
+// Strides are in elements; the innermost axis of every tensor is contiguous.
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* bias;  // nullptr: no bias
+  void* out;
+  float* lse;         // nullptr: lse not written
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t b_sb, b_sh, b_si;
+  int64_t l_sb, l_sh;
+  int B, H, N, d, dv;
+  int causal;
+  int bias_vec4;      // bias base 16-byte aligned and row stride a multiple of 4
+  float scale_log2;   // log2(e) / sqrt(d): scores in base-2 units
+  // Work decomposition. A unit is (batch*head, query tile, key split).
+  int n_qt;           // query tiles per (b, h)
+  int n_split;        // key splits per query tile (1: no split, no workspace)
+  // Scratch for split problems (see fa_api.cpp for the layout).
+  unsigned* counters; // one arrival counter per (b*h, query tile)
+  float* part_o;      // [unit][BM][dv] unnormalised numerators
+  float* part_ml;     // [unit][2][BM]  running max (base 2) and normaliser
+};
+
+// Query-tile height of the matrix-core kernel, and the key-tile width.
+constexpr int kMfmaBM = 128;
+constexpr int kMfmaBN = 64;
+// Query-tile height of the general (vector ALU) kernel.
+constexpr int kGenericBM = 64;
+
+// Launchers (each returns the hipError_t of the launch).
+hipError_t launch_mfma_bf16(const Params& p, int grid, hipStream_t stream);
+hipError_t launch_generic(const Params& p, bool is_bf16, hipStream_t stream);
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,155 @@
+/*
+ * fa.h — C ABI of the exact scaled-dot-product attention forward for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation is the one defined on the page "编译器与内核" (Compilers and
+ * kernels), section "FlashAttention 围绕 IO 改写算法", first display equation: for
+ * every batch b and head h,
+ *
+ *     S = Q K^T / sqrt(d) + C,    P = row-softmax(S),    O = P V,
+ *
+ * with Q, K of shape N x d, V of shape N x dv, and C an additive bias/mask in which
+ * -inf forbids a key. The library evaluates it with the online-softmax recurrence
+ * of the same section (running max m_t, rescale alpha_t = exp(m_{t-1} - m_t),
+ * running normaliser l_t and numerator o_t, O_i = o_T / l_T), so the N x N score and
+ * probability matrices never reach device memory. It also returns the per-row
+ * log-sum-exp  lse_i = m_i + ln(l_i) = ln sum_j exp(S_ij)  (natural log).
+ *
+ * C is the sum of (a) the optional fp32 bias tensor and (b) the causal mask
+ * (C_ij = -inf for key j > query i, square N x N, top-left aligned) when
+ * mask_mode == FA_MASK_CAUSAL. The scale is 1/sqrt(d) with d the Q/K width, also
+ * when d != dv. The bias is added after scaling and is not scaled.
+ *
+ * The page assumes every query row has at least one allowed key. For a row that has
+ * none, this library writes O = 0 and lse = -inf (a convention of this library).
+ *
+ * Numerics: bf16 inputs are multiplied on the matrix cores with fp32 accumulation;
+ * probabilities are rounded to bf16 before the P V product and the normaliser sums
+ * the rounded values; O is rounded to the output dtype once (round to nearest even).
+ * fp32 inputs are computed in fp32 throughout. Results equal the definition up to
+ * rounding ("exact" means the same function, not the same bits). For a fixed build,
+ * device, shape and input, results are bitwise reproducible from run to run: there are
+ * no floating-point atomics and partial results are merged in a fixed order.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_VERSION 100 /* major * 100 + minor */
+
+/* Status codes. Every validation happens before any device work is enqueued: a call
+ * that returns an error other than FA_ERR_LAUNCH has launched nothing. Errors of the
+ * asynchronous device work itself surface at the caller's next synchronisation. */
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,      /* q, k, v or out is NULL (with B*H*N > 0), or strides NULL where needed */
+  FA_ERR_SHAPE = -2,     /* negative size, size too large, or (d, dv) not supported */
+  FA_ERR_DTYPE = -3,     /* dtype is not FA_F32 or FA_BF16 */
+  FA_ERR_MASK = -4,      /* mask_mode is not FA_MASK_NONE or FA_MASK_CAUSAL */
+  FA_ERR_STRIDE = -5,    /* a negative stride, or rows of out / lse that overlap */
+  FA_ERR_ALIGN = -6,     /* a base pointer or row stride not 16-byte aligned (bias: 4-byte) */
+  FA_ERR_ALIAS = -7,     /* out or lse overlaps an input, or out overlaps lse */
+  FA_ERR_WORKSPACE = -8, /* workspace NULL or smaller than fa_fwd_workspace_size() */
+  FA_ERR_LAUNCH = -9,    /* the HIP runtime refused the launch */
+  FA_ERR_DEVICE = -10,   /* the current HIP device is not a gfx950 */
+  FA_ERR_ALLOC = -11     /* the library-owned workspace could not be allocated */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1 } fa_mask_mode;
+
+/* Element strides (not bytes). The innermost axis of every tensor is contiguous:
+ * the d axis of q and k, the dv axis of v and out, the key axis j of the bias and
+ * the n axis of lse. Strides must be >= 0; 0 broadcasts (inputs only). */
+typedef struct {
+  int64_t q[3];    /* q[b, h, n, :] at q + b*q[0] + h*q[1] + n*q[2]          */
+  int64_t k[3];    /* same for k                                             */
+  int64_t v[3];    /* same for v                                             */
+  int64_t out[3];  /* same for out                                           */
+  int64_t bias[3]; /* bias[b, h, i, :] at bias + b*bias[0] + h*bias[1] + i*bias[2] */
+  int64_t lse[2];  /* lse[b, h, :] at lse + b*lse[0] + h*lse[1]                */
+} fa_strides;
+
+/*
+ * fa_fwd — attention forward, enqueued on `stream`.
+ *
+ * q, k:   device pointers, dtype `dtype`, logical shape [B, H, N, d].
+ * v:      device pointer, dtype `dtype`, logical shape [B, H, N, dv].
+ * bias:   NULL, or a device pointer to fp32 values of logical shape [B, H, N, N]
+ *         (b or h stride 0 to broadcast); -inf entries forbid keys.
+ * mask_mode: FA_MASK_NONE or FA_MASK_CAUSAL (added to the bias when both are given).
+ * out:    device pointer, dtype `dtype`, logical shape [B, H, N, dv]; fully written.
+ * lse:    NULL (not written) or a device pointer to fp32 [B, H, N]; fully written.
+ * B, H, N: batch, heads, sequence length (>= 0; B*H*N == 0 returns FA_OK at once).
+ * d, dv:  Q/K width and V/O width; each must be 64 or 128.
+ * strides: element strides of every tensor (see fa_strides); NULL means contiguous
+ *         [B, H, N, *] tensors, a contiguous [B, H, N, N] bias and a contiguous lse.
+ * dtype:  FA_BF16 (bf16 q, k, v, out; fp32 accumulation) or FA_F32 (all fp32).
+ * stream: a hipStream_t (NULL = the default stream).
+ *
+ * Alignment: q, k, v, out and every non-zero q/k/v/out stride must be 16-byte
+ * aligned in bytes; bias and lse 4-byte aligned.
+ * Ownership: all pointers are caller-owned device memory; the library keeps none of
+ * them after the call's device work finishes, and never mutates q, k, v or bias.
+ * Split problems (few, long query tiles) need a scratch workspace: fa_fwd uses a
+ * buffer the library allocates on first need per (device, stream) and keeps until
+ * fa_shutdown(); calls on one stream are ordered, so they never share it unsafely.
+ * Returns FA_OK or a negative fa_status (see above). Asynchronous: the call returns
+ * before the device work finishes.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
+           void* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
+           const fa_strides* strides, int dtype, void* stream);
+
+/*
+ * fa_fwd_workspace_size — bytes of scratch memory that fa_fwd_ex needs for this
+ * problem (0 when the problem needs none). Depends only on its arguments and the
+ * current device's compute-unit count. Returns 0 for invalid arguments as well.
+ */
+size_t fa_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
+                             int dtype, int mask_mode);
+
+/*
+ * fa_workspace_init — make `workspace` ready for fa_fwd_ex: enqueues a fill kernel
+ * on `stream` that zeroes its first fa_workspace_counter_bytes() bytes (no memset
+ * node, so it may be captured in a graph). A workspace only needs this once: every
+ * completed fa_fwd_ex call leaves those bytes zero again.
+ */
+int fa_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes at the start of a workspace that hold arrival counters (always <= the size). */
+size_t fa_workspace_counter_bytes(void);
+
+/*
+ * fa_fwd_ex — fa_fwd with caller-provided scratch memory; allocates nothing.
+ * workspace: device memory of at least fa_fwd_workspace_size(...) bytes, 256-byte
+ * aligned, initialised once with fa_workspace_init. It may be NULL when the size is
+ * 0. Two calls that may run concurrently must not share a workspace.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
+              void* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
+              const fa_strides* strides, int dtype, void* stream, void* workspace,
+              size_t workspace_bytes);
+
+/* Static description of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* FA_VERSION of the loaded library. */
+int fa_version(void);
+
+/* Frees the library-owned workspaces of fa_fwd (synchronises each device first).
+ * Safe to call at any time when no fa_fwd call is in flight. */
+void fa_shutdown(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,44 @@
+"""Shared helpers of the GPU parity tests: tolerances and comparisons.
+
+Tolerances (applied element by element, GPU vs the fp64 oracle on the same inputs):
+  * fp32 path: max |dO| <= 1e-5;
+  * bf16 inputs with fp32 accumulation: |dO| <= 2e-2 + 1e-2 * |O_ref|;
+  * log-sum-exp: |dlse| <= 1e-3; rows whose oracle lse is -inf must be -inf.
+"""
+
+import numpy as np
+
+F32_ATOL = 1e-5
+BF16_ATOL = 2e-2
+BF16_RTOL = 1e-2
+LSE_ATOL = 1e-3
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_out(o_gpu, o_ref, dtype, where=""):
+    o = to_np(o_gpu) if not isinstance(o_gpu, np.ndarray) else o_gpu
+    assert np.isfinite(o).all(), f"non-finite output {where}"
+    err = np.abs(o - o_ref)
+    if dtype == "f32":
+        worst = float(err.max()) if err.size else 0.0
+        assert worst <= F32_ATOL, f"max |dO| = {worst:.3g} > {F32_ATOL} {where}"
+    else:
+        bound = BF16_ATOL + BF16_RTOL * np.abs(o_ref)
+        bad = err > bound
+        assert not bad.any(), (f"{int(bad.sum())} elements out of tolerance {where}; "
+                               f"max |dO| = {float(err.max()):.3g}")
+    return float(err.max()) if err.size else 0.0
+
+
+def check_lse(l_gpu, l_ref, where=""):
+    lg = to_np(l_gpu) if not isinstance(l_gpu, np.ndarray) else l_gpu
+    neg = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(lg), neg), f"-inf pattern of lse differs {where}"
+    fin = ~neg
+    err = np.abs(lg[fin] - l_ref[fin])
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= LSE_ATOL, f"max |dlse| = {worst:.3g} > {LSE_ATOL} {where}"
+    return worst

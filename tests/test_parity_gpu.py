@@ -1,0 +1,291 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Every case draws seeded synthetic inputs with the workloads' distributions, runs
+fa_fwd on the GPU, and compares with the oracle on the very same (bf16-rounded)
+values. Small cases compare every element; the full-size workloads, run with the
+same launch configuration the benchmark times, compare sampled rows that the oracle
+computes one by one.
+"""
+
+import numpy as np
+import pytest
+
+from exact_attention_35_amd import capi, workloads
+from oracle import sdpa_reference, sdpa_reference_rows
+from parity_util import check_lse, check_out, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, w, dev, **kw):
+    import torch
+
+    q, k, v = (inp[n].to(dev) if inp[n].device != dev else inp[n] for n in ("q", "k", "v"))
+    bias = inp["bias"]
+    if bias is not None:
+        bias = bias.to(dev)
+    out, lse = capi.fa_fwd(q, k, v, bias=bias, causal=w.causal, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _inputs(w, dev):
+    inp = workloads.make_inputs(w, device="cpu")
+    gpu = {}
+    for n, t in inp.items():
+        if t is None:
+            gpu[n] = None
+        elif w.layout == "bnhd" and n in ("q", "k", "v"):
+            # keep the [B, N, H, d] storage on the device too
+            gpu[n] = t.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+        else:
+            gpu[n] = t.to(dev)
+    return inp, gpu
+
+
+# ---------------------------------------------------------------- full elementwise
+
+def test_fp32_single_head_full(gpu_device):
+    w = workloads.workload(0)
+    inp, gpu = _inputs(w, gpu_device)
+    out, lse = _run(gpu, w, gpu_device)
+    o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
+    check_out(out, o_ref, "f32", w.name)
+    check_lse(lse, l_ref, w.name)
+
+
+SMALL = [
+    # (workload index, overrides): several query tiles, ragged tails, split and unsplit plans
+    (1, dict(N=1000)),
+    (1, dict(N=333, H=2)),
+    (2, dict(B=2, H=4, N=777)),
+    (3, dict(B=2, H=3, N=555)),
+    (4, dict(H=2, N=1500)),
+    (4, dict(B=1, H=40, N=300)),
+]
+
+
+@pytest.mark.parametrize("idx,over", SMALL, ids=[f"w{i}-{o}" for i, o in SMALL])
+def test_bf16_small_elementwise(gpu_device, idx, over):
+    w = workloads.workload(idx).resized(**over)
+    inp, gpu = _inputs(w, gpu_device)
+    out, lse = _run(gpu, w, gpu_device)
+    o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
+    check_out(out, o_ref, "bf16", w.name + str(over))
+    check_lse(lse, l_ref, w.name + str(over))
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 17, 63, 65, 127, 129, 255])
+@pytest.mark.parametrize("d,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_shapes(gpu_device, N, d, dv, dtype):
+    for causal, bias in ((True, False), (False, True)):
+        w = workloads.Workload("edge", B=1, H=2, N=N, d=d, dv=dv, dtype=dtype, layout="bhnd",
+                               causal=causal, bias=bias, mask_p=0.2 if bias else 0.0,
+                               seed=N * 1000 + d + dv)
+        inp, gpu = _inputs(w, gpu_device)
+        out, lse = _run(gpu, w, gpu_device)
+        o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
+        check_out(out, o_ref, dtype, f"N={N} d={d} dv={dv} causal={causal}")
+        check_lse(lse, l_ref, f"N={N} d={d} dv={dv}")
+
+
+# ---------------------------------------------------------------- full size, sampled rows
+
+def _sample_rows(N, rng, n=12):
+    fixed = [0, 1, 63, 64, 127, 128, 129, N // 2, N - 129, N - 128, N - 2, N - 1]
+    rnd = rng.integers(0, N, size=n).tolist()
+    return sorted({r for r in fixed + rnd if 0 <= r < N})
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_bf16_full_size_sampled(gpu_device, idx):
+    w = workloads.workload(idx)
+    inp, gpu = _inputs(w, gpu_device)
+    out, lse = _run(gpu, w, gpu_device)
+    out_c, lse_c = out.cpu(), lse.cpu()
+    assert bool(out_c.float().isfinite().all()), "non-finite output"
+    rng = np.random.default_rng(idx)
+    pairs = [(int(rng.integers(0, w.B)), int(rng.integers(0, w.H))) for _ in range(3)]
+    pairs += [(0, 0), (w.B - 1, w.H - 1)]
+    for b, h in sorted(set(pairs)):
+        rows = _sample_rows(w.N, rng)
+        o_ref, l_ref = sdpa_reference_rows(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal,
+                                           b, h, rows)
+        check_out(to_np(out_c[b, h, rows]), o_ref, "bf16", f"{w.name} b={b} h={h}")
+        check_lse(to_np(lse_c[b, h, rows]), l_ref, f"{w.name} b={b} h={h}")
+
+
+# ---------------------------------------------------------------- properties and contract
+
+def test_outputs_fully_written_and_guard_bands_untouched(gpu_device):
+    import torch
+
+    w = workloads.workload(1).resized(N=1111, H=3)
+    inp, gpu = _inputs(w, gpu_device)
+    B, H, N, dv = w.B, w.H, w.N, w.dv
+    pad = 4096
+    obuf = torch.full((B * H * N * dv + 2 * pad,), float("nan"), dtype=torch.bfloat16, device=gpu_device)
+    lbuf = torch.full((B * H * N + 2 * pad,), float("nan"), dtype=torch.float32, device=gpu_device)
+    obuf[:pad] = 7.0
+    obuf[-pad:] = 7.0
+    lbuf[:pad] = 7.0
+    lbuf[-pad:] = 7.0
+    out = obuf[pad:pad + B * H * N * dv].view(B, H, N, dv)
+    lse = lbuf[pad:pad + B * H * N].view(B, H, N)
+    _run(gpu, w, gpu_device, out=out, lse=lse)
+    assert bool(out.float().isfinite().all()) and bool(lse.isfinite().all())
+    assert bool((obuf[:pad] == 7).all()) and bool((obuf[-pad:] == 7).all())
+    assert bool((lbuf[:pad] == 7).all()) and bool((lbuf[-pad:] == 7).all())
+    o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], None, True)
+    check_out(out, o_ref, "bf16")
+    check_lse(lse, l_ref)
+
+
+def test_inputs_not_mutated_and_runs_bitwise_deterministic(gpu_device):
+    import torch
+
+    w = workloads.workload(1).resized(N=2000)
+    _, gpu = _inputs(w, gpu_device)
+    before = [gpu[n].clone() for n in ("q", "k", "v")]
+    o1, l1 = _run(gpu, w, gpu_device)
+    o2, l2 = _run(gpu, w, gpu_device)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, n in zip(before, ("q", "k", "v")):
+        assert torch.equal(a, gpu[n])
+
+
+def test_workspace_entry_point_matches(gpu_device):
+    import torch
+
+    for idx, over in ((1, dict(N=2000)), (1, {}), (2, dict(B=1, H=2, N=600))):
+        w = workloads.workload(idx).resized(**over)
+        _, gpu = _inputs(w, gpu_device)
+        o1, l1 = _run(gpu, w, gpu_device)
+        nbytes = capi.fa_fwd_workspace_size(w.B, w.H, w.N, w.d, w.dv, capi.FA_BF16, w.causal)
+        ws = None
+        if nbytes:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+            capi.fa_workspace_init(ws)
+        for _ in range(2):  # the workspace stays valid across calls
+            o2, l2 = capi.fa_fwd_ex(gpu["q"], gpu["k"], gpu["v"], ws, causal=w.causal)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        if nbytes:
+            with pytest.raises(capi.FaError):
+                capi.fa_fwd_ex(gpu["q"], gpu["k"], gpu["v"], ws[: nbytes // 2], causal=w.causal)
+
+
+def test_single_allowed_key_and_constant_v_exact(gpu_device):
+    import torch
+
+    w = workloads.workload(1).resized(N=700)
+    _, gpu = _inputs(w, gpu_device)
+    out, _ = _run(gpu, w, gpu_device)
+    assert torch.equal(out[0, 0, 0], gpu["v"][0, 0, 0])      # causal row 0 -> V[0]
+    vc = torch.full_like(gpu["v"], -1.3125)
+    out, _ = capi.fa_fwd(gpu["q"], gpu["k"], vc, causal=True)
+    torch.cuda.synchronize()
+    assert bool((out == -1.3125).all())
+    # a bias row with a single finite entry returns that value row
+    N = 300
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn(1, 1, N, 128, generator=g).bfloat16().to(gpu_device)
+    k = torch.randn(1, 1, N, 128, generator=g).bfloat16().to(gpu_device)
+    v = torch.randn(1, 1, N, 128, generator=g).bfloat16().to(gpu_device)
+    pick = torch.randint(0, N, (N,), generator=g)
+    bias = torch.full((1, 1, N, N), float("-inf"))
+    bias[0, 0, torch.arange(N), pick] = torch.randn(N, generator=g)
+    out, _ = capi.fa_fwd(q, k, v, bias=bias.to(gpu_device))
+    torch.cuda.synchronize()
+    assert torch.equal(out[0, 0], v[0, 0, pick.to(gpu_device)])
+
+
+def test_perturbation_changes_only_dependent_rows(gpu_device):
+    import torch
+
+    w = workloads.workload(1).resized(N=900)
+    _, gpu = _inputs(w, gpu_device)
+    o1, _ = _run(gpu, w, gpu_device)
+    j = 500
+    k2 = gpu["k"].clone()
+    k2[0, 0, j] = -k2[0, 0, j]
+    o2, _ = capi.fa_fwd(gpu["q"], k2, gpu["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[0, 0, :j], o2[0, 0, :j])
+    assert not torch.equal(o1[0, 0, j:], o2[0, 0, j:])
+    # bias perturbation: only row i of head h changes, in every batch
+    wb = workloads.workload(3).resized(B=2, H=2, N=200)
+    inp, gb = _inputs(wb, gpu_device)
+    ob1, _ = _run(gb, wb, gpu_device)
+    bias2 = gb["bias"].clone()
+    jj = int(torch.nonzero(torch.isfinite(inp["bias"][0, 1, 77]))[3])
+    bias2[0, 1, 77, jj] += 1.5
+    ob2, _ = capi.fa_fwd(gb["q"], gb["k"], gb["v"], bias=bias2)
+    torch.cuda.synchronize()
+    diff = (ob1 != ob2).any(dim=-1)
+    assert bool(diff[:, 1, 77].all()) and int(diff.sum()) == 2
+
+
+def test_masked_leading_tile_and_empty_row_convention(gpu_device):
+    import torch
+
+    N = 400
+    g = torch.Generator().manual_seed(9)
+    q = torch.randn(1, 1, N, 128, generator=g).bfloat16()
+    k = torch.randn(1, 1, N, 128, generator=g).bfloat16()
+    v = torch.randn(1, 1, N, 128, generator=g).bfloat16()
+    bias = torch.randn(1, 1, N, N, generator=g)
+    bias[0, 0, 200:, :128] = float("-inf")   # whole leading key tiles masked for these rows
+    bias[0, 0, 333, :] = float("-inf")       # a row with no allowed key
+    out, lse = capi.fa_fwd(q.to(gpu_device), k.to(gpu_device), v.to(gpu_device),
+                           bias=bias.to(gpu_device))
+    torch.cuda.synchronize()
+    o_ref, l_ref = sdpa_reference(q, k, v, bias, False, allow_empty_rows=True)
+    check_out(out, o_ref, "bf16")
+    check_lse(lse, l_ref)
+    assert bool((out[0, 0, 333] == 0).all()) and float(lse[0, 0, 333]) == float("-inf")
+
+
+def test_strided_inputs_and_outputs(gpu_device):
+    import torch
+
+    B, H, N, d = 2, 3, 300, 128
+    g = torch.Generator().manual_seed(5)
+    big = torch.randn(B, N, H, 3 * d, generator=g).bfloat16().to(gpu_device)  # packed qkv
+    q = big[..., :d].permute(0, 2, 1, 3)
+    k = big[..., d:2 * d].permute(0, 2, 1, 3)
+    v = big[..., 2 * d:].permute(0, 2, 1, 3)
+    out = torch.empty(B, N, H, d, dtype=torch.bfloat16, device=gpu_device).permute(0, 2, 1, 3)
+    lse = torch.empty(H, B, N, device=gpu_device).permute(1, 0, 2)
+    capi.fa_fwd(q, k, v, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = sdpa_reference(q.cpu(), k.cpu(), v.cpu(), None, True)
+    check_out(out, o_ref, "bf16")
+    check_lse(lse, l_ref)
+
+
+def test_two_streams_concurrently(gpu_device):
+    import torch
+
+    w1 = workloads.workload(1).resized(N=1500)
+    w2 = workloads.workload(2).resized(B=1, H=8, N=640)
+    i1, g1 = _inputs(w1, gpu_device)
+    i2, g2 = _inputs(w2, gpu_device)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            a = capi.fa_fwd(g1["q"], g1["k"], g1["v"], causal=True, stream=s1)
+        with torch.cuda.stream(s2):
+            b = capi.fa_fwd(g2["q"], g2["k"], g2["v"], causal=True, stream=s2)
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    r1 = sdpa_reference(i1["q"], i1["k"], i1["v"], None, True)
+    r2 = sdpa_reference(i2["q"], i2["k"], i2["v"], None, True)
+    for (o1, l1), (o2, l2) in outs:
+        check_out(o1, r1[0], "bf16")
+        check_lse(l1, r1[1])
+        check_out(o2, r2[0], "bf16")
+        check_lse(l2, r2[1])
