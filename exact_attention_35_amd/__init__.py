@@ -7,12 +7,12 @@ on first use; a missing library raises (there is no CPU fallback).
 
 from .capi import (FA_BF16, FA_F32, FA_MASK_CAUSAL, FA_MASK_NONE, FA_OK, FaError,  # noqa: F401
                    fa_fwd, fa_fwd_ex, fa_fwd_workspace_size, fa_shutdown, fa_status_string,
-                   fa_version, fa_workspace_counter_bytes, fa_workspace_init)
+                   fa_version)
 
 forward = fa_fwd
 
 __all__ = [
-    "forward", "fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_workspace_init",
-    "fa_workspace_counter_bytes", "fa_status_string", "fa_version", "fa_shutdown",
+    "forward", "fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
+    "fa_version", "fa_shutdown",
     "FaError", "FA_OK", "FA_F32", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
 ]

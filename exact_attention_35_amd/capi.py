@@ -15,8 +15,7 @@ import os
 __all__ = [
     "FaError", "FA_OK", "FA_F32", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
     "STATUS", "lib", "library_path", "fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size",
-    "fa_workspace_init", "fa_workspace_counter_bytes", "fa_status_string", "fa_version",
-    "fa_shutdown", "make_strides", "FaStrides", "EXPORTED",
+    "fa_status_string", "fa_version", "fa_shutdown", "make_strides", "FaStrides", "EXPORTED",
 ]
 
 FA_OK = 0
@@ -31,8 +30,8 @@ STATUS = {
 }
 
 # every symbol include/fa.h declares
-EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_workspace_init",
-            "fa_workspace_counter_bytes", "fa_status_string", "fa_version", "fa_shutdown")
+EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
+            "fa_version", "fa_shutdown")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -75,10 +74,6 @@ def lib():
     L.fa_fwd_ex.restype = ctypes.c_int
     L.fa_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     L.fa_fwd_workspace_size.restype = sz
-    L.fa_workspace_init.argtypes = [vp, sz, vp]
-    L.fa_workspace_init.restype = ctypes.c_int
-    L.fa_workspace_counter_bytes.argtypes = []
-    L.fa_workspace_counter_bytes.restype = sz
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -99,10 +94,6 @@ def fa_version() -> int:
 
 def fa_shutdown() -> None:
     lib().fa_shutdown()
-
-
-def fa_workspace_counter_bytes() -> int:
-    return int(lib().fa_workspace_counter_bytes())
 
 
 def _check(status: int) -> None:
@@ -196,11 +187,6 @@ def fa_fwd(q, k, v, bias=None, causal=False, out=None, lse=None, stream=None):
 def fa_fwd_workspace_size(B, H, N, d, dv, dtype_code, causal) -> int:
     return int(lib().fa_fwd_workspace_size(B, H, N, d, dv, dtype_code,
                                            FA_MASK_CAUSAL if causal else FA_MASK_NONE))
-
-
-def fa_workspace_init(workspace, stream=None) -> None:
-    _check(lib().fa_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
-                                   _stream_handle(stream, workspace.device)))
 
 
 def fa_fwd_ex(q, k, v, workspace, bias=None, causal=False, out=None, lse=None, stream=None):

@@ -29,8 +29,7 @@ namespace {
 
 using fa::Params;
 
-constexpr size_t kCounterBytes = 16384;  // arrival counters: up to 4096 split query tiles
-constexpr int kMaxSplit = 64;
+constexpr int kMaxSplitTiles = 4096;  // query tiles eligible for a split over keys
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi) in bytes
@@ -175,47 +174,59 @@ int device_info(int* dev_out, DevInfo* info) {
 struct Plan {
   bool mfma = false;
   int n_qt = 0;
-  int n_split = 1;
-  int grid = 0;
+  int chunk_tiles = 0;  // 0: no split over keys
+  int grid = 0;         // forward workgroups (units)
+  int merge_grid = 0;   // merge workgroups (0: no merge kernel)
   size_t ws_bytes = 0;
   size_t off_ml = 0, off_o = 0;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int env_split() {
-  static int v = [] {
-    const char* e = std::getenv("FA_NSPLIT");
-    return e ? std::atoi(e) : 0;
-  }();
-  return v;
+int env_int(const char* name) {
+  const char* e = std::getenv(name);
+  return e ? std::atoi(e) : 0;
+}
+
+// Key tiles of query tile qt (causal tiles stop at the diagonal).
+int64_t qtile_ntiles(int64_t N, int qt, bool causal) {
+  const int64_t bm = fa::kMfmaBM, bn = fa::kMfmaBN;
+  const int64_t kv = causal ? std::min(N, (qt + 1) * bm) : N;
+  return (kv + bn - 1) / bn;
 }
 
 Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask, int cus) {
   Plan pl;
   pl.mfma = dtype == FA_BF16;  // d, dv in {64, 128} already checked
   if (!pl.mfma) return pl;
-  const int bm = fa::kMfmaBM, bn = fa::kMfmaBN;
+  const bool causal = mask == FA_MASK_CAUSAL;
+  const int bm = fa::kMfmaBM;
   pl.n_qt = (int)((N + bm - 1) / bm);
-  const int64_t tiles = (int64_t)B * H * pl.n_qt;
-  const int ntiles_max = (int)((N + bn - 1) / bn);
-  int split = 1;
-  if (tiles > 0 && tiles < cus && tiles <= (int64_t)(kCounterBytes / sizeof(unsigned))) {
-    // Too few query tiles to occupy the chip: cut each tile's keys into ranges so
-    // that about two workgroups per compute unit are available.
-    split = (int)((2 * (int64_t)cus + tiles - 1) / tiles);
-    split = std::min(split, std::min(ntiles_max, kMaxSplit));
-    if (env_split() > 0) split = std::min(env_split(), std::min(ntiles_max, kMaxSplit));
-    split = std::max(split, 1);
+  const int64_t BH = B * H;
+  const int64_t tiles = BH * pl.n_qt;
+  pl.grid = (int)tiles;
+  if (tiles <= 0 || tiles >= cus || tiles > kMaxSplitTiles) return pl;
+  // Too few query tiles to occupy the chip: cut each tile's key range into ranges
+  // of about `chunk` key tiles, so that about `target` ranges exist in total.
+  int64_t total = 0;
+  for (int qt = 0; qt < pl.n_qt; ++qt) total += BH * qtile_ntiles(N, qt, causal);
+  const int64_t target = env_int("FA_SPLIT_UNITS") > 0 ? env_int("FA_SPLIT_UNITS") : 2 * (int64_t)cus;
+  const int64_t chunk = std::max<int64_t>(1, (total + target - 1) / target);
+  int64_t units = 0;
+  bool any_split = false;
+  for (int qt = 0; qt < pl.n_qt; ++qt) {
+    const int64_t nt = qtile_ntiles(N, qt, causal);
+    const int64_t nch = (nt + chunk - 1) / chunk;
+    units += BH * nch;
+    any_split |= nch > 1;
   }
-  pl.n_split = split;
-  pl.grid = (int)(tiles * split);
-  if (split > 1) {
-    const size_t units = (size_t)tiles * split;
-    pl.off_ml = kCounterBytes;
-    pl.off_o = round_up(pl.off_ml + units * 2 * bm * sizeof(float), 256);
-    pl.ws_bytes = round_up(pl.off_o + units * (size_t)bm * dv * sizeof(float), 256);
-  }
+  if (!any_split) return pl;
+  pl.chunk_tiles = (int)chunk;
+  pl.grid = (int)units;
+  pl.merge_grid = (int)(tiles * (bm / 32));
+  pl.off_ml = 0;
+  pl.off_o = round_up(units * 2 * bm * sizeof(float), 256);
+  pl.ws_bytes = round_up(pl.off_o + (size_t)units * bm * dv * sizeof(float), 256);
   return pl;
 }
 
@@ -235,20 +246,19 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
   p.bias_vec4 = P.bias && aligned(P.bias, 16) && s.bias[0] % 4 == 0 && s.bias[1] % 4 == 0 && s.bias[2] % 4 == 0;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.d));
   p.n_qt = pl.n_qt;
-  p.n_split = pl.n_split;
-  if (pl.n_split > 1) {
+  p.chunk_tiles = pl.chunk_tiles;
+  if (pl.ws_bytes > 0) {
     unsigned char* w = static_cast<unsigned char*>(ws);
-    p.counters = reinterpret_cast<unsigned*>(w);
     p.part_ml = reinterpret_cast<float*>(w + pl.off_ml);
     p.part_o = reinterpret_cast<float*>(w + pl.off_o);
   }
-  hipError_t e = pl.mfma ? fa::launch_mfma_bf16(p, pl.grid, stream)
+  hipError_t e = pl.mfma ? fa::launch_mfma_bf16(p, pl.grid, pl.merge_grid, stream)
                          : fa::launch_generic(p, P.dtype == FA_BF16, stream);
   if (std::getenv("FA_LOG"))
-    std::fprintf(stderr, "[fa] %s B=%lld H=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d n_qt=%d split=%d grid=%d ws=%zu\n",
+    std::fprintf(stderr, "[fa] %s B=%lld H=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d n_qt=%d chunk=%d grid=%d merge=%d ws=%zu\n",
                  pl.mfma ? "mfma_bf16" : (P.dtype == FA_BF16 ? "generic_bf16" : "generic_f32"),
                  (long long)P.B, (long long)P.H, (long long)P.N, (long long)P.d, (long long)P.dv,
-                 p.causal, P.bias != nullptr, pl.n_qt, pl.n_split, pl.grid, pl.ws_bytes);
+                 p.causal, P.bias != nullptr, pl.n_qt, pl.chunk_tiles, pl.grid, pl.merge_grid, pl.ws_bytes);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -282,10 +292,6 @@ int owned_workspace(int dev, hipStream_t stream, size_t need, void** out) {
     }
     void* p = nullptr;
     if (hipMalloc(&p, need) != hipSuccess) return FA_ERR_ALLOC;
-    if (fa::launch_fill_zero(p, kCounterBytes, stream) != hipSuccess) {
-      (void)hipFree(p);
-      return FA_ERR_ALLOC;
-    }
     w.ptr = p;
     w.bytes = need;
   }
@@ -342,20 +348,6 @@ size_t fa_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t
   DevInfo di;
   if (device_info(&dev, &di) != FA_OK) return 0;
   return make_plan(B, H, N, d, dv, dtype, mask_mode, di.cus).ws_bytes;
-}
-
-size_t fa_workspace_counter_bytes(void) { return kCounterBytes; }
-
-int fa_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
-  if (!workspace) return FA_ERR_NULL;
-  if (!aligned(workspace, 256)) return FA_ERR_WORKSPACE;
-  const size_t n = std::min(workspace_bytes, kCounterBytes);
-  int dev = 0;
-  DevInfo di;
-  int st = device_info(&dev, &di);
-  if (st != FA_OK) return st;
-  return fa::launch_fill_zero(workspace, n, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK
-                                                                                             : FA_ERR_LAUNCH;
 }
 
 const char* fa_status_string(int status) {

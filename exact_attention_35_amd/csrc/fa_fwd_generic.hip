@@ -155,23 +155,10 @@ hipError_t launch_t(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-__global__ void fill_zero_u32(uint32_t* p, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
-}
-
 }  // namespace
 
 hipError_t launch_generic(const Params& p, bool is_bf16, hipStream_t stream) {
   return is_bf16 ? launch_t<__bf16>(p, stream) : launch_t<float>(p, stream);
-}
-
-hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {
-  const size_t n = bytes / 4;
-  if (n == 0) return hipSuccess;
-  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
-  hipLaunchKernelGGL(fill_zero_u32, dim3(blocks), dim3(256), 0, stream, static_cast<uint32_t*>(ptr), n);
-  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -25,13 +25,12 @@ struct Params {
   int causal;
   int bias_vec4;      // bias base 16-byte aligned and row stride a multiple of 4
   float scale_log2;   // log2(e) / sqrt(d): scores in base-2 units
-  // Work decomposition. A unit is (batch*head, query tile, key split).
+  // Work decomposition. A unit is (batch*head, query tile, range of key tiles).
   int n_qt;           // query tiles per (b, h)
-  int n_split;        // key splits per query tile (1: no split, no workspace)
-  // Scratch for split problems (see fa_api.cpp for the layout).
-  unsigned* counters; // one arrival counter per (b*h, query tile)
-  float* part_o;      // [unit][BM][dv] unnormalised numerators
-  float* part_ml;     // [unit][2][BM]  running max (base 2) and normaliser
+  int chunk_tiles;    // 0: no split; else key tiles per range (ranges of a tile are balanced)
+  // Scratch for split problems: one slot per unit.
+  float* part_o;      // [slot][dv/4][BM][4] unnormalised numerators
+  float* part_ml;     // [slot][2][BM]       reference (base 2) and normaliser
 };
 
 // Query-tile height of the matrix-core kernel, and the key-tile width.
@@ -41,8 +40,7 @@ constexpr int kMfmaBN = 64;
 constexpr int kGenericBM = 64;
 
 // Launchers (each returns the hipError_t of the launch).
-hipError_t launch_mfma_bf16(const Params& p, int grid, hipStream_t stream);
+hipError_t launch_mfma_bf16(const Params& p, int grid, int merge_grid, hipStream_t stream);
 hipError_t launch_generic(const Params& p, bool is_bf16, hipStream_t stream);
-hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace fa

@@ -24,8 +24,9 @@
  * none, this library writes O = 0 and lse = -inf (a convention of this library).
  *
  * Numerics: bf16 inputs are multiplied on the matrix cores with fp32 accumulation;
- * probabilities are rounded to bf16 before the P V product and the normaliser sums
- * the rounded values; O is rounded to the output dtype once (round to nearest even).
+ * probabilities are rounded to bf16 for the P V product while the normaliser (and so
+ * the log-sum-exp) sums them unrounded in fp32; O is rounded to the output dtype once
+ * (round to nearest even).
  * fp32 inputs are computed in fp32 throughout. Results equal the definition up to
  * rounding ("exact" means the same function, not the same bits). For a fixed build,
  * device, shape and input, results are bitwise reproducible from run to run: there are
@@ -101,6 +102,8 @@ typedef struct {
  * Split problems (few, long query tiles) need a scratch workspace: fa_fwd uses a
  * buffer the library allocates on first need per (device, stream) and keeps until
  * fa_shutdown(); calls on one stream are ordered, so they never share it unsafely.
+ * Such problems run as two kernels on `stream`: the forward over key ranges, then a
+ * merge of each query tile's ranges.
  * Returns FA_OK or a negative fa_status (see above). Asynchronous: the call returns
  * before the device work finishes.
  */
@@ -117,21 +120,11 @@ size_t fa_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t
                              int dtype, int mask_mode);
 
 /*
- * fa_workspace_init — make `workspace` ready for fa_fwd_ex: enqueues a fill kernel
- * on `stream` that zeroes its first fa_workspace_counter_bytes() bytes (no memset
- * node, so it may be captured in a graph). A workspace only needs this once: every
- * completed fa_fwd_ex call leaves those bytes zero again.
- */
-int fa_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
-
-/* Bytes at the start of a workspace that hold arrival counters (always <= the size). */
-size_t fa_workspace_counter_bytes(void);
-
-/*
  * fa_fwd_ex — fa_fwd with caller-provided scratch memory; allocates nothing.
  * workspace: device memory of at least fa_fwd_workspace_size(...) bytes, 256-byte
- * aligned, initialised once with fa_workspace_init. It may be NULL when the size is
- * 0. Two calls that may run concurrently must not share a workspace.
+ * aligned; its contents need no initialisation and are scratch after the call. It may
+ * be NULL when the size is 0. Two calls that may run concurrently must not share a
+ * workspace.
  */
 int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
               void* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,

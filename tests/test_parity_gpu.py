@@ -165,8 +165,7 @@ def test_workspace_entry_point_matches(gpu_device):
         nbytes = capi.fa_fwd_workspace_size(w.B, w.H, w.N, w.d, w.dv, capi.FA_BF16, w.causal)
         ws = None
         if nbytes:
-            ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
-            capi.fa_workspace_init(ws)
+            ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device=gpu_device)
         for _ in range(2):  # the workspace stays valid across calls
             o2, l2 = capi.fa_fwd_ex(gpu["q"], gpu["k"], gpu["v"], ws, causal=w.causal)
             torch.cuda.synchronize()
