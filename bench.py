@@ -58,17 +58,20 @@ def read_traffic(workload: str):
 
 
 def copy_probe(steps: int) -> None:
-    """A plain device copy of 256 MiB, `steps` times (for FETCH_SIZE/WRITE_SIZE scale)."""
+    """A plain elementwise copy kernel (x * 1 -> y, fp32) over 256 MiB, `steps` times:
+    its FETCH_SIZE / WRITE_SIZE readings calibrate those counters against a known
+    256 MiB read and 256 MiB write per dispatch."""
     import torch
 
-    n = 256 << 20
-    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    n = (256 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(steps):
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "steps": steps}))
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "steps": steps}))
 
 
 def cpu_baseline(w, inp):

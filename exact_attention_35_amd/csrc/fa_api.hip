@@ -29,7 +29,8 @@ namespace {
 
 using fa::Params;
 
-constexpr int kMaxSplitTiles = 4096;  // query tiles eligible for a split over keys
+constexpr int kMaxSplitTiles = 4096;          // query tiles eligible for a split over keys
+constexpr int64_t kMaxRowStride = 1 << 24;     // bf16 k/v row stride limit (elements)
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi) in bytes
@@ -109,6 +110,8 @@ int validate(const Problem& P) {
     for (int i = 0; i < 3; ++i)
       if (all[t][i] < 0) return FA_ERR_STRIDE;
   if (s.lse[0] < 0 || s.lse[1] < 0) return FA_ERR_STRIDE;
+  // the bf16 kernel addresses a 64-row key tile with 32-bit byte offsets
+  if (P.dtype == FA_BF16 && (s.k[2] >= kMaxRowStride || s.v[2] >= kMaxRowStride)) return FA_ERR_STRIDE;
   const int64_t sz[3] = {P.B, P.H, P.N};
   if (!non_overlapping(sz, s.out, 3, P.dv)) return FA_ERR_STRIDE;
   if (P.lse && !non_overlapping(sz, s.lse, 2, P.N)) return FA_ERR_STRIDE;
@@ -211,7 +214,10 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype
   int64_t total = 0;
   for (int qt = 0; qt < pl.n_qt; ++qt) total += BH * qtile_ntiles(N, qt, causal);
   const int64_t target = env_int("FA_SPLIT_UNITS") > 0 ? env_int("FA_SPLIT_UNITS") : 2 * (int64_t)cus;
-  const int64_t chunk = std::max<int64_t>(1, (total + target - 1) / target);
+  int64_t chunk = std::max<int64_t>(1, (total + target - 1) / target);
+  // no query tile may be cut into more than kMaxRanges ranges
+  const int64_t nt_max = qtile_ntiles(N, pl.n_qt - 1, causal);
+  chunk = std::max<int64_t>(chunk, (nt_max + fa::kMaxRanges - 1) / fa::kMaxRanges);
   int64_t units = 0;
   bool any_split = false;
   for (int qt = 0; qt < pl.n_qt; ++qt) {

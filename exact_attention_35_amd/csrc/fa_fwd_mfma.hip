@@ -85,24 +85,42 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Copy one key tile (rows kv0 .. kv0+BN-1 of a [N, W] bf16 matrix with row stride
-// `sn`) into an LDS stage, 16 bytes per lane per instruction, chunk-swizzled.
+// Tile copies: rows kv0 .. kv0+BN-1 of a [N, W] bf16 matrix with row stride `sn`
+// go into an LDS stage, 16 bytes per lane per instruction, chunk-swizzled. Lane
+// `lane` of instruction i of wave `wave` fills 16-byte slot (wave*NLD + i)*64 + lane,
+// i.e. row slot/CH, physical chunk slot%CH, which holds logical chunk
+// (slot%CH) ^ (row mod CH). The per-lane byte offsets within a tile do not depend on
+// the tile, so they are computed once; rows past the sequence end (tail tile only)
+// are clamped to the last row.
 template <int W, int NLD>
-__device__ __forceinline__ void copy_tile(unsigned char* stage, const __bf16* base, int64_t sn,
-                                          int kv0, int N, int wave, int lane) {
-  constexpr int CH = W / 8;
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int slot0 = (wave * NLD + i) * 64;  // first 16-byte slot this instruction fills
-    const int slot = slot0 + lane;
-    const int row = slot / CH;
-    const int pch = slot % CH;
-    const int lch = pch ^ (row & (CH - 1));
-    const int key = min(kv0 + row, N - 1);
-    __builtin_amdgcn_global_load_lds(GLB_PTR(base + (int64_t)key * sn + lch * 8),
-                                     LDS_PTR(void, stage + slot0 * 16), 16, 0, 0);
+struct TileCopy {
+  static constexpr int CH = W / 8;
+  int off[NLD];  // byte offset of this lane's 16 bytes from the tile's first row
+  __device__ __forceinline__ static int slot_row(int wave, int i, int lane) { return ((wave * NLD + i) * 64 + lane) / CH; }
+  __device__ __forceinline__ static int slot_col(int wave, int i, int lane) {
+    const int slot = (wave * NLD + i) * 64 + lane;
+    return ((slot % CH) ^ ((slot / CH) & (CH - 1))) * 16;
   }
-}
+  __device__ __forceinline__ void init(int64_t sn, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) off[i] = (int)(slot_row(wave, i, lane) * sn * 2) + slot_col(wave, i, lane);
+  }
+  __device__ __forceinline__ void copy(unsigned char* stage, const __bf16* base, int64_t sn, int kv0,
+                                       int N, int wave, int lane) const {
+    const unsigned char* tile = reinterpret_cast<const unsigned char*>(base + (int64_t)kv0 * sn);
+    if (kv0 + kMfmaBN <= N) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        __builtin_amdgcn_global_load_lds(GLB_PTR(tile + off[i]), LDS_PTR(void, stage + (wave * NLD + i) * 1024), 16, 0, 0);
+    } else {  // tail tile: rows past the end read the last row
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int o = (int)(min(slot_row(wave, i, lane), N - 1 - kv0) * sn * 2) + slot_col(wave, i, lane);
+        __builtin_amdgcn_global_load_lds(GLB_PTR(tile + o), LDS_PTR(void, stage + (wave * NLD + i) * 1024), 16, 0, 0);
+      }
+    }
+  }
+};
 
 // Per-unit description: which (b*h, query tile) and which range of key tiles.
 struct Unit {
@@ -312,15 +330,19 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   };
 
   // ---- prologue: K(t_begin), K(t_begin+1), V(t_begin) into LDS; scores of t_begin ----
-  copy_tile<D, C::KLD>(kst(t_begin), kp, p.k_sn, t_begin * C::BN, N, wave, lane);
-  if (t_begin + 1 < t_end) copy_tile<D, C::KLD>(kst(t_begin + 1), kp, p.k_sn, (t_begin + 1) * C::BN, N, wave, lane);
-  copy_tile<DV, C::VLD>(vst(t_begin), vp, p.v_sn, t_begin * C::BN, N, wave, lane);
+  TileCopy<D, C::KLD> kcp;
+  TileCopy<DV, C::VLD> vcp;
+  kcp.init(p.k_sn, wave, lane);
+  vcp.init(p.v_sn, wave, lane);
+  kcp.copy(kst(t_begin), kp, p.k_sn, t_begin * C::BN, N, wave, lane);
+  if (t_begin + 1 < t_end) kcp.copy(kst(t_begin + 1), kp, p.k_sn, (t_begin + 1) * C::BN, N, wave, lane);
+  vcp.copy(vst(t_begin), vp, p.v_sn, t_begin * C::BN, N, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  floatx16 scur[2];
-  if (t_begin < tw_end) qk(kst(t_begin), scur);
-
-  for (int t = t_begin; t < t_end; ++t) {
+  // One key tile. `sc` holds the raw scores of tile t; the scores of tile t+1 are
+  // computed into `sn` while tile t's softmax runs. The caller alternates the two
+  // buffers, so no register copy is needed between tiles.
+  auto tile_step = [&](int t, floatx16 (&sc)[2], floatx16 (&sn)[2]) {
     // K(t+1) and V(t) have landed for every wave, and no wave still reads the stages
     // refilled below (K(t) was read for tile t's scores, V(t-1) by P V of tile t-1)
     __builtin_amdgcn_s_waitcnt(0);
@@ -329,24 +351,23 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     if constexpr (BIAS) {
       if (t < tw_end) load_bias(bcur, t * C::BN);
     }
-    if (t + 2 < t_end) copy_tile<D, C::KLD>(kst(t + 2), kp, p.k_sn, (t + 2) * C::BN, N, wave, lane);
-    if (t + 1 < t_end) copy_tile<DV, C::VLD>(vst(t + 1), vp, p.v_sn, (t + 1) * C::BN, N, wave, lane);
+    if (t + 2 < t_end) kcp.copy(kst(t + 2), kp, p.k_sn, (t + 2) * C::BN, N, wave, lane);
+    if (t + 1 < t_end) vcp.copy(vst(t + 1), vp, p.v_sn, (t + 1) * C::BN, N, wave, lane);
 
     const int kv0 = t * C::BN;
     const bool do_qk = t + 1 < tw_end;
     const bool do_sm = t < tw_end;
     const bool edge = (kv0 + C::BN > N) || (p.causal && kv0 + C::BN - 1 > wq0);
 
-    floatx16 snext[2];
     bf16x8 pcur[4];
     float alpha = 1.f;
     // scores of tile t+1 on the matrix cores while the vector ALUs run tile t's softmax
     if (do_qk && do_sm && !edge) {
-      qk(kst(t + 1), snext);
-      softmax(scur, pcur, kv0, false, alpha);
+      qk(kst(t + 1), sn);
+      softmax(sc, pcur, kv0, false, alpha);
     } else {
-      if (do_qk) qk(kst(t + 1), snext);
-      if (do_sm) softmax(scur, pcur, kv0, edge, alpha);
+      if (do_qk) qk(kst(t + 1), sn);
+      if (do_sm) softmax(sc, pcur, kv0, edge, alpha);
     }
     if (do_sm) {
       // o_{t-1} is rescaled by alpha_t before P(t) V(t) is added
@@ -356,10 +377,12 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
       }
       pv(vst(t), pcur);
     }
-    if (do_qk) {
-      scur[0] = snext[0];
-      scur[1] = snext[1];
-    }
+  };
+  floatx16 s0[2], s1[2];
+  if (t_begin < tw_end) qk(kst(t_begin), s0);
+  for (int t = t_begin; t < t_end; t += 2) {
+    tile_step(t, s0, s1);
+    if (t + 1 < t_end) tile_step(t + 1, s1, s0);
   }
 
   // ---- epilogue ----
@@ -403,13 +426,15 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
 }
 
 // Merge of the partial states of split query tiles. Block = (query tile, b*h, 32-row
-// group); thread = (row, 4-wide dv chunk) items. Reads each range's (m, l, o) in range
-// order, writes O (bf16) and lse.
+// group). The ranges' (m, l) of the 32 rows are staged in LDS and turned into weights
+// 2^(m_p - m) / l once per row; then every (row, 4-wide dv chunk) item sums its ranges
+// in range order, with all of its loads issued together (at most kMaxRanges ranges).
 template <int DV>
 __global__ __launch_bounds__(256) void merge_split(Params p) {
   constexpr int BM = kMfmaBM, BN = kMfmaBN, RG = 32;
+  __shared__ float w_s[kMaxRanges][RG];
   const int BH = p.B * p.H;
-  const int groups = BM / RG;
+  constexpr int groups = BM / RG;
   int blk = blockIdx.x;
   const int rg = blk % groups;
   blk /= groups;
@@ -426,35 +451,56 @@ __global__ __launch_bounds__(256) void merge_split(Params p) {
   if (nch == 1) return;  // written directly by the forward kernel
   const int slot0 = base + bh * nch;
   const int b = bh / p.H, h = bh % p.H;
-  __bf16* ob = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh;
-  for (int idx = threadIdx.x; idx < RG * (DV / 4); idx += 256) {
-    const int r = rg * RG + idx % RG;
-    const int c4 = idx / RG;
-    const int qr = qt * BM + r;
-    if (qr >= p.N) continue;
+  const int tid = threadIdx.x;
+  if (tid < RG) {
+    const int r = rg * RG + tid;
     float m = -INFINITY;
-    for (int j = 0; j < nch; ++j) m = fmaxf(m, p.part_ml[(int64_t)(slot0 + j) * (2 * BM) + r]);
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    float mp[kMaxRanges], lp[kMaxRanges];
+#pragma unroll
+    for (int j = 0; j < kMaxRanges; ++j) {
+      mp[j] = j < nch ? p.part_ml[(int64_t)(slot0 + j) * (2 * BM) + r] : -INFINITY;
+      lp[j] = j < nch ? p.part_ml[(int64_t)(slot0 + j) * (2 * BM) + BM + r] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxRanges; ++j) m = fmaxf(m, mp[j]);
     float l = 0.f;
     if (m != -INFINITY) {
-      for (int j = 0; j < nch; ++j) {
-        const float* ml = p.part_ml + (int64_t)(slot0 + j) * (2 * BM);
-        const float w = __builtin_amdgcn_exp2f(ml[r] - m);
-        l += w * ml[BM + r];
-        const floatx4 v4 = *reinterpret_cast<const floatx4*>(p.part_o + (int64_t)(slot0 + j) * (BM * DV) + (c4 * BM + r) * 4);
-        acc += w * v4;
+#pragma unroll
+      for (int j = 0; j < kMaxRanges; ++j) {
+        mp[j] = __builtin_amdgcn_exp2f(mp[j] - m);  // 0 for absent ranges
+        l += mp[j] * lp[j];
       }
     }
     const bool ok = m != -INFINITY && l > 0.f;
     const float inv = ok ? 1.f / l : 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxRanges; ++j) w_s[j][tid] = ok ? mp[j] * inv : 0.f;
+    const int qr = qt * BM + r;
+    if (p.lse && qr < p.N)
+      p.lse[b * p.l_sb + h * p.l_sh + qr] = ok ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  __bf16* ob = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh;
+  for (int idx = tid; idx < RG * (DV / 4); idx += 256) {
+    const int rr = idx % RG;
+    const int r = rg * RG + rr;
+    const int c4 = idx / RG;
+    const int qr = qt * BM + r;
+    if (qr >= p.N) continue;
+    const float* src = p.part_o + (int64_t)slot0 * (BM * DV) + (c4 * BM + r) * 4;
+    floatx4 v[kMaxRanges];
+#pragma unroll
+    for (int j = 0; j < kMaxRanges; ++j)
+      v[j] = j < nch ? *reinterpret_cast<const floatx4*>(src + (int64_t)j * (BM * DV)) : floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMaxRanges; ++j) acc += w_s[j][rr] * v[j];
     // chunk c4 = db*8 + r4*2 + g covers dv = db*32 + r4*8 + g*4 .. +4
     const int dv0 = (c4 >> 3) * 32 + ((c4 >> 1) & 3) * 8 + (c4 & 1) * 4;
     bf16x4 o4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * inv);
+    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
     *reinterpret_cast<bf16x4*>(ob + (int64_t)qr * p.o_sn + dv0) = o4;
-    if (c4 == 0 && p.lse)
-      p.lse[b * p.l_sb + h * p.l_sh + qr] = ok ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
   }
 }
 

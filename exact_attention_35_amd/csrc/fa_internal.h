@@ -36,6 +36,8 @@ struct Params {
 // Query-tile height of the matrix-core kernel, and the key-tile width.
 constexpr int kMfmaBM = 128;
 constexpr int kMfmaBN = 64;
+// Most key ranges a split query tile is cut into (the merge kernel's bound).
+constexpr int kMaxRanges = 16;
 // Query-tile height of the general (vector ALU) kernel.
 constexpr int kGenericBM = 64;
 

@@ -53,7 +53,8 @@ typedef enum {
   FA_ERR_SHAPE = -2,     /* negative size, size too large, or (d, dv) not supported */
   FA_ERR_DTYPE = -3,     /* dtype is not FA_F32 or FA_BF16 */
   FA_ERR_MASK = -4,      /* mask_mode is not FA_MASK_NONE or FA_MASK_CAUSAL */
-  FA_ERR_STRIDE = -5,    /* a negative stride, or rows of out / lse that overlap */
+  FA_ERR_STRIDE = -5,    /* a negative stride, rows of out / lse that overlap, or a bf16
+                            k / v row stride of 2^24 elements or more */
   FA_ERR_ALIGN = -6,     /* a base pointer or row stride not 16-byte aligned (bias: 4-byte) */
   FA_ERR_ALIAS = -7,     /* out or lse overlaps an input, or out overlaps lse */
   FA_ERR_WORKSPACE = -8, /* workspace NULL or smaller than fa_fwd_workspace_size() */

@@ -101,6 +101,7 @@ S = capi.STATUS
     (lambda c: c.s.q.__setitem__(2, -128), "FA_ERR_STRIDE"),
     (lambda c: c.s.out.__setitem__(2, 64), "FA_ERR_STRIDE"),       # rows overlap (dv=128)
     (lambda c: c.s.lse.__setitem__(1, 50), "FA_ERR_STRIDE"),       # heads overlap (N=100)
+    (lambda c: c.s.k.__setitem__(2, 1 << 24), "FA_ERR_STRIDE"),    # key tile offsets overflow
     (lambda c: setattr(c, "q", BASE + 2), "FA_ERR_ALIGN"),
     (lambda c: setattr(c, "out", c.out + 8), "FA_ERR_ALIGN"),
     (lambda c: c.s.k.__setitem__(2, 132), "FA_ERR_ALIGN"),         # 264-byte rows
