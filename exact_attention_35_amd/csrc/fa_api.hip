@@ -251,6 +251,7 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
   p.causal = P.mask == FA_MASK_CAUSAL;
   p.bias_vec4 = P.bias && aligned(P.bias, 16) && s.bias[0] % 4 == 0 && s.bias[1] % 4 == 0 && s.bias[2] % 4 == 0;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.d));
+  p.scale = (float)(1.0 / std::sqrt((double)P.d));
   p.n_qt = pl.n_qt;
   p.chunk_tiles = pl.chunk_tiles;
   if (pl.ws_bytes > 0) {

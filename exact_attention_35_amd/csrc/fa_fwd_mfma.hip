@@ -47,6 +47,8 @@
 //    ranges of each tile in range order (deterministic; no atomics):
 //    m = max_p m_p, l = sum_p 2^(m_p-m) l_p, o = sum_p 2^(m_p-m) o_p, O = o / l.
 
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -59,7 +61,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-#define GLB_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -89,36 +92,32 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
 // go into an LDS stage, 16 bytes per lane per instruction, chunk-swizzled. Lane
 // `lane` of instruction i of wave `wave` fills 16-byte slot (wave*NLD + i)*64 + lane,
 // i.e. row slot/CH, physical chunk slot%CH, which holds logical chunk
-// (slot%CH) ^ (row mod CH). The per-lane byte offsets within a tile do not depend on
-// the tile, so they are computed once; rows past the sequence end (tail tile only)
-// are clamped to the last row.
+// (slot%CH) ^ (row mod CH). The loads go through a buffer resource whose base is the
+// tile's first row and whose size covers only the rows that exist, so the per-lane
+// byte offsets do not depend on the tile, and the rows past the sequence end (tail
+// tile only) read as zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const __bf16* base, int64_t sn, int kv0, int N) {
+  const int rows = min(kMfmaBN, N - kv0);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(base + (int64_t)kv0 * sn), 0,
+                                           rows * (int)sn * 2, kBufferWord3);
+}
+
 template <int W, int NLD>
 struct TileCopy {
   static constexpr int CH = W / 8;
   int off[NLD];  // byte offset of this lane's 16 bytes from the tile's first row
-  __device__ __forceinline__ static int slot_row(int wave, int i, int lane) { return ((wave * NLD + i) * 64 + lane) / CH; }
-  __device__ __forceinline__ static int slot_col(int wave, int i, int lane) {
-    const int slot = (wave * NLD + i) * 64 + lane;
-    return ((slot % CH) ^ ((slot / CH) & (CH - 1))) * 16;
-  }
   __device__ __forceinline__ void init(int64_t sn, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) off[i] = (int)(slot_row(wave, i, lane) * sn * 2) + slot_col(wave, i, lane);
-  }
-  __device__ __forceinline__ void copy(unsigned char* stage, const __bf16* base, int64_t sn, int kv0,
-                                       int N, int wave, int lane) const {
-    const unsigned char* tile = reinterpret_cast<const unsigned char*>(base + (int64_t)kv0 * sn);
-    if (kv0 + kMfmaBN <= N) {
-#pragma unroll
-      for (int i = 0; i < NLD; ++i)
-        __builtin_amdgcn_global_load_lds(GLB_PTR(tile + off[i]), LDS_PTR(void, stage + (wave * NLD + i) * 1024), 16, 0, 0);
-    } else {  // tail tile: rows past the end read the last row
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int o = (int)(min(slot_row(wave, i, lane), N - 1 - kv0) * sn * 2) + slot_col(wave, i, lane);
-        __builtin_amdgcn_global_load_lds(GLB_PTR(tile + o), LDS_PTR(void, stage + (wave * NLD + i) * 1024), 16, 0, 0);
-      }
+    for (int i = 0; i < NLD; ++i) {
+      const int slot = (wave * NLD + i) * 64 + lane;
+      const int row = slot / CH;
+      off[i] = (int)(row * sn * 2) + ((slot % CH) ^ (row & (CH - 1))) * 16;
     }
+  }
+  __device__ __forceinline__ void copy(unsigned char* stage, __amdgpu_buffer_rsrc_t r, int wave) const {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, stage + (wave * NLD + i) * 1024), 16, off[i], 0, 0, 0);
   }
 };
 
@@ -163,13 +162,67 @@ __device__ __forceinline__ Unit decode_unit(const Params& p, int u, int BM, int 
   return w;
 }
 
+// ---- compile-time helpers of the interleaved tile body ----
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// The softmax of one tile as a list of micro-steps, in dependency order:
+//   [0, NPRE)            bias only: x = s / sqrt(d) + bias, one element each
+//   [MAX0, MAX0 + 16)    block max: two chains of 8 steps (one chain per key block)
+//   XCH                  half-wave exchange of the max, reference, alpha, -reference
+//   [ELT0, ELT0 + 34)    step k: exponential of element k (k < 32), and the fp32 sum
+//                        and bf16 conversion of element k - 2 (k >= 2)
+//   UPD                  normaliser update
+// Each step has an estimated cost in clocks; the steps are spread over the tile's
+// matrix instructions so that every slot carries about the same vector ALU time.
+template <bool BIAS>
+struct SmPlan {
+  static constexpr int NPRE = BIAS ? 32 : 0;
+  static constexpr int MAX0 = NPRE;
+  static constexpr int XCH = MAX0 + 16;
+  static constexpr int ELT0 = XCH + 1;
+  static constexpr int UPD = ELT0 + 34;
+  static constexpr int NOPS = UPD + 1;
+  static constexpr int cost(int k) {
+    return k < MAX0 ? 4 : k < XCH ? 4 : k == XCH ? 48 : k < UPD ? 20 : 8;
+  }
+  static constexpr int total() {
+    int c = 0;
+    for (int k = 0; k < NOPS; ++k) c += cost(k);
+    return c;
+  }
+  // first step of slot i of ns: the first step whose start time is >= i/ns of the total
+  static constexpr int first(int i, int ns) {
+    if (i >= ns) return NOPS;
+    int c = 0;
+    for (int k = 0; k < NOPS; ++k) {
+      if ((long)c * ns >= (long)i * total()) return k;
+      c += cost(k);
+    }
+    return NOPS;
+  }
+};
+
+// Softmax state of one tile, shared by its micro-steps.
+struct SmState {
+  float mx[2];   // block max of the two key blocks (per lane)
+  float nref;    // minus the reference, or 0 while no allowed key has been seen
+  float ps[4];   // partial fp32 sums of the probabilities
+  float pf[32];  // probabilities awaiting their sum and bf16 conversion
+};
+
 template <int D, int DV, bool BIAS>
 __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   using C = Cfg<D, DV>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
-  // LDS stages: K(0), K(1), V(0), V(1)
-  auto kst = [&](int i) { return smem + (i & 1) * C::KTILE; };
-  auto vst = [&](int i) { return smem + 2 * C::KTILE + (i & 1) * C::VTILE; };
+  // LDS stages, one array each: the compiler can then tell that a copy into one stage
+  // never overlaps operand reads from the other, and does not wait for the copy.
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[C::KTILE], k_lds1[C::KTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[C::VTILE], v_lds1[C::VTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -229,6 +282,17 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     const int dbp = (C::VCH == 16 && hh) ? (db ^ 2) : db;  // chunk bit 3 flipped by hh
     return (16 * sg + 8 * hh) * (DV * 2) + voff[dbp];
   };
+  auto k_operand = [&](const unsigned char* ks, int kk, int kb) {
+    return *reinterpret_cast<const bf16x8*>(ks + kb * 32 * (D * 2) + koff[kk]);
+  };
+  auto v_operand = [&](const unsigned char* vs, int sg, int db) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + vaddr(sg, 0, db)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + vaddr(sg, 1, db)));
+    bf16x8 a;
+    a.lo = __builtin_bit_cast(bf16x4, lo);
+    a.hi = __builtin_bit_cast(bf16x4, hi);
+    return a;
+  };
 
   floatx16 oacc[C::NDB];
 #pragma unroll
@@ -236,32 +300,24 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   float m_ref = -INFINITY;  // reference (base 2); same in both half-waves
   float l_run = 0.f;        // this half-wave's share of the normaliser
 
+  // S^T(tile) = K Q^T: 2 key blocks x KK dim steps (the two chains alternate).
   auto qk = [&](const unsigned char* ks, floatx16 (&s)[2]) {
     s[0] = floatx16{};
     s[1] = floatx16{};
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * (D * 2) + koff[kk]);
-        s[kb] = mfma32(a, qreg[kk], s[kb]);
-      }
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(k_operand(ks, kk, kb), qreg[kk], s[kb]);
   };
+  // O^T += V^T P^T over the tile's 4 groups of 16 keys; dv blocks innermost.
   auto pv = [&](const unsigned char* vs, const bf16x8 (&pk)[4]) {
 #pragma unroll
     for (int sg = 0; sg < 4; ++sg)
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + vaddr(sg, 0, db)));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + vaddr(sg, 1, db)));
-        bf16x8 a;
-        a.lo = __builtin_bit_cast(bf16x4, lo);
-        a.hi = __builtin_bit_cast(bf16x4, hi);
-        oacc[db] = mfma32(a, pk[sg], oacc[db]);
-      }
+      for (int db = 0; db < C::NDB; ++db) oacc[db] = mfma32(v_operand(vs, sg, db), pk[sg], oacc[db]);
   };
   float bcur[BIAS ? 32 : 1];
-  auto load_bias = [&](float (&bv)[BIAS ? 32 : 1], int kv0) {
+  auto load_bias = [&](int kv0) {
     if constexpr (BIAS) {
       if (p.bias_vec4 && kv0 + C::BN <= N) {
 #pragma unroll
@@ -270,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
           for (int r4 = 0; r4 < 4; ++r4) {
             const floatx4 t4 = *reinterpret_cast<const floatx4*>(brow + kv0 + kb * 32 + r4 * 8 + g * 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bv[kb * 16 + r4 * 4 + e] = t4[e];
+            for (int e = 0; e < 4; ++e) bcur[kb * 16 + r4 * 4 + e] = t4[e];
           }
       } else {
 #pragma unroll
@@ -279,21 +335,59 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
           for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              bv[kb * 16 + r4 * 4 + e] = brow[min(kv0 + kb * 32 + r4 * 8 + g * 4 + e, N - 1)];
+              bcur[kb * 16 + r4 * 4 + e] = brow[min(kv0 + kb * 32 + r4 * 8 + g * 4 + e, N - 1)];
       }
     }
   };
+  // Factor from the (biased) score to base-2 logits: without a bias the raw dot
+  // product is scaled by log2(e)/sqrt(d); with one, x = s/sqrt(d) + bias is formed
+  // first and scaled by log2(e).
+  const float cs = BIAS ? kLog2e : p.scale_log2;
 
-  // softmax of one tile: scores s (raw dot products) -> bf16 P operands, rescale
-  // factor alpha for o and l, fp32 row-sum added to l_run.
-  auto softmax = [&](floatx16 (&s)[2], bf16x8 (&pk)[4], int kv0, bool edge, float& alpha) {
-    const float cs = BIAS ? 1.f : p.scale_log2;  // factor from s to base-2 logits
-    if constexpr (BIAS) {
+  // micro-step k of the softmax of scores s (see SmPlan); writes pk and alpha
+  auto sm_step = [&](auto K, SmState& st, floatx16 (&s)[2], bf16x8 (&pk)[4], float& alpha) {
+    using Pl = SmPlan<BIAS>;
+    constexpr int k = decltype(K)::value;
+    if constexpr (k < Pl::MAX0) {
+      s[k / 16][k % 16] = fmaf(s[k / 16][k % 16], p.scale, bcur[k]);
+    } else if constexpr (k < Pl::XCH) {
+      constexpr int c = (k - Pl::MAX0) & 1, j = (k - Pl::MAX0) >> 1;
+      if constexpr (j == 0) st.mx[c] = fmaxf(fmaxf(s[c][0], s[c][1]), s[c][2]);
+      else if constexpr (j < 7) st.mx[c] = fmaxf(fmaxf(st.mx[c], s[c][2 * j + 1]), s[c][2 * j + 2]);
+      else st.mx[c] = fmaxf(st.mx[c], s[c][15]);
+    } else if constexpr (k == Pl::XCH) {
+      float bmax = fmaxf(st.mx[0], st.mx[1]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+      bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cs;
+      // move the reference only when the block max exceeds it by more than kTau
+      const bool move = bmax > m_ref + kTau;
+      const float new_ref = move ? bmax : m_ref;
+      alpha = move ? __builtin_amdgcn_exp2f(m_ref - new_ref) : 1.f;  // exp2(-inf) = 0
+      m_ref = new_ref;
+      st.nref = (new_ref == -INFINITY) ? 0.f : -new_ref;  // no allowed key yet: add nothing
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], p.scale_log2, bcur[kb * 16 + r] * kLog2e);
+      for (int i = 0; i < 4; ++i) st.ps[i] = 0.f;
+    } else if constexpr (k < Pl::UPD) {
+      constexpr int e = k - Pl::ELT0;
+      if constexpr (e < 32) st.pf[e] = __builtin_amdgcn_exp2f(fmaf(s[e / 16][e % 16], cs, st.nref));
+      if constexpr (e >= 2) {
+        constexpr int f = e - 2;
+        st.ps[f & 3] += st.pf[f];
+        if constexpr (f & 1) {
+          constexpr int r = f % 16;
+          pk[(f / 16) * 2 + r / 8][r % 8 - 1] = (__bf16)st.pf[f - 1];
+          pk[(f / 16) * 2 + r / 8][r % 8] = (__bf16)st.pf[f];
+        }
+      }
+    } else {
+      l_run = alpha * l_run + ((st.ps[0] + st.ps[1]) + (st.ps[2] + st.ps[3]));
     }
+  };
+  // The general softmax (any tile, with element masks when `edge`): same arithmetic.
+  auto softmax = [&](floatx16 (&s)[2], bf16x8 (&pk)[4], int kv0, bool edge, float& alpha) {
+    using Pl = SmPlan<BIAS>;
+    SmState st;
+    static_for<0, Pl::MAX0>([&](auto K) { sm_step(K, st, s, pk, alpha); });
     if (edge) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -303,86 +397,106 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
           if (key >= N || (p.causal && key > qi)) s[kb][r] = -INFINITY;
         }
     }
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[kb][r]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32)) * cs;
-    // move the reference only when the block max exceeds it by more than kTau
-    const bool move = bmax > m_ref + kTau;
-    const float new_ref = move ? bmax : m_ref;
-    alpha = move ? __builtin_amdgcn_exp2f(m_ref - new_ref) : 1.f;  // exp2(-inf) = 0
-    m_ref = new_ref;
-    const float nref = (new_ref == -INFINITY) ? 0.f : -new_ref;  // no allowed key yet: add nothing
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][hs * 8 + e], cs, nref));
-          pk[kb * 2 + hs][e] = (__bf16)pe;
-          psum += pe;
-        }
-    l_run = alpha * l_run + psum;
+    static_for<Pl::MAX0, Pl::NOPS>([&](auto K) { sm_step(K, st, s, pk, alpha); });
   };
 
-  // ---- prologue: K(t_begin), K(t_begin+1), V(t_begin) into LDS; scores of t_begin ----
+  // The steady-state tile body: the scores of tile t+1 and P(t-1) V(t-1) on the
+  // matrix cores, the softmax of tile t on the vector ALUs, as one fixed sequence
+  // of NS slots. Slot i issues matrix instruction i (the QK^T ones first, then the
+  // P V ones), the LDS operand read of instruction i + LA, and its share of the
+  // softmax micro-steps; sched_barrier keeps the compiler from regrouping them.
+  auto fused = [&](const unsigned char* ks, const unsigned char* vs, floatx16 (&sc)[2], floatx16 (&sn)[2],
+                   bf16x8 (&pc)[4], const bf16x8 (&pp)[4], float& alpha) {
+    using Pl = SmPlan<BIAS>;
+    constexpr int NQ = 2 * C::KK, NP = 4 * C::NDB, NS = NQ + NP;
+    constexpr int LA = 3;  // operand reads run this many instructions ahead
+    auto operand = [&](auto J) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j < NQ) return k_operand(ks, j / 2, j % 2);
+      else return v_operand(vs, (j - NQ) / C::NDB, (j - NQ) % C::NDB);
+    };
+    bf16x8 ring[LA];
+    static_for<0, LA>([&](auto J) { ring[J] = operand(J); });
+    sn[0] = floatx16{};
+    sn[1] = floatx16{};
+    SmState st;
+    static_for<0, NS>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const bf16x8 a = ring[i % LA];
+      if constexpr (i + LA < NS) ring[i % LA] = operand(std::integral_constant<int, i + LA>{});
+      if constexpr (i < NQ) {
+        sn[i % 2] = mfma32(a, qreg[i / 2], sn[i % 2]);
+      } else {
+        constexpr int j = i - NQ;
+        oacc[j % C::NDB] = mfma32(a, pp[j / C::NDB], oacc[j % C::NDB]);
+      }
+      static_for<Pl::first(i, NS), Pl::first(i + 1, NS)>([&](auto K) { sm_step(K, st, sc, pc, alpha); });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
   TileCopy<D, C::KLD> kcp;
   TileCopy<DV, C::VLD> vcp;
   kcp.init(p.k_sn, wave, lane);
   vcp.init(p.v_sn, wave, lane);
-  kcp.copy(kst(t_begin), kp, p.k_sn, t_begin * C::BN, N, wave, lane);
-  if (t_begin + 1 < t_end) kcp.copy(kst(t_begin + 1), kp, p.k_sn, (t_begin + 1) * C::BN, N, wave, lane);
-  vcp.copy(vst(t_begin), vp, p.v_sn, t_begin * C::BN, N, wave, lane);
+  auto copy_k = [&](unsigned char* st, int t) { kcp.copy(st, tile_rsrc(kp, p.k_sn, t * C::BN, N), wave); };
+  auto copy_v = [&](unsigned char* st, int t) { vcp.copy(st, tile_rsrc(vp, p.v_sn, t * C::BN, N), wave); };
+
+  // ---- prologue: K(t_begin), K(t_begin+1) into LDS; scores of t_begin ----
+  copy_k(k_lds0, t_begin);
+  if (t_begin + 1 < t_end) copy_k(k_lds1, t_begin + 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // One key tile. `sc` holds the raw scores of tile t; the scores of tile t+1 are
-  // computed into `sn` while tile t's softmax runs. The caller alternates the two
-  // buffers, so no register copy is needed between tiles.
-  auto tile_step = [&](int t, floatx16 (&sc)[2], floatx16 (&sn)[2]) {
-    // K(t+1) and V(t) have landed for every wave, and no wave still reads the stages
-    // refilled below (K(t) was read for tile t's scores, V(t-1) by P V of tile t-1)
+
+  // Iteration t (stage parity PAR = (t - t_begin) mod 2): the matrix cores compute the
+  // scores of tile t+1 and add P(t-1) V(t-1) into o while the vector ALUs run the
+  // softmax of tile t; the copies of K(t+2) and V(t) are in flight meanwhile. K(t)
+  // and V(t) live in stage PAR. `sc`/`sn` hold the scores of tiles t and t+1, `pc`/`pp`
+  // the bf16 probabilities of tiles t and t-1; the caller swaps the roles every
+  // iteration, so no register copies are needed. o is rescaled by alpha(t-1) before
+  // P(t-1) V(t-1) is added.
+  float alpha_prev = 1.f;
+  auto step = [&](auto PARc, int t, floatx16 (&sc)[2], floatx16 (&sn)[2], bf16x8 (&pc)[4],
+                  const bf16x8 (&pp)[4]) {
+    constexpr int PAR = decltype(PARc)::value;
+    unsigned char* k_same = PAR ? k_lds1 : k_lds0;   // K(t), refilled with K(t+2)
+    unsigned char* k_next = PAR ? k_lds0 : k_lds1;   // K(t+1)
+    unsigned char* v_same = PAR ? v_lds1 : v_lds0;   // filled with V(t)
+    unsigned char* v_prev = PAR ? v_lds0 : v_lds1;   // V(t-1)
+    // K(t+1) and V(t-1) have landed for every wave, and no wave still reads the stages
+    // refilled below (K(t) was read for the scores of tile t, V(t-2) by P V of t-2)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // bias of this tile first: waiting for it later leaves the copies below in flight
+    if (t + 2 < t_end) copy_k(k_same, t + 2);
+    if (t < t_end) copy_v(v_same, t);
     if constexpr (BIAS) {
-      if (t < tw_end) load_bias(bcur, t * C::BN);
+      if (t < tw_end) load_bias(t * C::BN);
     }
-    if (t + 2 < t_end) kcp.copy(kst(t + 2), kp, p.k_sn, (t + 2) * C::BN, N, wave, lane);
-    if (t + 1 < t_end) vcp.copy(vst(t + 1), vp, p.v_sn, (t + 1) * C::BN, N, wave, lane);
-
     const int kv0 = t * C::BN;
     const bool do_qk = t + 1 < tw_end;
     const bool do_sm = t < tw_end;
+    const bool do_pv = t > t_begin && t - 1 < tw_end;
     const bool edge = (kv0 + C::BN > N) || (p.causal && kv0 + C::BN - 1 > wq0);
-
-    bf16x8 pcur[4];
-    float alpha = 1.f;
-    // scores of tile t+1 on the matrix cores while the vector ALUs run tile t's softmax
-    if (do_qk && do_sm && !edge) {
-      qk(kst(t + 1), sn);
-      softmax(sc, pcur, kv0, false, alpha);
-    } else {
-      if (do_qk) qk(kst(t + 1), sn);
-      if (do_sm) softmax(sc, pcur, kv0, edge, alpha);
-    }
-    if (do_sm) {
-      // o_{t-1} is rescaled by alpha_t before P(t) V(t) is added
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+    if (do_pv && __builtin_amdgcn_ballot_w64(alpha_prev != 1.f)) {
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
-      }
-      pv(vst(t), pcur);
+      for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha_prev;
     }
+    float alpha = 1.f;
+    if (do_qk && do_sm && do_pv && !edge) {
+      fused(k_next, v_prev, sc, sn, pc, pp, alpha);
+    } else {
+      if (do_qk) qk(k_next, sn);
+      if (do_sm) softmax(sc, pc, kv0, edge, alpha);
+      if (do_pv) pv(v_prev, pp);
+    }
+    alpha_prev = alpha;
   };
-  floatx16 s0[2], s1[2];
-  if (t_begin < tw_end) qk(kst(t_begin), s0);
-  for (int t = t_begin; t < t_end; t += 2) {
-    tile_step(t, s0, s1);
-    if (t + 1 < t_end) tile_step(t + 1, s1, s0);
+  floatx16 sA[2], sB[2];
+  bf16x8 pA[4], pB[4];
+  if (t_begin < tw_end) qk(k_lds0, sA);
+  for (int t = t_begin; t <= t_end; t += 2) {
+    step(std::integral_constant<int, 0>{}, t, sA, sB, pA, pB);
+    if (t + 1 <= t_end) step(std::integral_constant<int, 1>{}, t + 1, sB, sA, pB, pA);
   }
 
   // ---- epilogue ----
@@ -503,6 +617,18 @@ __global__ __launch_bounds__(256) void merge_split(Params p) {
     *reinterpret_cast<bf16x4*>(ob + (int64_t)qr * p.o_sn + dv0) = o4;
   }
 }
+
+// Every variant is instantiated explicitly: the host pass then emits a launch stub
+// for each of them (implicit instantiation through the launch macro alone left all
+// but one of them undefined with this compiler).
+template __global__ void fwd_mfma<64, 64, false>(Params);
+template __global__ void fwd_mfma<64, 64, true>(Params);
+template __global__ void fwd_mfma<64, 128, false>(Params);
+template __global__ void fwd_mfma<64, 128, true>(Params);
+template __global__ void fwd_mfma<128, 64, false>(Params);
+template __global__ void fwd_mfma<128, 64, true>(Params);
+template __global__ void fwd_mfma<128, 128, false>(Params);
+template __global__ void fwd_mfma<128, 128, true>(Params);
 
 template <int D, int DV>
 hipError_t launch_dd(const Params& p, int grid, int merge_grid, hipStream_t stream) {

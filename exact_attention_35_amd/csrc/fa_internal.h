@@ -25,6 +25,7 @@ struct Params {
   int causal;
   int bias_vec4;      // bias base 16-byte aligned and row stride a multiple of 4
   float scale_log2;   // log2(e) / sqrt(d): scores in base-2 units
+  float scale;        // 1 / sqrt(d)
   // Work decomposition. A unit is (batch*head, query tile, range of key tiles).
   int n_qt;           // query tiles per (b, h)
   int chunk_tiles;    // 0: no split; else key tiles per range (ranges of a tile are balanced)
