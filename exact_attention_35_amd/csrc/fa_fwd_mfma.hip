@@ -102,7 +102,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const __bf16* base, 
                                            rows * (int)sn * 2, kBufferWord3);
 }
 
-template <int W, int NLD>
+// XOR keys of the two LDS layouts (16-byte chunk index ^= key(row)):
+//  * K rows: key = row mod CH. The A-operand read of Q K^T has 8 (or 16) lanes
+//    on consecutive rows at one logical chunk, which the key spreads over distinct
+//    banks.
+//  * V rows: key = s(row mod 4) mod CH with s = (0, 10, 4, 14). A transposing read of
+//    P V has each 16-lane group on 4 consecutive rows x 2 logical chunks, and each
+//    32-lane half on 4 rows x 4 chunks; s makes both sets hit distinct banks whether
+//    the LDS serves 128 or 256 bytes per clock. The key only depends on row mod 4.
+__device__ __forceinline__ constexpr int v_swizzle_key(int row) { return ((row & 1) * 10 + (row & 2) * 2); }
+
+template <int W, int NLD, bool VKEY>
 struct TileCopy {
   static constexpr int CH = W / 8;
   int off[NLD];  // byte offset of this lane's 16 bytes from the tile's first row
@@ -111,7 +121,8 @@ struct TileCopy {
     for (int i = 0; i < NLD; ++i) {
       const int slot = (wave * NLD + i) * 64 + lane;
       const int row = slot / CH;
-      off[i] = (int)(row * sn * 2) + ((slot % CH) ^ (row & (CH - 1))) * 16;
+      const int key = (VKEY ? v_swizzle_key(row) : row) & (CH - 1);
+      off[i] = (int)(row * sn * 2) + ((slot % CH) ^ key) * 16;
     }
   }
   __device__ __forceinline__ void copy(unsigned char* stage, __amdgpu_buffer_rsrc_t r, int wave) const {
@@ -267,21 +278,18 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     koff[kk] = l32 * (D * 2) + (((2 * kk + g) ^ (l32 & (C::KCH - 1))) * 16);
   // V operand (transposing read): within a 16-lane group G, lane L reads row
   // k0 + L/4 at dv d0 + 4*(L%4), k0 = 16*sg + 8*hh + 4*g, d0 = 32*db + 16*(G&1).
-  // The row's swizzle key (row mod VCH) is 8*hh + 4*g + L/4 for VCH = 16 and
-  // 4*g + L/4 for VCH = 8: sg never enters it, and hh only flips chunk bit 3 when
-  // VCH = 16, i.e. maps dv block db to db ^ 2. So NDB base offsets cover all reads.
+  // The row's swizzle key depends on the row mod 4 = L/4 only, so one base offset
+  // per dv block covers every (sg, hh).
   const int G = lane >> 4, L = lane & 15;
   const int vrow = 4 * g + (L >> 2);
+  const int vkey = v_swizzle_key(L >> 2) & (C::VCH - 1);
   int voff[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) {
     const int col = 32 * db + 16 * (G & 1) + 4 * (L & 3);
-    voff[db] = vrow * (DV * 2) + (((col >> 3) ^ (vrow & (C::VCH - 1))) * 16) + (col & 7) * 2;
+    voff[db] = vrow * (DV * 2) + (((col >> 3) ^ vkey) * 16) + (col & 7) * 2;
   }
-  auto vaddr = [&](int sg, int hh, int db) {
-    const int dbp = (C::VCH == 16 && hh) ? (db ^ 2) : db;  // chunk bit 3 flipped by hh
-    return (16 * sg + 8 * hh) * (DV * 2) + voff[dbp];
-  };
+  auto vaddr = [&](int sg, int hh, int db) { return (16 * sg + 8 * hh) * (DV * 2) + voff[db]; };
   auto k_operand = [&](const unsigned char* ks, int kk, int kb) {
     return *reinterpret_cast<const bf16x8*>(ks + kb * 32 * (D * 2) + koff[kk]);
   };
@@ -435,8 +443,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     });
   };
 
-  TileCopy<D, C::KLD> kcp;
-  TileCopy<DV, C::VLD> vcp;
+  TileCopy<D, C::KLD, false> kcp;
+  TileCopy<DV, C::VLD, true> vcp;
   kcp.init(p.k_sn, wave, lane);
   vcp.init(p.v_sn, wave, lane);
   auto copy_k = [&](unsigned char* st, int t) { kcp.copy(st, tile_rsrc(kp, p.k_sn, t * C::BN, N), wave); };
