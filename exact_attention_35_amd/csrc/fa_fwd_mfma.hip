@@ -189,8 +189,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 //   [ELT0, ELT0 + 34)    step k: exponential of element k (k < 32), and the fp32 sum
 //                        and bf16 conversion of element k - 2 (k >= 2)
 //   UPD                  normaliser update
-// Each step has an estimated cost in clocks; the steps are spread over the tile's
-// matrix instructions so that every slot carries about the same vector ALU time.
+// Each step has an estimated cost in clocks. The steps are spread over the NS slots of
+// the fused tile body so that the cumulative cost grows in proportion, except that a
+// step is pulled earlier when it has a deadline: the score registers of key block 0
+// (elements 0..15) are overwritten by the next tile's Q K^T from slot NP on, those of
+// block 1 from slot P2 on, so every step that reads them must come before.
 template <bool BIAS>
 struct SmPlan {
   static constexpr int NPRE = BIAS ? 32 : 0;
@@ -207,15 +210,20 @@ struct SmPlan {
     for (int k = 0; k < NOPS; ++k) c += cost(k);
     return c;
   }
-  // first step of slot i of ns: the first step whose start time is >= i/ns of the total
-  static constexpr int first(int i, int ns) {
-    if (i >= ns) return NOPS;
-    int c = 0;
-    for (int k = 0; k < NOPS; ++k) {
-      if ((long)c * ns >= (long)i * total()) return k;
-      c += cost(k);
+  static constexpr int deadline(int k, int NP, int P2, int NS) {
+    return k < ELT0 + 16 ? NP - 1 : k < ELT0 + 32 ? P2 - 1 : NS - 1;
+  }
+  // number of steps placed in slots 0 .. i-1
+  static constexpr int first(int i, int NP, int P2, int NS) {
+    int k = 0, c = 0;
+    for (int sl = 0; sl < i; ++sl) {
+      const long target = (long)total() * (sl + 1) / NS;
+      while (k < NOPS && (c + cost(k) <= target || deadline(k, NP, P2, NS) <= sl)) {
+        c += cost(k);
+        ++k;
+      }
     }
-    return NOPS;
+    return k;
   }
 };
 
@@ -408,37 +416,42 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     static_for<Pl::MAX0, Pl::NOPS>([&](auto K) { sm_step(K, st, s, pk, alpha); });
   };
 
-  // The steady-state tile body: the scores of tile t+1 and P(t-1) V(t-1) on the
-  // matrix cores, the softmax of tile t on the vector ALUs, as one fixed sequence
-  // of NS slots. Slot i issues matrix instruction i (the QK^T ones first, then the
-  // P V ones), the LDS operand read of instruction i + LA, and its share of the
-  // softmax micro-steps; sched_barrier keeps the compiler from regrouping them.
-  auto fused = [&](const unsigned char* ks, const unsigned char* vs, floatx16 (&sc)[2], floatx16 (&sn)[2],
-                   bf16x8 (&pc)[4], const bf16x8 (&pp)[4], float& alpha) {
+  // The steady-state tile body as one fixed sequence of NS slots. The matrix cores
+  // first add P(t-1) V(t-1) into o (slots 0 .. NP-1), then form the scores of tile
+  // t+1, key block 0 (slots NP .. P2-1) and key block 1 (P2 .. NS-1), into the same
+  // registers that hold the scores of tile t; the vector ALUs run the softmax of
+  // tile t meanwhile, reading each key block before its registers are overwritten.
+  // Slot i issues one matrix instruction, the LDS operand read of the instruction
+  // LA slots ahead, and its share of the softmax micro-steps; sched_barrier keeps
+  // the compiler from regrouping them.
+  auto fused = [&](const unsigned char* ks, const unsigned char* vs, floatx16 (&s)[2], bf16x8 (&pc)[4],
+                   const bf16x8 (&pp)[4], float& alpha) {
     using Pl = SmPlan<BIAS>;
-    constexpr int NQ = 2 * C::KK, NP = 4 * C::NDB, NS = NQ + NP;
-    constexpr int LA = 3;  // operand reads run this many instructions ahead
+    constexpr int NP = 4 * C::NDB, P2 = NP + C::KK, NS = P2 + C::KK;
+    constexpr int LA = 3;  // operand reads run this many slots ahead
+    static_assert(Pl::first(NP, NP, P2, NS) >= Pl::ELT0 + 16 && Pl::first(P2, NP, P2, NS) >= Pl::ELT0 + 32,
+                  "softmax steps must read each key block before it is overwritten");
     auto operand = [&](auto J) {
       constexpr int j = decltype(J)::value;
-      if constexpr (j < NQ) return k_operand(ks, j / 2, j % 2);
-      else return v_operand(vs, (j - NQ) / C::NDB, (j - NQ) % C::NDB);
+      if constexpr (j < NP) return v_operand(vs, j / C::NDB, j % C::NDB);
+      else if constexpr (j < P2) return k_operand(ks, j - NP, 0);
+      else return k_operand(ks, j - P2, 1);
     };
     bf16x8 ring[LA];
     static_for<0, LA>([&](auto J) { ring[J] = operand(J); });
-    sn[0] = floatx16{};
-    sn[1] = floatx16{};
     SmState st;
     static_for<0, NS>([&](auto I) {
       constexpr int i = decltype(I)::value;
       const bf16x8 a = ring[i % LA];
       if constexpr (i + LA < NS) ring[i % LA] = operand(std::integral_constant<int, i + LA>{});
-      if constexpr (i < NQ) {
-        sn[i % 2] = mfma32(a, qreg[i / 2], sn[i % 2]);
+      if constexpr (i < NP) {
+        oacc[i % C::NDB] = mfma32(a, pp[i / C::NDB], oacc[i % C::NDB]);
       } else {
-        constexpr int j = i - NQ;
-        oacc[j % C::NDB] = mfma32(a, pp[j / C::NDB], oacc[j % C::NDB]);
+        constexpr int kb = i < P2 ? 0 : 1, kk = i - (kb ? P2 : NP);
+        s[kb] = mfma32(a, qreg[kk], kk == 0 ? floatx16{} : s[kb]);
       }
-      static_for<Pl::first(i, NS), Pl::first(i + 1, NS)>([&](auto K) { sm_step(K, st, sc, pc, alpha); });
+      static_for<Pl::first(i, NP, P2, NS), Pl::first(i + 1, NP, P2, NS)>(
+          [&](auto K) { sm_step(K, st, s, pc, alpha); });
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -456,16 +469,15 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Iteration t (stage parity PAR = (t - t_begin) mod 2): the matrix cores compute the
-  // scores of tile t+1 and add P(t-1) V(t-1) into o while the vector ALUs run the
-  // softmax of tile t; the copies of K(t+2) and V(t) are in flight meanwhile. K(t)
-  // and V(t) live in stage PAR. `sc`/`sn` hold the scores of tiles t and t+1, `pc`/`pp`
-  // the bf16 probabilities of tiles t and t-1; the caller swaps the roles every
-  // iteration, so no register copies are needed. o is rescaled by alpha(t-1) before
-  // P(t-1) V(t-1) is added.
+  // Iteration t (stage parity PAR = (t - t_begin) mod 2): the matrix cores add
+  // P(t-1) V(t-1) into o and compute the scores of tile t+1 while the vector ALUs run
+  // the softmax of tile t; the copies of K(t+2) and V(t) are in flight meanwhile. K(t)
+  // and V(t) live in stage PAR. `s` holds the scores of tile t on entry and of tile
+  // t+1 on exit; `pc`/`pp` hold the bf16 probabilities of tiles t and t-1, and the
+  // caller swaps their roles every iteration, so no register copies are needed. o is
+  // rescaled by alpha(t-1) before P(t-1) V(t-1) is added.
   float alpha_prev = 1.f;
-  auto step = [&](auto PARc, int t, floatx16 (&sc)[2], floatx16 (&sn)[2], bf16x8 (&pc)[4],
-                  const bf16x8 (&pp)[4]) {
+  auto step = [&](auto PARc, int t, floatx16 (&s)[2], bf16x8 (&pc)[4], const bf16x8 (&pp)[4]) {
     constexpr int PAR = decltype(PARc)::value;
     unsigned char* k_same = PAR ? k_lds1 : k_lds0;   // K(t), refilled with K(t+2)
     unsigned char* k_next = PAR ? k_lds0 : k_lds1;   // K(t+1)
@@ -491,20 +503,20 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     }
     float alpha = 1.f;
     if (do_qk && do_sm && do_pv && !edge) {
-      fused(k_next, v_prev, sc, sn, pc, pp, alpha);
+      fused(k_next, v_prev, s, pc, pp, alpha);
     } else {
-      if (do_qk) qk(k_next, sn);
-      if (do_sm) softmax(sc, pc, kv0, edge, alpha);
+      if (do_sm) softmax(s, pc, kv0, edge, alpha);
+      if (do_qk) qk(k_next, s);
       if (do_pv) pv(v_prev, pp);
     }
     alpha_prev = alpha;
   };
-  floatx16 sA[2], sB[2];
+  floatx16 s[2];
   bf16x8 pA[4], pB[4];
-  if (t_begin < tw_end) qk(k_lds0, sA);
+  if (t_begin < tw_end) qk(k_lds0, s);
   for (int t = t_begin; t <= t_end; t += 2) {
-    step(std::integral_constant<int, 0>{}, t, sA, sB, pA, pB);
-    if (t + 1 <= t_end) step(std::integral_constant<int, 1>{}, t + 1, sB, sA, pB, pA);
+    step(std::integral_constant<int, 0>{}, t, s, pA, pB);
+    if (t + 1 <= t_end) step(std::integral_constant<int, 1>{}, t + 1, s, pB, pA);
   }
 
   // ---- epilogue ----
