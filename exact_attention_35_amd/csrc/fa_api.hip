@@ -210,7 +210,8 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype
   pl.grid = (int)tiles;
   if (tiles <= 0 || tiles >= cus || tiles > kMaxSplitTiles) return pl;
   // Too few query tiles to occupy the chip: cut each tile's key range into ranges
-  // of about `chunk` key tiles, so that about `target` ranges exist in total.
+  // of about `chunk` key tiles, so that about `target` ranges (two workgroups per CU)
+  // exist in total.
   int64_t total = 0;
   for (int qt = 0; qt < pl.n_qt; ++qt) total += BH * qtile_ntiles(N, qt, causal);
   const int64_t target = env_int("FA_SPLIT_UNITS") > 0 ? env_int("FA_SPLIT_UNITS") : 2 * (int64_t)cus;
@@ -218,13 +219,18 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype
   // no query tile may be cut into more than kMaxRanges ranges
   const int64_t nt_max = qtile_ntiles(N, pl.n_qt - 1, causal);
   chunk = std::max<int64_t>(chunk, (nt_max + fa::kMaxRanges - 1) / fa::kMaxRanges);
+  // the ranges must fit in one wave of workgroups: grow the chunk until they do
   int64_t units = 0;
   bool any_split = false;
-  for (int qt = 0; qt < pl.n_qt; ++qt) {
-    const int64_t nt = qtile_ntiles(N, qt, causal);
-    const int64_t nch = (nt + chunk - 1) / chunk;
-    units += BH * nch;
-    any_split |= nch > 1;
+  for (;; ++chunk) {
+    units = 0;
+    any_split = false;
+    for (int qt = 0; qt < pl.n_qt; ++qt) {
+      const int64_t nch = (qtile_ntiles(N, qt, causal) + chunk - 1) / chunk;
+      units += BH * nch;
+      any_split |= nch > 1;
+    }
+    if (units <= target || !any_split) break;
   }
   if (!any_split) return pl;
   pl.chunk_tiles = (int)chunk;

@@ -425,7 +425,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   // LA slots ahead, and its share of the softmax micro-steps; sched_barrier keeps
   // the compiler from regrouping them.
   auto fused = [&](const unsigned char* ks, const unsigned char* vs, floatx16 (&s)[2], bf16x8 (&pc)[4],
-                   const bf16x8 (&pp)[4], float& alpha) {
+                   const bf16x8 (&pp)[4], float& alpha, int next_kv0) {
     using Pl = SmPlan<BIAS>;
     constexpr int NP = 4 * C::NDB, P2 = NP + C::KK, NS = P2 + C::KK;
     constexpr int LA = 3;  // operand reads run this many slots ahead
@@ -452,6 +452,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
       }
       static_for<Pl::first(i, NP, P2, NS), Pl::first(i + 1, NP, P2, NS)>(
           [&](auto K) { sm_step(K, st, s, pc, alpha); });
+      // the bias of the next tile is loaded as soon as this tile's bias steps are done
+      if constexpr (BIAS && Pl::first(i, NP, P2, NS) < Pl::NPRE && Pl::first(i + 1, NP, P2, NS) >= Pl::NPRE)
+        load_bias(next_kv0);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -489,9 +492,6 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     __syncthreads();
     if (t + 2 < t_end) copy_k(k_same, t + 2);
     if (t < t_end) copy_v(v_same, t);
-    if constexpr (BIAS) {
-      if (t < tw_end) load_bias(t * C::BN);
-    }
     const int kv0 = t * C::BN;
     const bool do_qk = t + 1 < tw_end;
     const bool do_sm = t < tw_end;
@@ -503,9 +503,12 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     }
     float alpha = 1.f;
     if (do_qk && do_sm && do_pv && !edge) {
-      fused(k_next, v_prev, s, pc, pp, alpha);
+      fused(k_next, v_prev, s, pc, pp, alpha, kv0 + C::BN);
     } else {
       if (do_sm) softmax(s, pc, kv0, edge, alpha);
+      if constexpr (BIAS) {
+        if (t + 1 < tw_end) load_bias(kv0 + C::BN);  // the bias of tile t+1, one tile ahead
+      }
       if (do_qk) qk(k_next, s);
       if (do_pv) pv(v_prev, pp);
     }
@@ -514,6 +517,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   floatx16 s[2];
   bf16x8 pA[4], pB[4];
   if (t_begin < tw_end) qk(k_lds0, s);
+  if constexpr (BIAS) {
+    if (t_begin < tw_end) load_bias(t_begin * C::BN);
+  }
   for (int t = t_begin; t <= t_end; t += 2) {
     step(std::integral_constant<int, 0>{}, t, s, pA, pB);
     if (t + 1 <= t_end) step(std::integral_constant<int, 1>{}, t + 1, s, pB, pA);
