@@ -208,7 +208,7 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype
   const int64_t BH = B * H;
   const int64_t tiles = BH * pl.n_qt;
   pl.grid = (int)tiles;
-  if (tiles <= 0 || tiles >= cus || tiles > kMaxSplitTiles) return pl;
+  if (tiles <= 0 || tiles >= cus || tiles > kMaxSplitTiles || pl.n_qt > fa::kMaxSplitQTiles) return pl;
   // Too few query tiles to occupy the chip: cut each tile's key range into ranges
   // of about `chunk` key tiles, so that about `target` ranges (two workgroups per CU)
   // exist in total.
@@ -235,7 +235,7 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype
   if (!any_split) return pl;
   pl.chunk_tiles = (int)chunk;
   pl.grid = (int)units;
-  pl.merge_grid = (int)(tiles * (bm / 32));
+  pl.merge_grid = (int)(tiles * (fa::kMergeGroups * dv / 128));
   pl.off_ml = 0;
   pl.off_o = round_up(units * 2 * bm * sizeof(float), 256);
   pl.ws_bytes = round_up(pl.off_o + (size_t)units * bm * dv * sizeof(float), 256);
@@ -260,6 +260,16 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
   p.scale = (float)(1.0 / std::sqrt((double)P.d));
   p.n_qt = pl.n_qt;
   p.chunk_tiles = pl.chunk_tiles;
+  if (pl.chunk_tiles > 0) {  // unit table of the split plan (query tiles from the last)
+    int32_t acc = 0;
+    for (int e = 0; e < pl.n_qt; ++e) {
+      const int64_t nch = (qtile_ntiles(P.N, pl.n_qt - 1 - e, p.causal) + pl.chunk_tiles - 1) / pl.chunk_tiles;
+      p.ubase[e] = acc;
+      p.nchq[e] = (uint8_t)nch;
+      acc += (int32_t)(P.B * P.H * nch);
+    }
+    p.ubase[pl.n_qt] = acc;
+  }
   if (pl.ws_bytes > 0) {
     unsigned char* w = static_cast<unsigned char*>(ws);
     p.part_ml = reinterpret_cast<float*>(w + pl.off_ml);

@@ -155,14 +155,17 @@ __device__ __forceinline__ Unit decode_unit(const Params& p, int u, int BM, int 
     w.nch = 1;
     return w;
   }
-  int base = 0, qt = p.n_qt - 1, nch = 1, nt = 1;
-  for (; qt >= 0; --qt) {
-    nt = qtile_ntiles(p, qt, BM, BN);
-    nch = (nt + p.chunk_tiles - 1) / p.chunk_tiles;
-    if (u < base + BH * nch) break;
-    base += BH * nch;
+  // the last entry e with ubase[e] <= u (ubase increases with e)
+  int lo = 0, hi = p.n_qt - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.ubase[mid] <= u) lo = mid;
+    else hi = mid - 1;
   }
-  const int rem = u - base;
+  const int qt = p.n_qt - 1 - lo;
+  const int nch = p.nchq[lo];
+  const int nt = qtile_ntiles(p, qt, BM, BN);
+  const int rem = u - p.ubase[lo];
   w.qt = qt;
   w.bh = rem / nch;
   const int c = rem % nch;
@@ -548,7 +551,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     return;
   }
 
-  // ---- split: this range's partial state; layout per slot [dv/4][BM][4] ----
+  // ---- split: this range's partial state; layout per slot [BM/32][dv/4][32][4]:
+  // one wave's 32 rows of one 16-byte dv chunk are 512 consecutive bytes ----
   float* po = p.part_o + (int64_t)U.slot * (C::BM * DV);
   float* pml = p.part_ml + (int64_t)U.slot * (2 * C::BM);
 #pragma unroll
@@ -557,7 +561,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     for (int r4 = 0; r4 < 4; ++r4) {
       const int c4 = db * 8 + r4 * 2 + g;
       const floatx4 v4 = {oacc[db][r4 * 4 + 0], oacc[db][r4 * 4 + 1], oacc[db][r4 * 4 + 2], oacc[db][r4 * 4 + 3]};
-      *reinterpret_cast<floatx4*>(po + (c4 * C::BM + row) * 4) = v4;
+      *reinterpret_cast<floatx4*>(po + ((wave * (DV / 4) + c4) * 32 + l32) * 4) = v4;
     }
   if (g == 0) {
     pml[row] = m_ref;
@@ -565,13 +569,18 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   }
 }
 
-// Merge of the partial states of split query tiles. Block = (query tile, b*h, 32-row
-// group). The ranges' (m, l) of the 32 rows are staged in LDS and turned into weights
-// 2^(m_p - m) / l once per row; then every (row, 4-wide dv chunk) item sums its ranges
-// in range order, with all of its loads issued together (at most kMaxRanges ranges).
+// Merge of the partial states of split query tiles. Block = (query tile, b*h, group of
+// RG rows), thread = (row, 16-byte dv chunk), so each thread merges one item and the
+// whole merge costs one memory round trip: every thread first issues the loads of its
+// item in every range, while the first RG threads load their row's (m_p, l_p), turn
+// them into weights 2^(m_p - m) / l (m = max_p m_p, l = sum_p 2^(m_p - m) l_p) and stage
+// them in LDS; then O = sum_p w_p o_p in range order (deterministic).
 template <int DV>
 __global__ __launch_bounds__(256) void merge_split(Params p) {
-  constexpr int BM = kMfmaBM, BN = kMfmaBN, RG = 32;
+  constexpr int BM = kMfmaBM;
+  constexpr int NC4 = DV / 4;    // 16-byte chunks of a row of o
+  constexpr int RG = 256 / NC4;  // rows per block: 8 (dv = 128) or 16 (dv = 64)
+  static_assert(BM / RG == kMergeGroups * DV / 128, "merge grid and block shape disagree");
   __shared__ float w_s[kMaxRanges][RG];
   const int BH = p.B * p.H;
   constexpr int groups = BM / RG;
@@ -580,27 +589,32 @@ __global__ __launch_bounds__(256) void merge_split(Params p) {
   blk /= groups;
   const int bh = blk % BH;
   const int qt = blk / BH;
-  // slot base of this query tile (units enumerate query tiles from the last)
-  int base = 0, nch = 1;
-  for (int t = p.n_qt - 1; t >= qt; --t) {
-    const int kv_len = p.causal ? min(p.N, (t + 1) * BM) : p.N;
-    const int nt = (kv_len + BN - 1) / BN;
-    nch = (nt + p.chunk_tiles - 1) / p.chunk_tiles;
-    if (t > qt) base += BH * nch;
-  }
+  // units enumerate query tiles from the last one
+  const int e = p.n_qt - 1 - qt;
+  const int nch = p.nchq[e];
   if (nch == 1) return;  // written directly by the forward kernel
-  const int slot0 = base + bh * nch;
+  const int slot0 = p.ubase[e] + bh * nch;
   const int b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x;
+  const int rr = tid % RG;
+  const int c4 = tid / RG;
+  const int r = rg * RG + rr;  // row within the query tile
+  const int qr = qt * BM + r;
+  // a slot holds [BM/32][dv/4][32][4] floats: row r, chunk c4 at ((r/32)*NC4 + c4)*32 + r%32
+  const float* src = p.part_o + (int64_t)slot0 * (BM * DV) + (((r >> 5) * NC4 + c4) * 32 + (r & 31)) * 4;
+  floatx4 v[kMaxRanges];
+#pragma unroll
+  for (int j = 0; j < kMaxRanges; ++j)
+    v[j] = j < nch ? *reinterpret_cast<const floatx4*>(src + (int64_t)j * (BM * DV)) : floatx4{0.f, 0.f, 0.f, 0.f};
   if (tid < RG) {
-    const int r = rg * RG + tid;
-    float m = -INFINITY;
     float mp[kMaxRanges], lp[kMaxRanges];
 #pragma unroll
     for (int j = 0; j < kMaxRanges; ++j) {
-      mp[j] = j < nch ? p.part_ml[(int64_t)(slot0 + j) * (2 * BM) + r] : -INFINITY;
-      lp[j] = j < nch ? p.part_ml[(int64_t)(slot0 + j) * (2 * BM) + BM + r] : 0.f;
+      const float* ml = p.part_ml + (int64_t)(slot0 + j) * (2 * BM);
+      mp[j] = j < nch ? ml[r] : -INFINITY;
+      lp[j] = j < nch ? ml[BM + r] : 0.f;
     }
+    float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kMaxRanges; ++j) m = fmaxf(m, mp[j]);
     float l = 0.f;
@@ -614,34 +628,22 @@ __global__ __launch_bounds__(256) void merge_split(Params p) {
     const bool ok = m != -INFINITY && l > 0.f;
     const float inv = ok ? 1.f / l : 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j) w_s[j][tid] = ok ? mp[j] * inv : 0.f;
-    const int qr = qt * BM + r;
+    for (int j = 0; j < kMaxRanges; ++j) w_s[j][rr] = ok ? mp[j] * inv : 0.f;
     if (p.lse && qr < p.N)
       p.lse[b * p.l_sb + h * p.l_sh + qr] = ok ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  __bf16* ob = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh;
-  for (int idx = tid; idx < RG * (DV / 4); idx += 256) {
-    const int rr = idx % RG;
-    const int r = rg * RG + rr;
-    const int c4 = idx / RG;
-    const int qr = qt * BM + r;
-    if (qr >= p.N) continue;
-    const float* src = p.part_o + (int64_t)slot0 * (BM * DV) + (c4 * BM + r) * 4;
-    floatx4 v[kMaxRanges];
+  if (qr >= p.N) return;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j)
-      v[j] = j < nch ? *reinterpret_cast<const floatx4*>(src + (int64_t)j * (BM * DV)) : floatx4{0.f, 0.f, 0.f, 0.f};
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kMaxRanges; ++j) acc += w_s[j][rr] * v[j];
+  // chunk c4 = db*8 + r4*2 + g covers dv = db*32 + r4*8 + g*4 .. +4
+  const int dv0 = (c4 >> 3) * 32 + ((c4 >> 1) & 3) * 8 + (c4 & 1) * 4;
+  bf16x4 o4;
 #pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j) acc += w_s[j][rr] * v[j];
-    // chunk c4 = db*8 + r4*2 + g covers dv = db*32 + r4*8 + g*4 .. +4
-    const int dv0 = (c4 >> 3) * 32 + ((c4 >> 1) & 3) * 8 + (c4 & 1) * 4;
-    bf16x4 o4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
-    *reinterpret_cast<bf16x4*>(ob + (int64_t)qr * p.o_sn + dv0) = o4;
-  }
+  for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
+  __bf16* orow = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_sn;
+  *reinterpret_cast<bf16x4*>(orow + dv0) = o4;
 }
 
 // Every variant is instantiated explicitly: the host pass then emits a launch stub

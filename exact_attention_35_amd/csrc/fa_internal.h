@@ -6,6 +6,10 @@
 
 namespace fa {
 
+// Most query tiles of a plan that splits over keys (split plans have fewer query
+// tiles than the GPU has compute units).
+constexpr int kMaxSplitQTiles = 256;
+
 // Everything a forward kernel needs, passed by value as the kernel argument.
 // Strides are in elements; the innermost axis of every tensor is contiguous.
 struct Params {
@@ -30,8 +34,12 @@ struct Params {
   int n_qt;           // query tiles per (b, h)
   int chunk_tiles;    // 0: no split; else key tiles per range (ranges of a tile are balanced)
   // Scratch for split problems: one slot per unit.
-  float* part_o;      // [slot][dv/4][BM][4] unnormalised numerators
+  float* part_o;      // [slot][BM/32][dv/4][32][4] unnormalised numerators
   float* part_ml;     // [slot][2][BM]       reference (base 2) and normaliser
+  // Split plans: units enumerate query tiles from the last one; entry e (query tile
+  // n_qt-1-e) owns units [ubase[e], ubase[e+1]), nchq[e] ranges for each (b, h).
+  int32_t ubase[kMaxSplitQTiles + 1];
+  uint8_t nchq[kMaxSplitQTiles];
 };
 
 // Query-tile height of the matrix-core kernel, and the key-tile width.
@@ -39,6 +47,8 @@ constexpr int kMfmaBM = 128;
 constexpr int kMfmaBN = 64;
 // Most key ranges a split query tile is cut into (the merge kernel's bound).
 constexpr int kMaxRanges = 16;
+// Merge blocks per split query tile at dv = 128 (8 rows each; dv = 64 takes half).
+constexpr int kMergeGroups = 16;
 // Query-tile height of the general (vector ALU) kernel.
 constexpr int kGenericBM = 64;
 
