@@ -187,6 +187,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // The softmax of one tile as a list of micro-steps, in dependency order:
 //   [0, NPRE)            bias only: x = s / sqrt(d) + bias, one element each
+//   MSK                  edge tiles only: causal / sequence-end element mask
 //   [MAX0, MAX0 + 16)    block max: two chains of 8 steps (one chain per key block)
 //   XCH                  half-wave exchange of the max, reference, alpha, -reference
 //   [ELT0, ELT0 + 34)    step k: exponential of element k (k < 32), and the fp32 sum
@@ -197,16 +198,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 // step is pulled earlier when it has a deadline: the score registers of key block 0
 // (elements 0..15) are overwritten by the next tile's Q K^T from slot NP on, those of
 // block 1 from slot P2 on, so every step that reads them must come before.
-template <bool BIAS>
+template <bool BIAS, bool EDGE = false>
 struct SmPlan {
   static constexpr int NPRE = BIAS ? 32 : 0;
-  static constexpr int MAX0 = NPRE;
+  static constexpr int MSK = NPRE;
+  static constexpr int MAX0 = NPRE + (EDGE ? 1 : 0);
   static constexpr int XCH = MAX0 + 16;
   static constexpr int ELT0 = XCH + 1;
   static constexpr int UPD = ELT0 + 34;
   static constexpr int NOPS = UPD + 1;
   static constexpr int cost(int k) {
-    return k < MAX0 ? 4 : k < XCH ? 4 : k == XCH ? 48 : k < UPD ? 20 : 8;
+    return k < NPRE ? 4 : k < MAX0 ? 96 : k < XCH ? 4 : k == XCH ? 48 : k < UPD ? 20 : 8;
   }
   static constexpr int total() {
     int c = 0;
@@ -364,11 +366,20 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   const float cs = BIAS ? kLog2e : p.scale_log2;
 
   // micro-step k of the softmax of scores s (see SmPlan); writes pk and alpha
-  auto sm_step = [&](auto K, SmState& st, floatx16 (&s)[2], bf16x8 (&pk)[4], float& alpha) {
-    using Pl = SmPlan<BIAS>;
+  auto sm_step = [&](auto K, SmState& st, floatx16 (&s)[2], bf16x8 (&pk)[4], float& alpha, auto PlanTag,
+                     int kv0) {
+    using Pl = typename decltype(PlanTag)::type;
     constexpr int k = decltype(K)::value;
-    if constexpr (k < Pl::MAX0) {
+    if constexpr (k < Pl::NPRE) {
       s[k / 16][k % 16] = fmaf(s[k / 16][k % 16], p.scale, bcur[k]);
+    } else if constexpr (k < Pl::MAX0) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+          if (key >= N || (p.causal && key > qi)) s[kb][r] = -INFINITY;
+        }
     } else if constexpr (k < Pl::XCH) {
       constexpr int c = (k - Pl::MAX0) & 1, j = (k - Pl::MAX0) >> 1;
       if constexpr (j == 0) st.mx[c] = fmaxf(fmaxf(s[c][0], s[c][1]), s[c][2]);
@@ -403,10 +414,11 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     }
   };
   // The general softmax (any tile, with element masks when `edge`): same arithmetic.
+  const std::common_type<SmPlan<BIAS>> plain_plan;
   auto softmax = [&](floatx16 (&s)[2], bf16x8 (&pk)[4], int kv0, bool edge, float& alpha) {
     using Pl = SmPlan<BIAS>;
     SmState st;
-    static_for<0, Pl::MAX0>([&](auto K) { sm_step(K, st, s, pk, alpha); });
+    static_for<0, Pl::MAX0>([&](auto K) { sm_step(K, st, s, pk, alpha, plain_plan, kv0); });
     if (edge) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -416,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
           if (key >= N || (p.causal && key > qi)) s[kb][r] = -INFINITY;
         }
     }
-    static_for<Pl::MAX0, Pl::NOPS>([&](auto K) { sm_step(K, st, s, pk, alpha); });
+    static_for<Pl::MAX0, Pl::NOPS>([&](auto K) { sm_step(K, st, s, pk, alpha, plain_plan, kv0); });
   };
 
   // The steady-state tile body as one fixed sequence of NS slots. The matrix cores
@@ -454,10 +466,38 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
         s[kb] = mfma32(a, qreg[kk], kk == 0 ? floatx16{} : s[kb]);
       }
       static_for<Pl::first(i, NP, P2, NS), Pl::first(i + 1, NP, P2, NS)>(
-          [&](auto K) { sm_step(K, st, s, pc, alpha); });
+          [&](auto K) { sm_step(K, st, s, pc, alpha, plain_plan, 0); });
       // the bias of the next tile is loaded as soon as this tile's bias steps are done
       if constexpr (BIAS && Pl::first(i, NP, P2, NS) < Pl::NPRE && Pl::first(i + 1, NP, P2, NS) >= Pl::NPRE)
         load_bias(next_kv0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // A wave's last tile (no next scores to form; the causal diagonal tile, or the
+  // last tile of its key range): P(t-1) V(t-1) on the matrix cores while the vector
+  // ALUs run the softmax of tile t, element masks included when EDGE.
+  auto fused_last = [&](const unsigned char* vs, floatx16 (&s)[2], bf16x8 (&pc)[4], const bf16x8 (&pp)[4],
+                        float& alpha, int kv0, auto EDGEc) {
+    constexpr bool EDGE = decltype(EDGEc)::value;
+    using Pl = SmPlan<BIAS, EDGE>;
+    const std::common_type<Pl> plan;
+    constexpr int NP = 4 * C::NDB;
+    constexpr int LA = 3;
+    auto operand = [&](auto J) {
+      constexpr int j = decltype(J)::value;
+      return v_operand(vs, j / C::NDB, j % C::NDB);
+    };
+    bf16x8 ring[LA];
+    static_for<0, LA>([&](auto J) { ring[J] = operand(J); });
+    SmState st;
+    static_for<0, NP>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const bf16x8 a = ring[i % LA];
+      if constexpr (i + LA < NP) ring[i % LA] = operand(std::integral_constant<int, i + LA>{});
+      oacc[i % C::NDB] = mfma32(a, pp[i / C::NDB], oacc[i % C::NDB]);
+      static_for<Pl::first(i, NP, NP, NP), Pl::first(i + 1, NP, NP, NP)>(
+          [&](auto K) { sm_step(K, st, s, pc, alpha, plan, kv0); });
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -507,6 +547,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     float alpha = 1.f;
     if (do_qk && do_sm && do_pv && !edge) {
       fused(k_next, v_prev, s, pc, pp, alpha, kv0 + C::BN);
+    } else if (!do_qk && do_sm && do_pv) {
+      if (edge) fused_last(v_prev, s, pc, pp, alpha, kv0, std::true_type{});
+      else fused_last(v_prev, s, pc, pp, alpha, kv0, std::false_type{});
     } else {
       if (do_sm) softmax(s, pc, kv0, edge, alpha);
       if constexpr (BIAS) {
