@@ -29,7 +29,7 @@ namespace {
 
 using fa::Params;
 
-constexpr int kMaxSplitTiles = 4096;          // query tiles eligible for a split over keys
+constexpr int kMaxSplitTiles = 255;           // (b, h, query tile)s eligible for a split (8-bit fields)
 constexpr int64_t kMaxRowStride = 1 << 24;     // bf16 k/v row stride limit (elements)
 
 struct Range {
@@ -214,7 +214,8 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype
   // exist in total.
   int64_t total = 0;
   for (int qt = 0; qt < pl.n_qt; ++qt) total += BH * qtile_ntiles(N, qt, causal);
-  const int64_t target = env_int("FA_SPLIT_UNITS") > 0 ? env_int("FA_SPLIT_UNITS") : 2 * (int64_t)cus;
+  const int64_t target = std::min<int64_t>(fa::kMaxSplitUnits,
+                                           env_int("FA_SPLIT_UNITS") > 0 ? env_int("FA_SPLIT_UNITS") : 2 * (int64_t)cus);
   int64_t chunk = std::max<int64_t>(1, (total + target - 1) / target);
   // no query tile may be cut into more than kMaxRanges ranges
   const int64_t nt_max = qtile_ntiles(N, pl.n_qt - 1, causal);
@@ -269,6 +270,11 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
       acc += (int32_t)(P.B * P.H * nch);
     }
     p.ubase[pl.n_qt] = acc;
+    for (int e = 0; e < pl.n_qt; ++e)
+      for (int64_t bh = 0; bh < P.B * P.H; ++bh)
+        for (int c = 0; c < p.nchq[e]; ++c)
+          p.unit_info[p.ubase[e] + bh * p.nchq[e] + c] =
+              (uint32_t)(pl.n_qt - 1 - e) | (uint32_t)bh << 8 | (uint32_t)c << 16 | (uint32_t)p.nchq[e] << 24;
   }
   if (pl.ws_bytes > 0) {
     unsigned char* w = static_cast<unsigned char*>(ws);

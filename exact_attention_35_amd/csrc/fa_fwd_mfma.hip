@@ -155,20 +155,13 @@ __device__ __forceinline__ Unit decode_unit(const Params& p, int u, int BM, int 
     w.nch = 1;
     return w;
   }
-  // the last entry e with ubase[e] <= u (ubase increases with e)
-  int lo = 0, hi = p.n_qt - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.ubase[mid] <= u) lo = mid;
-    else hi = mid - 1;
-  }
-  const int qt = p.n_qt - 1 - lo;
-  const int nch = p.nchq[lo];
+  const unsigned info = p.unit_info[u];
+  const int qt = info & 0xff;
+  const int nch = info >> 24;
+  const int c = (info >> 16) & 0xff;
   const int nt = qtile_ntiles(p, qt, BM, BN);
-  const int rem = u - p.ubase[lo];
   w.qt = qt;
-  w.bh = rem / nch;
-  const int c = rem % nch;
+  w.bh = (info >> 8) & 0xff;
   w.t_begin = (int)((int64_t)c * nt / nch);
   w.t_end = (int)((int64_t)(c + 1) * nt / nch);
   w.slot = u;

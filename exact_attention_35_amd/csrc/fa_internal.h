@@ -9,6 +9,8 @@ namespace fa {
 // Most query tiles of a plan that splits over keys (split plans have fewer query
 // tiles than the GPU has compute units).
 constexpr int kMaxSplitQTiles = 256;
+// Most units (workgroups) of a split plan.
+constexpr int kMaxSplitUnits = 512;
 
 // Everything a forward kernel needs, passed by value as the kernel argument.
 // Strides are in elements; the innermost axis of every tensor is contiguous.
@@ -40,6 +42,10 @@ struct Params {
   // n_qt-1-e) owns units [ubase[e], ubase[e+1]), nchq[e] ranges for each (b, h).
   int32_t ubase[kMaxSplitQTiles + 1];
   uint8_t nchq[kMaxSplitQTiles];
+  // Split plans: unit u is query tile (unit_info[u] & 0xff), b*h ((>> 8) & 0xff),
+  // range index ((>> 16) & 0xff) of (>> 24) ranges, so a workgroup decodes its unit
+  // with one load.
+  uint32_t unit_info[kMaxSplitUnits];
 };
 
 // Query-tile height of the matrix-core kernel, and the key-tile width.
