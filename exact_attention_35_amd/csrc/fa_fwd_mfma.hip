@@ -183,22 +183,23 @@ __device__ __forceinline__ void static_for(F&& f) {
 //   MSK                  edge tiles only: causal / sequence-end element mask
 //   [MAX0, MAX0 + 16)    block max: two chains of 8 steps (one chain per key block)
 //   XCH                  half-wave exchange of the max, reference, alpha, -reference
-//   [ELT0, ELT0 + 34)    step k: exponential of element k (k < 32), and the fp32 sum
-//                        and bf16 conversion of element k - 2 (k >= 2)
+//   [ELT0, ELT0+32+LAG)  step k: exponential of element k (k < 32), and the fp32 sum
+//                        and bf16 conversion of element k - LAG (k >= LAG)
 //   UPD                  normaliser update
 // Each step has an estimated cost in clocks. The steps are spread over the NS slots of
 // the fused tile body so that the cumulative cost grows in proportion, except that a
 // step is pulled earlier when it has a deadline: the score registers of key block 0
 // (elements 0..15) are overwritten by the next tile's Q K^T from slot NP on, those of
 // block 1 from slot P2 on, so every step that reads them must come before.
-template <bool BIAS, bool EDGE = false>
+template <bool BIAS, bool EDGE = false, int LAG_ = 2>
 struct SmPlan {
+  static constexpr int LAG = LAG_;  // steps between an exponential and the use of its result
   static constexpr int NPRE = BIAS ? 32 : 0;
   static constexpr int MSK = NPRE;
   static constexpr int MAX0 = NPRE + (EDGE ? 1 : 0);
   static constexpr int XCH = MAX0 + 16;
   static constexpr int ELT0 = XCH + 1;
-  static constexpr int UPD = ELT0 + 34;
+  static constexpr int UPD = ELT0 + 32 + LAG;
   static constexpr int NOPS = UPD + 1;
   static constexpr int cost(int k) {
     return k < NPRE ? 4 : k < MAX0 ? 96 : k < XCH ? 4 : k == XCH ? 48 : k < UPD ? 20 : 8;
@@ -393,8 +394,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     } else if constexpr (k < Pl::UPD) {
       constexpr int e = k - Pl::ELT0;
       if constexpr (e < 32) st.pf[e] = __builtin_amdgcn_exp2f(fmaf(s[e / 16][e % 16], cs, st.nref));
-      if constexpr (e >= 2) {
-        constexpr int f = e - 2;
+      if constexpr (e >= Pl::LAG) {
+        constexpr int f = e - Pl::LAG;
         st.ps[f & 3] += st.pf[f];
         if constexpr (f & 1) {
           constexpr int r = f % 16;
@@ -408,10 +409,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   };
   // The general softmax (any tile, with element masks when `edge`): same arithmetic.
   const std::common_type<SmPlan<BIAS>> plain_plan;
+  // The general softmax runs its steps back to back, so an exponential's result is
+  // used 8 steps later (its latency is not hidden behind matrix instructions here).
+  const std::common_type<SmPlan<BIAS, false, 8>> seq_plan;
   auto softmax = [&](floatx16 (&s)[2], bf16x8 (&pk)[4], int kv0, bool edge, float& alpha) {
-    using Pl = SmPlan<BIAS>;
+    using Pl = SmPlan<BIAS, false, 8>;
     SmState st;
-    static_for<0, Pl::MAX0>([&](auto K) { sm_step(K, st, s, pk, alpha, plain_plan, kv0); });
+    static_for<0, Pl::MAX0>([&](auto K) { sm_step(K, st, s, pk, alpha, seq_plan, kv0); });
     if (edge) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
           if (key >= N || (p.causal && key > qi)) s[kb][r] = -INFINITY;
         }
     }
-    static_for<Pl::MAX0, Pl::NOPS>([&](auto K) { sm_step(K, st, s, pk, alpha, plain_plan, kv0); });
+    static_for<Pl::MAX0, Pl::NOPS>([&](auto K) { sm_step(K, st, s, pk, alpha, seq_plan, kv0); });
   };
 
   // The steady-state tile body as one fixed sequence of NS slots. The matrix cores
@@ -693,6 +697,7 @@ template __global__ void fwd_mfma<128, 64, false>(Params);
 template __global__ void fwd_mfma<128, 64, true>(Params);
 template __global__ void fwd_mfma<128, 128, false>(Params);
 template __global__ void fwd_mfma<128, 128, true>(Params);
+
 
 template <int D, int DV>
 hipError_t launch_dd(const Params& p, int grid, int merge_grid, hipStream_t stream) {
