@@ -59,10 +59,15 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
+// Cache policy of a buffer store (sc0 | sc1): system scope, so the L2 writes the data
+// through instead of keeping it dirty. The split partial states are read by the next
+// kernel only; written through, they need no write-back of the L2 at the kernel's end.
+constexpr int kStoreWriteThrough = 1 | 16;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -142,30 +147,25 @@ __device__ __forceinline__ int qtile_ntiles(const Params& p, int qt, int BM, int
   return (kv_len + BN - 1) / BN;
 }
 
+// Units of a plan without a split are (b*h, query tile) pairs, longest query tile
+// first; a split plan reads its unit from the table. The decode is branch-free, so the
+// table entry and the plan type are read from the kernel arguments in one round trip.
 __device__ __forceinline__ Unit decode_unit(const Params& p, int u, int BM, int BN) {
+  static_assert((kMaxSplitUnits & (kMaxSplitUnits - 1)) == 0, "unit table size must be a power of two");
+  const unsigned info = p.unit_info[u & (kMaxSplitUnits - 1)];  // inside the table for any plan
+  const bool split = p.chunk_tiles != 0;
+  const unsigned BH = (unsigned)(p.B * p.H);
+  const unsigned r = (unsigned)u / BH;
   Unit w;
-  const int BH = p.B * p.H;
-  if (p.chunk_tiles == 0) {  // no split: units ordered longest query tile first
-    w.bh = u % BH;
-    const int r = u / BH;
-    w.qt = p.causal ? (p.n_qt - 1 - r) : r;
-    w.t_begin = 0;
-    w.t_end = qtile_ntiles(p, w.qt, BM, BN);
-    w.slot = -1;
-    w.nch = 1;
-    return w;
-  }
-  const unsigned info = p.unit_info[u];
-  const int qt = info & 0xff;
-  const int nch = info >> 24;
-  const int c = (info >> 16) & 0xff;
-  const int nt = qtile_ntiles(p, qt, BM, BN);
-  w.qt = qt;
-  w.bh = (info >> 8) & 0xff;
-  w.t_begin = (int)((int64_t)c * nt / nch);
-  w.t_end = (int)((int64_t)(c + 1) * nt / nch);
-  w.slot = u;
-  w.nch = nch;
+  w.qt = split ? (int)(info & 0xff) : (p.causal ? p.n_qt - 1 - (int)r : (int)r);
+  w.bh = split ? (int)((info >> 8) & 0xff) : (int)((unsigned)u - r * BH);
+  const unsigned nch = split ? info >> 24 : 1u;
+  const unsigned c = split ? (info >> 16) & 0xff : 0u;
+  const unsigned nt = (unsigned)qtile_ntiles(p, w.qt, BM, BN);
+  w.t_begin = (int)(c * nt / nch);  // c, nt < 2^16
+  w.t_end = (int)((c + 1) * nt / nch);
+  w.slot = split ? u : -1;
+  w.nch = (int)nch;
   return w;
 }
 
@@ -248,6 +248,12 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   const int g = lane >> 5;    // half-wave
   const int l32 = lane & 31;  // query within the wave's 32-row block
 
+  // One word of each cache line of the kernel arguments that the prologue reads, and the
+  // unit's table entry, are read before anything depends on them: these scalar loads
+  // share one memory round trip, and later argument reads hit the scalar cache (a
+  // dependent chain of argument reads costs a round trip per cache line).
+  asm volatile("" ::"s"(p.q), "s"(p.k_sn), "s"(p.b_si), "s"(p.chunk_tiles),
+               "s"(p.unit_info[blockIdx.x & (kMaxSplitUnits - 1)]));
   const Unit U = decode_unit(p, blockIdx.x, C::BM, C::BN);
   const int b = U.bh / p.H;
   const int h = U.bh % p.H;
@@ -593,19 +599,22 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
 
   // ---- split: this range's partial state; layout per slot [BM/32][dv/4][32][4]:
   // one wave's 32 rows of one 16-byte dv chunk are 512 consecutive bytes ----
-  float* po = p.part_o + (int64_t)U.slot * (C::BM * DV);
-  float* pml = p.part_ml + (int64_t)U.slot * (2 * C::BM);
+  const __amdgpu_buffer_rsrc_t po = __builtin_amdgcn_make_buffer_rsrc(
+      p.part_o + (int64_t)U.slot * (C::BM * DV), 0, C::BM * DV * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t pml = __builtin_amdgcn_make_buffer_rsrc(
+      p.part_ml + (int64_t)U.slot * (2 * C::BM), 0, 2 * C::BM * 4, kBufferWord3);
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int c4 = db * 8 + r4 * 2 + g;
       const floatx4 v4 = {oacc[db][r4 * 4 + 0], oacc[db][r4 * 4 + 1], oacc[db][r4 * 4 + 2], oacc[db][r4 * 4 + 3]};
-      *reinterpret_cast<floatx4*>(po + ((wave * (DV / 4) + c4) * 32 + l32) * 4) = v4;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), po,
+                                             ((wave * (DV / 4) + c4) * 32 + l32) * 16, 0, kStoreWriteThrough);
     }
   if (g == 0) {
-    pml[row] = m_ref;
-    pml[C::BM + row] = l_tot;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref), pml, row * 4, 0, kStoreWriteThrough);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_tot), pml, (C::BM + row) * 4, 0, kStoreWriteThrough);
   }
 }
 
