@@ -263,25 +263,24 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
   p.chunk_tiles = pl.chunk_tiles;
   if (pl.chunk_tiles > 0) {  // unit table of the split plan (query tiles from the last)
     int32_t acc = 0;
-    for (int e = 0; e < pl.n_qt; ++e) {
-      const int64_t nch = (qtile_ntiles(P.N, pl.n_qt - 1 - e, p.causal) + pl.chunk_tiles - 1) / pl.chunk_tiles;
-      p.ubase[e] = acc;
-      p.nchq[e] = (uint8_t)nch;
+    for (int qt = pl.n_qt - 1; qt >= 0; --qt) {
+      const int64_t nch = (qtile_ntiles(P.N, qt, p.causal) + pl.chunk_tiles - 1) / pl.chunk_tiles;
+      p.ubase[qt] = acc;
+      p.nchq[qt] = (uint8_t)nch;
+      for (int64_t bh = 0; bh < P.B * P.H; ++bh)
+        for (int c = 0; c < nch; ++c)
+          p.unit_info[acc + bh * nch + c] =
+              (uint32_t)qt | (uint32_t)bh << 8 | (uint32_t)c << 16 | (uint32_t)nch << 24;
       acc += (int32_t)(P.B * P.H * nch);
     }
     p.ubase[pl.n_qt] = acc;
-    for (int e = 0; e < pl.n_qt; ++e)
-      for (int64_t bh = 0; bh < P.B * P.H; ++bh)
-        for (int c = 0; c < p.nchq[e]; ++c)
-          p.unit_info[p.ubase[e] + bh * p.nchq[e] + c] =
-              (uint32_t)(pl.n_qt - 1 - e) | (uint32_t)bh << 8 | (uint32_t)c << 16 | (uint32_t)p.nchq[e] << 24;
   }
   if (pl.ws_bytes > 0) {
     unsigned char* w = static_cast<unsigned char*>(ws);
     p.part_ml = reinterpret_cast<float*>(w + pl.off_ml);
     p.part_o = reinterpret_cast<float*>(w + pl.off_o);
   }
-  hipError_t e = pl.mfma ? fa::launch_mfma_bf16(p, pl.grid, pl.merge_grid, stream)
+  hipError_t e = pl.mfma ? fa::launch_mfma_bf16(p, pl.grid, pl.merge_grid > 0, stream)
                          : fa::launch_generic(p, P.dtype == FA_BF16, stream);
   if (std::getenv("FA_LOG"))
     std::fprintf(stderr, "[fa] %s B=%lld H=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d n_qt=%d chunk=%d grid=%d merge=%d ws=%zu\n",

@@ -618,12 +618,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   }
 }
 
-// Merge of the partial states of split query tiles. Block = (query tile, b*h, group of
-// RG rows), thread = (row, 16-byte dv chunk), so each thread merges one item and the
-// whole merge costs one memory round trip: every thread first issues the loads of its
-// item in every range, while the first RG threads load their row's (m_p, l_p), turn
-// them into weights 2^(m_p - m) / l (m = max_p m_p, l = sum_p 2^(m_p - m) l_p) and stage
-// them in LDS; then O = sum_p w_p o_p in range order (deterministic).
+// Merge of the partial states of split query tiles. Block = (group of RG rows, b*h,
+// query tile) = (blockIdx.x, .y, .z), thread = (row, 16-byte dv chunk), so each thread
+// merges one item and the merge costs one memory round trip after the kernel
+// arguments: every thread first issues the loads of its item in every range, while the
+// first RG threads load their row's (m_p, l_p), turn them into weights 2^(m_p - m) / l
+// (m = max_p m_p, l = sum_p 2^(m_p - m) l_p) and stage them in LDS; then
+// O = sum_p w_p o_p in range order (deterministic).
 template <int DV>
 __global__ __launch_bounds__(256) void merge_split(Params p) {
   constexpr int BM = kMfmaBM;
@@ -631,18 +632,14 @@ __global__ __launch_bounds__(256) void merge_split(Params p) {
   constexpr int RG = 256 / NC4;  // rows per block: 8 (dv = 128) or 16 (dv = 64)
   static_assert(BM / RG == kMergeGroups * DV / 128, "merge grid and block shape disagree");
   __shared__ float w_s[kMaxRanges][RG];
-  const int BH = p.B * p.H;
-  constexpr int groups = BM / RG;
-  int blk = blockIdx.x;
-  const int rg = blk % groups;
-  blk /= groups;
-  const int bh = blk % BH;
-  const int qt = blk / BH;
-  // units enumerate query tiles from the last one
-  const int e = p.n_qt - 1 - qt;
-  const int nch = p.nchq[e];
+  const int rg = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int qt = blockIdx.z;
+  // the argument cache lines used below and the tile's table entries in one round trip
+  asm volatile("" ::"s"(p.out), "s"(p.o_sn), "s"(p.N), "s"(p.part_ml), "s"(p.ubase[qt]), "s"((int)p.nchq[qt]));
+  const int nch = p.nchq[qt];
   if (nch == 1) return;  // written directly by the forward kernel
-  const int slot0 = p.ubase[e] + bh * nch;
+  const int slot0 = p.ubase[qt] + bh * nch;
   const int b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x;
   const int rr = tid % RG;
@@ -709,24 +706,24 @@ template __global__ void fwd_mfma<128, 128, true>(Params);
 
 
 template <int D, int DV>
-hipError_t launch_dd(const Params& p, int grid, int merge_grid, hipStream_t stream) {
+hipError_t launch_dd(const Params& p, int grid, bool merge, hipStream_t stream) {
   if (p.bias)
     hipLaunchKernelGGL((fwd_mfma<D, DV, true>), dim3(grid), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((fwd_mfma<D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || merge_grid == 0) return e;
-  hipLaunchKernelGGL((merge_split<DV>), dim3(merge_grid), dim3(256), 0, stream, p);
+  if (e != hipSuccess || !merge) return e;
+  hipLaunchKernelGGL((merge_split<DV>), dim3(kMergeGroups * DV / 128, p.B * p.H, p.n_qt), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_mfma_bf16(const Params& p, int grid, int merge_grid, hipStream_t stream) {
-  if (p.d == 128 && p.dv == 128) return launch_dd<128, 128>(p, grid, merge_grid, stream);
-  if (p.d == 64 && p.dv == 128) return launch_dd<64, 128>(p, grid, merge_grid, stream);
-  if (p.d == 128 && p.dv == 64) return launch_dd<128, 64>(p, grid, merge_grid, stream);
-  if (p.d == 64 && p.dv == 64) return launch_dd<64, 64>(p, grid, merge_grid, stream);
+hipError_t launch_mfma_bf16(const Params& p, int grid, bool merge, hipStream_t stream) {
+  if (p.d == 128 && p.dv == 128) return launch_dd<128, 128>(p, grid, merge, stream);
+  if (p.d == 64 && p.dv == 128) return launch_dd<64, 128>(p, grid, merge, stream);
+  if (p.d == 128 && p.dv == 64) return launch_dd<128, 64>(p, grid, merge, stream);
+  if (p.d == 64 && p.dv == 64) return launch_dd<64, 64>(p, grid, merge, stream);
   return hipErrorInvalidValue;
 }
 

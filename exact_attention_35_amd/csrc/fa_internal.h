@@ -38,8 +38,8 @@ struct Params {
   // Scratch for split problems: one slot per unit.
   float* part_o;      // [slot][BM/32][dv/4][32][4] unnormalised numerators
   float* part_ml;     // [slot][2][BM]       reference (base 2) and normaliser
-  // Split plans: units enumerate query tiles from the last one; entry e (query tile
-  // n_qt-1-e) owns units [ubase[e], ubase[e+1]), nchq[e] ranges for each (b, h).
+  // Split plans: units enumerate query tiles from the last one; query tile qt owns
+  // units ubase[qt] .. ubase[qt] + B*H*nchq[qt] - 1, nchq[qt] ranges for each (b, h).
   int32_t ubase[kMaxSplitQTiles + 1];
   uint8_t nchq[kMaxSplitQTiles];
   // Split plans: unit u is query tile (unit_info[u] & 0xff), b*h ((>> 8) & 0xff),
@@ -59,7 +59,8 @@ constexpr int kMergeGroups = 16;
 constexpr int kGenericBM = 64;
 
 // Launchers (each returns the hipError_t of the launch).
-hipError_t launch_mfma_bf16(const Params& p, int grid, int merge_grid, hipStream_t stream);
+// grid: forward units; merge: whether split query tiles need the merge kernel.
+hipError_t launch_mfma_bf16(const Params& p, int grid, bool merge, hipStream_t stream);
 hipError_t launch_generic(const Params& p, bool is_bf16, hipStream_t stream);
 
 }  // namespace fa
