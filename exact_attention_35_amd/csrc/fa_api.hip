@@ -14,12 +14,17 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
+#include <random>
 #include <utility>
 
 #include "fa.h"
@@ -29,7 +34,7 @@ namespace {
 
 using fa::Params;
 
-constexpr int kMaxSplitTiles = 255;           // (b, h, query tile)s eligible for a split (8-bit fields)
+constexpr int kMaxSplitBH = 64;  // split plans: b*h fits the unit table's 6-bit field
 constexpr int64_t kMaxRowStride = 1 << 24;     // bf16 k/v row stride limit (elements)
 
 struct Range {
@@ -177,11 +182,17 @@ int device_info(int* dev_out, DevInfo* info) {
 struct Plan {
   bool mfma = false;
   int n_qt = 0;
-  int chunk_tiles = 0;  // 0: no split over keys
+  bool split = false;   // query tiles cut into key ranges (units) merged afterwards
+  struct Ranges {       // the key ranges of one query tile
+    int nch;
+    int begin[fa::kMaxRanges], len[fa::kMaxRanges];
+  };
+  Ranges ranges[fa::kMaxSplitQTiles];
   int grid = 0;         // forward workgroups (units)
-  int merge_grid = 0;   // merge workgroups (0: no merge kernel)
+  int merge_grid = 0;   // blocks of a separate merge kernel (0: no split query tile)
+  int merge_blocks = 0; // merge blocks appended to the forward grid instead
   size_t ws_bytes = 0;
-  size_t off_ml = 0, off_o = 0;
+  size_t off_flag = 0, off_ml = 0, off_o = 0;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -198,6 +209,56 @@ int64_t qtile_ntiles(int64_t N, int qt, bool causal) {
   return (kv + bn - 1) / bn;
 }
 
+// Cost model of the split plans, in key tiles: the second workgroup on a CU runs its
+// tiles about 1.3x slower than the first while both run (the older waves issue first),
+// and the range holding a causal query tile's diagonal costs about 1.5 tiles more
+// (masked tiles; half the waves stop one tile earlier). Units 0 .. cus-1 are the first
+// workgroups of their CUs.
+constexpr double kSecondSlotCost = 1.3;
+constexpr double kDiagonalCost = 1.5;
+
+// Cuts nt key tiles into nch consecutive ranges of about equal cost for units u0 ..
+// u0+nch-1 (range k costs len_k * c_k, plus the diagonal cost for the last range);
+// returns the largest range cost.
+double cut_even(int nt, int nch, int64_t u0, int cus, double diag, Plan::Ranges* r) {
+  double c[fa::kMaxRanges], inv_sum = 0.0, extra = 0.0;
+  for (int k = 0; k < nch; ++k) {
+    c[k] = u0 + k < cus ? 1.0 : kSecondSlotCost;
+    inv_sum += 1.0 / c[k];
+  }
+  extra = diag / c[nch - 1];
+  const double T = (nt + extra) / inv_sum;  // the common cost if tiles were divisible
+  int t = 0;
+  double acc = 0.0, worst = 0.0;
+  for (int k = 0; k < nch; ++k) {
+    acc += T / c[k] - (k == nch - 1 ? extra : 0.0);
+    int end = k == nch - 1 ? nt : (int)std::lround(acc);
+    end = std::min(std::max(end, t + 1), nt - (nch - 1 - k));  // every range keeps >= 1 tile
+    r->begin[k] = t;
+    r->len[k] = end - t;
+    worst = std::max(worst, r->len[k] * c[k] + (k == nch - 1 ? diag : 0.0));
+    t = end;
+  }
+  r->nch = nch;
+  return worst;
+}
+
+// Cuts every query tile, from the last one, into the fewest equal-cost ranges whose
+// cost is at most `cap`. Returns the number of units, or -1 when a tile would need more
+// than kMaxRanges ranges.
+int64_t cut_ranges(const Plan& pl, int64_t N, int64_t BH, bool causal, int cus, double cap, Plan::Ranges* out) {
+  int64_t u = 0;
+  for (int qt = pl.n_qt - 1; qt >= 0; --qt) {
+    const int nt = (int)qtile_ntiles(N, qt, causal);
+    const double diag = causal ? kDiagonalCost : 0.0;
+    int nch = 1;
+    while (cut_even(nt, nch, u, cus, diag, &out[qt]) > cap && nch < std::min(nt, fa::kMaxRanges)) ++nch;
+    if (cut_even(nt, nch, u, cus, diag, &out[qt]) > cap && nch < nt) return -1;
+    u += BH * nch;
+  }
+  return u;
+}
+
 Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask, int cus) {
   Plan pl;
   pl.mfma = dtype == FA_BF16;  // d, dv in {64, 128} already checked
@@ -208,42 +269,79 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype
   const int64_t BH = B * H;
   const int64_t tiles = BH * pl.n_qt;
   pl.grid = (int)tiles;
-  if (tiles <= 0 || tiles >= cus || tiles > kMaxSplitTiles || pl.n_qt > fa::kMaxSplitQTiles) return pl;
-  // Too few query tiles to occupy the chip: cut each tile's key range into ranges
-  // of about `chunk` key tiles, so that about `target` ranges (two workgroups per CU)
-  // exist in total.
-  int64_t total = 0;
-  for (int qt = 0; qt < pl.n_qt; ++qt) total += BH * qtile_ntiles(N, qt, causal);
+  // Split only where the query tiles leave CUs idle and the unit table's fields fit
+  // (b*h < 64, query tile < 256, key tiles < 512).
+  if (tiles <= 0 || tiles >= cus || BH > kMaxSplitBH || pl.n_qt > fa::kMaxSplitQTiles) return pl;
+  // Cut the query tiles' key ranges into units of about equal cost, as many as the CUs
+  // hold at once (two workgroups per CU): the smallest cost cap whose cut fits.
   const int64_t target = std::min<int64_t>(fa::kMaxSplitUnits,
                                            env_int("FA_SPLIT_UNITS") > 0 ? env_int("FA_SPLIT_UNITS") : 2 * (int64_t)cus);
-  int64_t chunk = std::max<int64_t>(1, (total + target - 1) / target);
-  // no query tile may be cut into more than kMaxRanges ranges
-  const int64_t nt_max = qtile_ntiles(N, pl.n_qt - 1, causal);
-  chunk = std::max<int64_t>(chunk, (nt_max + fa::kMaxRanges - 1) / fa::kMaxRanges);
-  // the ranges must fit in one wave of workgroups: grow the chunk until they do
-  int64_t units = 0;
-  bool any_split = false;
-  for (;; ++chunk) {
-    units = 0;
-    any_split = false;
-    for (int qt = 0; qt < pl.n_qt; ++qt) {
-      const int64_t nch = (qtile_ntiles(N, qt, causal) + chunk - 1) / chunk;
-      units += BH * nch;
-      any_split |= nch > 1;
-    }
-    if (units <= target || !any_split) break;
+  double lo = 0.5, hi = (double)qtile_ntiles(N, pl.n_qt - 1, causal) * kSecondSlotCost + kDiagonalCost + 1.0;
+  if (cut_ranges(pl, N, BH, causal, cus, hi, pl.ranges) < 0) return pl;
+  for (int it = 0; it < 24; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    const int64_t u = cut_ranges(pl, N, BH, causal, cus, mid, pl.ranges);
+    if (u >= 0 && u <= target) hi = mid;
+    else lo = mid;
   }
-  if (!any_split) return pl;
-  pl.chunk_tiles = (int)chunk;
+  const int64_t units = cut_ranges(pl, N, BH, causal, cus, hi, pl.ranges);
+  int64_t n_split = 0;
+  for (int qt = 0; qt < pl.n_qt; ++qt) n_split += pl.ranges[qt].nch > 1;
+  if (n_split == 0) return pl;
+  pl.split = true;
   pl.grid = (int)units;
-  pl.merge_grid = (int)(tiles * (fa::kMergeGroups * dv / 128));
-  pl.off_ml = 0;
-  pl.off_o = round_up(units * 2 * bm * sizeof(float), 256);
+  pl.merge_grid = (int)(tiles * fa::merge_groups((int)dv, 1));
+  pl.merge_blocks = (int)(n_split * BH * fa::merge_groups((int)dv, fa::kFusedMergeItems));
+  pl.off_flag = 0;
+  pl.off_ml = round_up(units * sizeof(uint64_t), 256);
+  pl.off_o = round_up(pl.off_ml + units * 2 * bm * sizeof(float), 256);
   pl.ws_bytes = round_up(pl.off_o + (size_t)units * bm * dv * sizeof(float), 256);
   return pl;
 }
 
+// The plan of a problem depends only on its shape and the CU count; cutting the ranges
+// of a split plan takes a while on the host, so plans are kept (a bounded map; a
+// caller holds its plan by shared pointer, so clearing the map never frees one in use).
+std::shared_ptr<const Plan> cached_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype,
+                                        int mask, int cus) {
+  using Key = std::array<int64_t, 8>;
+  static std::mutex mu;
+  static std::map<Key, std::shared_ptr<const Plan>> cache;
+  const Key key{B, H, N, d, dv, dtype, mask, cus};
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  auto pl = std::make_shared<const Plan>(make_plan(B, H, N, d, dv, dtype, mask, cus));
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache.size() >= 256) cache.clear();
+  cache.emplace(key, pl);
+  return pl;
+}
+
 // ---------------------------------------------------------------- launch
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();  // not ours to report; take the path that is safe under capture
+    return true;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
+// A number unique to each call (odd, so never the zero of fresh memory), published by
+// the units of an in-kernel merge. It starts at a random value, so flags left in a
+// workspace by other calls or processes do not match it.
+uint64_t next_call_number() {
+  static std::atomic<uint64_t> next{[] {
+    std::random_device rd;
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return ((((uint64_t)rd() << 32) ^ rd()) ^ (t * 0x9E3779B97F4A7C15ull)) | 1ull;
+  }()};
+  return next.fetch_add(2, std::memory_order_relaxed);
+}
+
 int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
   Params p{};
   p.q = P.q; p.k = P.k; p.v = P.v; p.bias = P.bias; p.out = P.out; p.lse = P.lse;
@@ -260,33 +358,42 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.d));
   p.scale = (float)(1.0 / std::sqrt((double)P.d));
   p.n_qt = pl.n_qt;
-  p.chunk_tiles = pl.chunk_tiles;
-  if (pl.chunk_tiles > 0) {  // unit table of the split plan (query tiles from the last)
+  p.split = pl.split;
+  if (pl.split) {  // unit table of the split plan (query tiles from the last)
     int32_t acc = 0;
     for (int qt = pl.n_qt - 1; qt >= 0; --qt) {
-      const int64_t nch = (qtile_ntiles(P.N, qt, p.causal) + pl.chunk_tiles - 1) / pl.chunk_tiles;
+      const Plan::Ranges& r = pl.ranges[qt];
       p.ubase[qt] = acc;
-      p.nchq[qt] = (uint8_t)nch;
+      p.nchq[qt] = (uint8_t)r.nch;
       for (int64_t bh = 0; bh < P.B * P.H; ++bh)
-        for (int c = 0; c < nch; ++c)
-          p.unit_info[acc + bh * nch + c] =
-              (uint32_t)qt | (uint32_t)bh << 8 | (uint32_t)c << 16 | (uint32_t)nch << 24;
-      acc += (int32_t)(P.B * P.H * nch);
+        for (int c = 0; c < r.nch; ++c)
+          p.unit_info[acc + bh * r.nch + c] =
+              (uint32_t)qt | (uint32_t)r.begin[c] << 8 | (uint32_t)r.len[c] << 17 | (uint32_t)bh << 26;
+      acc += (int32_t)(P.B * P.H * r.nch);
     }
     p.ubase[pl.n_qt] = acc;
   }
+  // Split query tiles are merged by blocks appended to the forward grid, except under
+  // graph capture (a replay would reuse this call's number, so the flags of the previous
+  // replay would already match): there a separate merge kernel follows.
+  const bool split = pl.split;
+  const bool in_kernel_merge = split && !stream_capturing(stream) && env_int("FA_MERGE_KERNEL") == 0;
+  p.n_units = pl.grid;
+  p.seq = next_call_number();
   if (pl.ws_bytes > 0) {
     unsigned char* w = static_cast<unsigned char*>(ws);
+    p.part_flag = in_kernel_merge ? reinterpret_cast<uint64_t*>(w + pl.off_flag) : nullptr;
     p.part_ml = reinterpret_cast<float*>(w + pl.off_ml);
     p.part_o = reinterpret_cast<float*>(w + pl.off_o);
   }
-  hipError_t e = pl.mfma ? fa::launch_mfma_bf16(p, pl.grid, pl.merge_grid > 0, stream)
+  const int grid = pl.grid + (in_kernel_merge ? pl.merge_blocks : 0);
+  hipError_t e = pl.mfma ? fa::launch_mfma_bf16(p, grid, split && !in_kernel_merge, stream)
                          : fa::launch_generic(p, P.dtype == FA_BF16, stream);
   if (std::getenv("FA_LOG"))
-    std::fprintf(stderr, "[fa] %s B=%lld H=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d n_qt=%d chunk=%d grid=%d merge=%d ws=%zu\n",
+    std::fprintf(stderr, "[fa] %s B=%lld H=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d n_qt=%d split=%d grid=%d merge=%d ws=%zu\n",
                  pl.mfma ? "mfma_bf16" : (P.dtype == FA_BF16 ? "generic_bf16" : "generic_f32"),
                  (long long)P.B, (long long)P.H, (long long)P.N, (long long)P.d, (long long)P.dv,
-                 p.causal, P.bias != nullptr, pl.n_qt, pl.chunk_tiles, pl.grid, pl.merge_grid, pl.ws_bytes);
+                 p.causal, P.bias != nullptr, pl.n_qt, (int)pl.split, grid, pl.merge_grid, pl.ws_bytes);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -342,7 +449,8 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias, in
   int dev = 0;
   DevInfo di;
   if ((st = device_info(&dev, &di)) != FA_OK) return st;
-  const Plan pl = make_plan(B, H, N, d, dv, dtype, mask_mode, di.cus);
+  const std::shared_ptr<const Plan> plan = cached_plan(B, H, N, d, dv, dtype, mask_mode, di.cus);
+  const Plan& pl = *plan;
   if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes || !aligned(workspace, 256)) return FA_ERR_WORKSPACE;
   }
@@ -359,7 +467,8 @@ int fa_fwd(const void* q, const void* k, const void* v, const float* bias, int m
   int dev = 0;
   DevInfo di;
   if ((st = device_info(&dev, &di)) != FA_OK) return st;
-  const Plan pl = make_plan(B, H, N, d, dv, dtype, mask_mode, di.cus);
+  const std::shared_ptr<const Plan> plan = cached_plan(B, H, N, d, dv, dtype, mask_mode, di.cus);
+  const Plan& pl = *plan;
   void* ws = nullptr;
   if (pl.ws_bytes > 0) {
     st = owned_workspace(dev, static_cast<hipStream_t>(stream), pl.ws_bytes, &ws);
@@ -375,7 +484,7 @@ size_t fa_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t
   int dev = 0;
   DevInfo di;
   if (device_info(&dev, &di) != FA_OK) return 0;
-  return make_plan(B, H, N, d, dv, dtype, mask_mode, di.cus).ws_bytes;
+  return cached_plan(B, H, N, d, dv, dtype, mask_mode, di.cus)->ws_bytes;
 }
 
 const char* fa_status_string(int status) {

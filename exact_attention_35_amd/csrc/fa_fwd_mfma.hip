@@ -138,8 +138,11 @@ struct TileCopy {
 };
 
 // Per-unit description: which (b*h, query tile) and which range of key tiles.
+// `partial`: the range is one of several of its query tile, so the unit writes a
+// partial state to be merged; otherwise it writes the output rows itself.
 struct Unit {
-  int bh, qt, t_begin, t_end, slot, nch;
+  int bh, qt, t_begin, t_end, slot;
+  bool partial;
 };
 
 __device__ __forceinline__ int qtile_ntiles(const Params& p, int qt, int BM, int BN) {
@@ -153,19 +156,18 @@ __device__ __forceinline__ int qtile_ntiles(const Params& p, int qt, int BM, int
 __device__ __forceinline__ Unit decode_unit(const Params& p, int u, int BM, int BN) {
   static_assert((kMaxSplitUnits & (kMaxSplitUnits - 1)) == 0, "unit table size must be a power of two");
   const unsigned info = p.unit_info[u & (kMaxSplitUnits - 1)];  // inside the table for any plan
-  const bool split = p.chunk_tiles != 0;
+  const bool split = p.split != 0;
   const unsigned BH = (unsigned)(p.B * p.H);
   const unsigned r = (unsigned)u / BH;
   Unit w;
   w.qt = split ? (int)(info & 0xff) : (p.causal ? p.n_qt - 1 - (int)r : (int)r);
-  w.bh = split ? (int)((info >> 8) & 0xff) : (int)((unsigned)u - r * BH);
-  const unsigned nch = split ? info >> 24 : 1u;
-  const unsigned c = split ? (info >> 16) & 0xff : 0u;
-  const unsigned nt = (unsigned)qtile_ntiles(p, w.qt, BM, BN);
-  w.t_begin = (int)(c * nt / nch);  // c, nt < 2^16
-  w.t_end = (int)((c + 1) * nt / nch);
-  w.slot = split ? u : -1;
-  w.nch = (int)nch;
+  w.bh = split ? (int)(info >> 26) : (int)((unsigned)u - r * BH);
+  const int nt = qtile_ntiles(p, w.qt, BM, BN);
+  w.t_begin = split ? (int)((info >> 8) & 0x1ff) : 0;
+  const int len = split ? (int)((info >> 17) & 0x1ff) : nt;
+  w.t_end = w.t_begin + len;
+  w.partial = len < nt;
+  w.slot = u;
   return w;
 }
 
@@ -234,6 +236,146 @@ struct SmState {
   float pf[32];  // probabilities awaiting their sum and bf16 conversion
 };
 
+// ---- merge of the partial states of split query tiles ----
+// One block merges RG = IT * RG1 rows of one query tile of one b*h: thread = (16-byte
+// dv chunk, IT rows RG1 apart), so the merge costs one memory round trip: every thread
+// first issues the loads of its items in every range, while the first RG threads load
+// their row's (m_p, l_p), turn them into weights 2^(m_p - m) / l (m = max_p m_p,
+// l = sum_p 2^(m_p - m) l_p) and stage them in LDS; then O = sum_p w_p o_p in range
+// order (deterministic, and the same arithmetic for any IT).
+// COHERENT: the partial states were written by workgroups of the same kernel, maybe on
+// another XCD, so they are read with agent-scope loads (sc1), which do not use lines of
+// the workspace that this XCD's L2 may still hold from an earlier call.
+// ok = false (the ranges never published their states) makes the block's rows NaN.
+constexpr int kLoadAgentScope = 16;  // buffer load cache policy: sc1
+
+template <int DV, int IT, bool COHERENT>
+__device__ __forceinline__ void merge_rows(const Params& p, int qt, int bh, int rg, float* w_s, bool ok) {
+  constexpr int BM = kMfmaBM;
+  constexpr int NC4 = DV / 4;      // 16-byte chunks of a row of o
+  constexpr int RG1 = 256 / NC4;   // rows of one item per thread: 8 (dv = 128) or 16 (dv = 64)
+  constexpr int RG = IT * RG1;     // rows per block
+  static_assert(BM / RG == merge_groups(DV, IT), "merge grid and block shape disagree");
+  constexpr int kPolicy = COHERENT ? kLoadAgentScope : 0;
+  const int nch = p.nchq[qt];
+  const int slot0 = p.ubase[qt] + bh * nch;
+  const int b = bh / p.H, h = bh % p.H;
+  const int tid = threadIdx.x;
+  const int rr = tid % RG1;
+  const int c4 = tid / RG1;
+  // slot j holds [BM/32][dv/4][32][4] floats: row r, chunk c4 at ((r/32)*NC4 + c4)*32 + r%32
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(p.part_o + (int64_t)slot0 * (BM * DV), 0, nch * BM * DV * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rml =
+      __builtin_amdgcn_make_buffer_rsrc(p.part_ml + (int64_t)slot0 * (2 * BM), 0, nch * 2 * BM * 4, kBufferWord3);
+  floatx4 v[IT][kMaxRanges];
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int r = rg * RG + k * RG1 + rr;  // row within the query tile
+    const int off = (((r >> 5) * NC4 + c4) * 32 + (r & 31)) * 16;
+#pragma unroll
+    for (int j = 0; j < kMaxRanges; ++j)
+      v[k][j] = j < nch ? __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + j * (BM * DV * 4), 0, kPolicy))
+                        : floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (tid < RG) {
+    const int r = rg * RG + tid;
+    const int qr = qt * BM + r;
+    float mp[kMaxRanges], lp[kMaxRanges];
+#pragma unroll
+    for (int j = 0; j < kMaxRanges; ++j) {
+      mp[j] = j < nch ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rml, (j * 2 * BM + r) * 4, 0, kPolicy))
+                      : -INFINITY;
+      lp[j] = j < nch ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rml, (j * 2 * BM + BM + r) * 4, 0, kPolicy))
+                      : 0.f;
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMaxRanges; ++j) m = fmaxf(m, mp[j]);
+    float l = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kMaxRanges; ++j) {
+        mp[j] = __builtin_amdgcn_exp2f(mp[j] - m);  // 0 for absent ranges
+        l += mp[j] * lp[j];
+      }
+    }
+    const bool any = m != -INFINITY && l > 0.f;
+    const float inv = !ok ? __builtin_nanf("") : any ? 1.f / l : 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxRanges; ++j) w_s[j * RG + tid] = ok && !any ? 0.f : mp[j] * inv;
+    if (p.lse && qr < p.N)
+      p.lse[b * p.l_sb + h * p.l_sh + qr] =
+          !ok ? __builtin_nanf("") : any ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  // chunk c4 = db*8 + r4*2 + g covers dv = db*32 + r4*8 + g*4 .. +4
+  const int dv0 = (c4 >> 3) * 32 + ((c4 >> 1) & 3) * 8 + (c4 & 1) * 4;
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int qr = qt * BM + rg * RG + k * RG1 + rr;
+    if (qr >= p.N) continue;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMaxRanges; ++j) acc += w_s[j * RG + k * RG1 + rr] * v[k][j];
+    bf16x4 o4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
+    __bf16* orow = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_sn;
+    *reinterpret_cast<bf16x4*>(orow + dv0) = o4;
+  }
+}
+
+// Merge blocks of the forward kernel itself (blocks n_units on): split query tiles from
+// the last one, then b*h, then groups of rows. The units of the tile publish their
+// partial states by storing this call's number into their flags once the states are
+// written through to memory; wave 0 polls the flags (one lane per range) with
+// agent-scope loads until all of them hold it. The merge blocks come after every unit
+// in the grid, so a waiting merge block never holds back a unit. The polls are bounded:
+// a tile whose ranges never publish gets NaN rows instead of a hang.
+constexpr int kMaxMergePolls = 1 << 20;
+
+template <int DV>
+__device__ void merge_block(const Params& p, int m, float* w_s) {
+  constexpr int RG = kFusedMergeItems * 256 / (DV / 4);
+  constexpr int groups = merge_groups(DV, kFusedMergeItems);
+  const int BH = p.B * p.H;
+  const int rg = m % groups;
+  const int t = m / groups;
+  const int bh = t % BH;
+  const int qt = p.n_qt - 1 - t / BH;
+  const int nch = p.nchq[qt];
+  const uint64_t* flag = p.part_flag + p.ubase[qt] + bh * nch;
+  int* ok_s = reinterpret_cast<int*>(w_s + kMaxRanges * RG);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    bool done = false;
+    for (int it = 0; it < kMaxMergePolls; ++it) {
+      const bool mine = lane >= nch || __hip_atomic_load(flag + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.seq;
+      if (__builtin_amdgcn_ballot_w64(!mine) == 0) {
+        done = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    if (lane == 0) *ok_s = done;
+  }
+  __syncthreads();
+  merge_rows<DV, kFusedMergeItems, true>(p, qt, bh, rg, w_s, *ok_s != 0);
+}
+
+// Separate merge kernel (used where the forward kernel runs without merge blocks):
+// block = (group of rows, b*h, query tile) = (blockIdx.x, .y, .z).
+template <int DV>
+__global__ __launch_bounds__(256) void merge_split(Params p) {
+  __shared__ float w_s[kMaxRanges * (256 / (DV / 4))];
+  const int qt = blockIdx.z;
+  // the argument cache lines used below and the tile's table entries in one round trip
+  asm volatile("" ::"s"(p.out), "s"(p.o_sn), "s"(p.N), "s"(p.part_ml), "s"(p.ubase[qt]), "s"((int)p.nchq[qt]));
+  if (p.nchq[qt] == 1) return;  // written directly by the forward kernel
+  merge_rows<DV, 1, false>(p, qt, blockIdx.y, blockIdx.x, w_s, true);
+}
+
 template <int D, int DV, bool BIAS>
 __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   using C = Cfg<D, DV>;
@@ -242,6 +384,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[C::KTILE], k_lds1[C::KTILE];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[C::VTILE], v_lds1[C::VTILE];
 
+  if ((int)blockIdx.x >= p.n_units) {  // merge block (the LDS stages are free for it)
+    merge_block<DV>(p, blockIdx.x - p.n_units, reinterpret_cast<float*>(k_lds0));
+    return;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -252,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   // unit's table entry, are read before anything depends on them: these scalar loads
   // share one memory round trip, and later argument reads hit the scalar cache (a
   // dependent chain of argument reads costs a round trip per cache line).
-  asm volatile("" ::"s"(p.q), "s"(p.k_sn), "s"(p.b_si), "s"(p.chunk_tiles),
+  asm volatile("" ::"s"(p.q), "s"(p.k_sn), "s"(p.b_si), "s"(p.split),
                "s"(p.unit_info[blockIdx.x & (kMaxSplitUnits - 1)]));
   const Unit U = decode_unit(p, blockIdx.x, C::BM, C::BN);
   const int b = U.bh / p.H;
@@ -579,7 +725,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const int row = wave * 32 + l32;  // row within the query tile
 
-  if (U.nch == 1) {
+  if (!U.partial) {
     if (!qvalid) return;
     __bf16* op = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qi * p.o_sn;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -616,80 +762,11 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref), pml, row * 4, 0, kStoreWriteThrough);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_tot), pml, (C::BM + row) * 4, 0, kStoreWriteThrough);
   }
-}
-
-// Merge of the partial states of split query tiles. Block = (group of RG rows, b*h,
-// query tile) = (blockIdx.x, .y, .z), thread = (row, 16-byte dv chunk), so each thread
-// merges one item and the merge costs one memory round trip after the kernel
-// arguments: every thread first issues the loads of its item in every range, while the
-// first RG threads load their row's (m_p, l_p), turn them into weights 2^(m_p - m) / l
-// (m = max_p m_p, l = sum_p 2^(m_p - m) l_p) and stage them in LDS; then
-// O = sum_p w_p o_p in range order (deterministic).
-template <int DV>
-__global__ __launch_bounds__(256) void merge_split(Params p) {
-  constexpr int BM = kMfmaBM;
-  constexpr int NC4 = DV / 4;    // 16-byte chunks of a row of o
-  constexpr int RG = 256 / NC4;  // rows per block: 8 (dv = 128) or 16 (dv = 64)
-  static_assert(BM / RG == kMergeGroups * DV / 128, "merge grid and block shape disagree");
-  __shared__ float w_s[kMaxRanges][RG];
-  const int rg = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int qt = blockIdx.z;
-  // the argument cache lines used below and the tile's table entries in one round trip
-  asm volatile("" ::"s"(p.out), "s"(p.o_sn), "s"(p.N), "s"(p.part_ml), "s"(p.ubase[qt]), "s"((int)p.nchq[qt]));
-  const int nch = p.nchq[qt];
-  if (nch == 1) return;  // written directly by the forward kernel
-  const int slot0 = p.ubase[qt] + bh * nch;
-  const int b = bh / p.H, h = bh % p.H;
-  const int tid = threadIdx.x;
-  const int rr = tid % RG;
-  const int c4 = tid / RG;
-  const int r = rg * RG + rr;  // row within the query tile
-  const int qr = qt * BM + r;
-  // a slot holds [BM/32][dv/4][32][4] floats: row r, chunk c4 at ((r/32)*NC4 + c4)*32 + r%32
-  const float* src = p.part_o + (int64_t)slot0 * (BM * DV) + (((r >> 5) * NC4 + c4) * 32 + (r & 31)) * 4;
-  floatx4 v[kMaxRanges];
-#pragma unroll
-  for (int j = 0; j < kMaxRanges; ++j)
-    v[j] = j < nch ? *reinterpret_cast<const floatx4*>(src + (int64_t)j * (BM * DV)) : floatx4{0.f, 0.f, 0.f, 0.f};
-  if (tid < RG) {
-    float mp[kMaxRanges], lp[kMaxRanges];
-#pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j) {
-      const float* ml = p.part_ml + (int64_t)(slot0 + j) * (2 * BM);
-      mp[j] = j < nch ? ml[r] : -INFINITY;
-      lp[j] = j < nch ? ml[BM + r] : 0.f;
-    }
-    float m = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j) m = fmaxf(m, mp[j]);
-    float l = 0.f;
-    if (m != -INFINITY) {
-#pragma unroll
-      for (int j = 0; j < kMaxRanges; ++j) {
-        mp[j] = __builtin_amdgcn_exp2f(mp[j] - m);  // 0 for absent ranges
-        l += mp[j] * lp[j];
-      }
-    }
-    const bool ok = m != -INFINITY && l > 0.f;
-    const float inv = ok ? 1.f / l : 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j) w_s[j][rr] = ok ? mp[j] * inv : 0.f;
-    if (p.lse && qr < p.N)
-      p.lse[b * p.l_sb + h * p.l_sh + qr] = ok ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  if (p.part_flag) {  // merged by merge blocks of this kernel: publish the state
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are complete (written through)
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(p.part_flag + U.slot, p.seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  if (qr >= p.N) return;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < kMaxRanges; ++j) acc += w_s[j][rr] * v[j];
-  // chunk c4 = db*8 + r4*2 + g covers dv = db*32 + r4*8 + g*4 .. +4
-  const int dv0 = (c4 >> 3) * 32 + ((c4 >> 1) & 3) * 8 + (c4 & 1) * 4;
-  bf16x4 o4;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
-  __bf16* orow = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_sn;
-  *reinterpret_cast<bf16x4*>(orow + dv0) = o4;
 }
 
 // Every variant is instantiated explicitly: the host pass then emits a launch stub
@@ -713,7 +790,7 @@ hipError_t launch_dd(const Params& p, int grid, bool merge, hipStream_t stream) 
     hipLaunchKernelGGL((fwd_mfma<D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !merge) return e;
-  hipLaunchKernelGGL((merge_split<DV>), dim3(kMergeGroups * DV / 128, p.B * p.H, p.n_qt), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((merge_split<DV>), dim3(merge_groups(DV, 1), p.B * p.H, p.n_qt), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -34,17 +34,23 @@ struct Params {
   float scale;        // 1 / sqrt(d)
   // Work decomposition. A unit is (batch*head, query tile, range of key tiles).
   int n_qt;           // query tiles per (b, h)
-  int chunk_tiles;    // 0: no split; else key tiles per range (ranges of a tile are balanced)
+  int split;          // 1: query tiles cut into key ranges (see unit_info), merged afterwards
   // Scratch for split problems: one slot per unit.
   float* part_o;      // [slot][BM/32][dv/4][32][4] unnormalised numerators
   float* part_ml;     // [slot][2][BM]       reference (base 2) and normaliser
+  // Merge inside the forward kernel: blocks n_units .. gridDim.x-1 merge the split query
+  // tiles; unit u publishes its partial state by storing `seq` (a number unique to this
+  // call) into part_flag[u]. part_flag = nullptr: a separate merge kernel follows.
+  uint64_t* part_flag;
+  uint64_t seq;
+  int n_units;        // forward units (blocks 0 .. n_units-1)
   // Split plans: units enumerate query tiles from the last one; query tile qt owns
   // units ubase[qt] .. ubase[qt] + B*H*nchq[qt] - 1, nchq[qt] ranges for each (b, h).
   int32_t ubase[kMaxSplitQTiles + 1];
   uint8_t nchq[kMaxSplitQTiles];
-  // Split plans: unit u is query tile (unit_info[u] & 0xff), b*h ((>> 8) & 0xff),
-  // range index ((>> 16) & 0xff) of (>> 24) ranges, so a workgroup decodes its unit
-  // with one load.
+  // Split plans: unit u is query tile (unit_info[u] & 0xff), key tiles from
+  // ((>> 8) & 0x1ff), count ((>> 17) & 0x1ff), b*h (>> 26), so a workgroup decodes its
+  // unit with one load.
   uint32_t unit_info[kMaxSplitUnits];
 };
 
@@ -53,8 +59,12 @@ constexpr int kMfmaBM = 128;
 constexpr int kMfmaBN = 64;
 // Most key ranges a split query tile is cut into (the merge kernel's bound).
 constexpr int kMaxRanges = 16;
-// Merge blocks per split query tile at dv = 128 (8 rows each; dv = 64 takes half).
-constexpr int kMergeGroups = 16;
+// Merge blocks per split query tile when each of a block's 256 threads merges `items`
+// 16-byte chunks (rows of 8 * items at dv = 128, 16 * items at dv = 64).
+constexpr int merge_groups(int dv, int items) { return kMfmaBM * dv / (1024 * items); }
+// Items per thread of the merge blocks inside the forward kernel (fewer, larger blocks:
+// they hold a forward kernel's resources) and of the separate merge kernel.
+constexpr int kFusedMergeItems = 2;
 // Query-tile height of the general (vector ALU) kernel.
 constexpr int kGenericBM = 64;
 

@@ -175,6 +175,32 @@ def test_workspace_entry_point_matches(gpu_device):
                 capi.fa_fwd_ex(gpu["q"], gpu["k"], gpu["v"], ws[: nbytes // 2], causal=w.causal)
 
 
+# split problems (fewer query tiles than compute units) with the merge of their key
+# ranges done by merge blocks of the forward kernel and by the separate merge kernel
+SPLIT = [(1, dict(N=1000)), (3, dict(B=1, H=2, N=1100)), (4, dict(H=2, N=1500)), (1, {})]
+
+
+@pytest.mark.parametrize("idx,over", SPLIT, ids=[f"w{i}-{o}" for i, o in SPLIT])
+def test_split_merge_paths_agree(gpu_device, monkeypatch, idx, over):
+    import torch
+
+    w = workloads.workload(idx).resized(**over)
+    inp, gpu = _inputs(w, gpu_device)
+    monkeypatch.delenv("FA_MERGE_KERNEL", raising=False)
+    runs = [_run(gpu, w, gpu_device) for _ in range(3)]  # each call publishes a new number
+    monkeypatch.setenv("FA_MERGE_KERNEL", "1")
+    runs.append(_run(gpu, w, gpu_device))
+    o1, l1 = runs[0]
+    for o, l in runs[1:]:  # same arithmetic in the same order: bitwise equal
+        assert torch.equal(o1, o) and torch.equal(l1, l)
+    if w.N <= 2048:
+        o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
+        check_out(o1, o_ref, "bf16", w.name + str(over))
+        check_lse(l1, l_ref, w.name + str(over))
+    else:
+        assert bool(o1.float().isfinite().all()) and bool(l1.isfinite().all())
+
+
 def test_single_allowed_key_and_constant_v_exact(gpu_device):
     import torch
 
