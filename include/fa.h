@@ -103,8 +103,9 @@ typedef struct {
  * Split problems (few, long query tiles) need a scratch workspace: fa_fwd uses a
  * buffer the library allocates on first need per (device, stream) and keeps until
  * fa_shutdown(); calls on one stream are ordered, so they never share it unsafely.
- * Such problems run as two kernels on `stream`: the forward over key ranges, then a
- * merge of each query tile's ranges.
+ * Such problems run as one kernel on `stream`: workgroups over key ranges, then
+ * workgroups that merge each query tile's ranges once those have published their
+ * states; while `stream` is capturing a graph, the merge is a second kernel instead.
  * Returns FA_OK or a negative fa_status (see above). Asynchronous: the call returns
  * before the device work finishes.
  */
