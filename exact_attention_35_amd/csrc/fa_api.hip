@@ -295,7 +295,7 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype
   pl.off_flag = 0;
   pl.off_ml = round_up(units * sizeof(uint64_t), 256);
   pl.off_o = round_up(pl.off_ml + units * 2 * bm * sizeof(float), 256);
-  pl.ws_bytes = round_up(pl.off_o + (size_t)units * bm * dv * sizeof(float), 256);
+  pl.ws_bytes = round_up(pl.off_o + (size_t)units * bm * dv * 2, 256);  // bf16 numerators
   return pl;
 }
 
@@ -384,7 +384,7 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
     unsigned char* w = static_cast<unsigned char*>(ws);
     p.part_flag = in_kernel_merge ? reinterpret_cast<uint64_t*>(w + pl.off_flag) : nullptr;
     p.part_ml = reinterpret_cast<float*>(w + pl.off_ml);
-    p.part_o = reinterpret_cast<float*>(w + pl.off_o);
+    p.part_o = reinterpret_cast<__bf16*>(w + pl.off_o);
   }
   const int grid = pl.grid + (in_kernel_merge ? pl.merge_blocks : 0);
   hipError_t e = pl.mfma ? fa::launch_mfma_bf16(p, grid, split && !in_kernel_merge, stream)

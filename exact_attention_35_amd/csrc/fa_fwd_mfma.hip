@@ -60,6 +60,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format, no swizzle).
@@ -240,9 +241,10 @@ struct SmState {
 // One block merges RG = IT * RG1 rows of one query tile of one b*h: thread = (16-byte
 // dv chunk, IT rows RG1 apart), so the merge costs one memory round trip: every thread
 // first issues the loads of its items in every range, while the first RG threads load
-// their row's (m_p, l_p), turn them into weights 2^(m_p - m) / l (m = max_p m_p,
-// l = sum_p 2^(m_p - m) l_p) and stage them in LDS; then O = sum_p w_p o_p in range
-// order (deterministic, and the same arithmetic for any IT).
+// their row's (m_p, l_p), turn them into weights 2^(m_p - m) l_p / l (m = max_p m_p,
+// l = sum_p 2^(m_p - m) l_p) and stage them in LDS; then O = sum_p w_p (o_p / l_p) in
+// range order (deterministic, and the same arithmetic for any IT), o_p / l_p being the
+// normalised output each range stored.
 // COHERENT: the partial states were written by workgroups of the same kernel, maybe on
 // another XCD, so they are read with agent-scope loads (sc1), which do not use lines of
 // the workspace that this XCD's L2 may still hold from an earlier call.
@@ -263,20 +265,22 @@ __device__ __forceinline__ void merge_rows(const Params& p, int qt, int bh, int 
   const int tid = threadIdx.x;
   const int rr = tid % RG1;
   const int c4 = tid / RG1;
-  // slot j holds [BM/32][dv/4][32][4] floats: row r, chunk c4 at ((r/32)*NC4 + c4)*32 + r%32
+  // slot j holds [BM/32][dv/4][32][4] bf16: row r, chunk c4 at ((r/32)*NC4 + c4)*32 + r%32
   const __amdgpu_buffer_rsrc_t ro =
-      __builtin_amdgcn_make_buffer_rsrc(p.part_o + (int64_t)slot0 * (BM * DV), 0, nch * BM * DV * 4, kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc(p.part_o + (int64_t)slot0 * (BM * DV), 0, nch * BM * DV * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rml =
       __builtin_amdgcn_make_buffer_rsrc(p.part_ml + (int64_t)slot0 * (2 * BM), 0, nch * 2 * BM * 4, kBufferWord3);
   floatx4 v[IT][kMaxRanges];
 #pragma unroll
   for (int k = 0; k < IT; ++k) {
     const int r = rg * RG + k * RG1 + rr;  // row within the query tile
-    const int off = (((r >> 5) * NC4 + c4) * 32 + (r & 31)) * 16;
+    const int off = (((r >> 5) * NC4 + c4) * 32 + (r & 31)) * 8;
 #pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j)
-      v[k][j] = j < nch ? __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + j * (BM * DV * 4), 0, kPolicy))
-                        : floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kMaxRanges; ++j) {
+      const bf16x4 h = j < nch ? __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(ro, off + j * (BM * DV * 2), 0, kPolicy))
+                               : bf16x4{};
+      v[k][j] = floatx4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    }
   }
   if (tid < RG) {
     const int r = rg * RG + tid;
@@ -303,7 +307,7 @@ __device__ __forceinline__ void merge_rows(const Params& p, int qt, int bh, int 
     const bool any = m != -INFINITY && l > 0.f;
     const float inv = !ok ? __builtin_nanf("") : any ? 1.f / l : 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j) w_s[j * RG + tid] = ok && !any ? 0.f : mp[j] * inv;
+    for (int j = 0; j < kMaxRanges; ++j) w_s[j * RG + tid] = ok && !any ? 0.f : mp[j] * lp[j] * inv;
     if (p.lse && qr < p.N)
       p.lse[b * p.l_sb + h * p.l_sh + qr] =
           !ok ? __builtin_nanf("") : any ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
@@ -743,20 +747,26 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     return;
   }
 
-  // ---- split: this range's partial state; layout per slot [BM/32][dv/4][32][4]:
-  // one wave's 32 rows of one 16-byte dv chunk are 512 consecutive bytes ----
+  // ---- split: this range's partial state: its own normalised output o / l in bf16
+  // (a convex combination of V rows, so the rounding costs at most 2^-9 max|v|, that of
+  // the bf16 output itself, and equal V rows come back exactly), layout per slot
+  // [BM/32][dv/4][32][4]: one wave's 32 rows of 4 dv values are 256 consecutive bytes;
+  // m and l stay fp32. ----
   const __amdgpu_buffer_rsrc_t po = __builtin_amdgcn_make_buffer_rsrc(
-      p.part_o + (int64_t)U.slot * (C::BM * DV), 0, C::BM * DV * 4, kBufferWord3);
+      p.part_o + (int64_t)U.slot * (C::BM * DV), 0, C::BM * DV * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t pml = __builtin_amdgcn_make_buffer_rsrc(
       p.part_ml + (int64_t)U.slot * (2 * C::BM), 0, 2 * C::BM * 4, kBufferWord3);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int c4 = db * 8 + r4 * 2 + g;
-      const floatx4 v4 = {oacc[db][r4 * 4 + 0], oacc[db][r4 * 4 + 1], oacc[db][r4 * 4 + 2], oacc[db][r4 * 4 + 3]};
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), po,
-                                             ((wave * (DV / 4) + c4) * 32 + l32) * 16, 0, kStoreWriteThrough);
+      bf16x4 h4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h4[e] = (__bf16)(oacc[db][r4 * 4 + e] * inv);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), po,
+                                            ((wave * (DV / 4) + c4) * 32 + l32) * 8, 0, kStoreWriteThrough);
     }
   if (g == 0) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref), pml, row * 4, 0, kStoreWriteThrough);

@@ -36,7 +36,7 @@ struct Params {
   int n_qt;           // query tiles per (b, h)
   int split;          // 1: query tiles cut into key ranges (see unit_info), merged afterwards
   // Scratch for split problems: one slot per unit.
-  float* part_o;      // [slot][BM/32][dv/4][32][4] unnormalised numerators
+  __bf16* part_o;     // [slot][BM/32][dv/4][32][4] unnormalised numerators (bf16)
   float* part_ml;     // [slot][2][BM]       reference (base 2) and normaliser
   // Merge inside the forward kernel: blocks n_units .. gridDim.x-1 merge the split query
   // tiles; unit u publishes its partial state by storing `seq` (a number unique to this
