@@ -201,6 +201,40 @@ def test_split_merge_paths_agree(gpu_device, monkeypatch, idx, over):
         assert bool(o1.float().isfinite().all()) and bool(l1.isfinite().all())
 
 
+def test_graph_capture_replays_match_eager(gpu_device):
+    """A split problem captured into a HIP graph (there the merge is a second kernel)
+    gives, on every replay, bitwise the eager result (merge blocks in the forward
+    kernel) for the inputs of that replay; eager work runs between the replays."""
+    import torch
+
+    w = workloads.workload(1).resized(N=1500)
+    _, gpu = _inputs(w, gpu_device)
+    q, k, v = (gpu[n].clone() for n in ("q", "k", "v"))
+    nbytes = capi.fa_fwd_workspace_size(w.B, w.H, w.N, w.d, w.dv, capi.FA_BF16, True)
+    assert nbytes > 0  # a split plan
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+    out = torch.empty(w.B, w.H, w.N, w.dv, dtype=q.dtype, device=gpu_device)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=gpu_device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        capi.fa_fwd_ex(q, k, v, ws, causal=True, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        capi.fa_fwd_ex(q, k, v, ws, causal=True, out=out, lse=lse)
+    gen = torch.Generator().manual_seed(11)
+    for _ in range(3):
+        q.copy_(torch.randn(q.shape, generator=gen).to(q.dtype).to(gpu_device))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_ref, l_ref = capi.fa_fwd(q, k, v, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(lse, l_ref)
+
+
 def test_single_allowed_key_and_constant_v_exact(gpu_device):
     import torch
 
