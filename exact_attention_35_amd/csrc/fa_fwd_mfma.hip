@@ -21,15 +21,18 @@
 //    dv column; two such reads give the 8 keys the P^T operand holds in that lane.
 //  * The O^T accumulator again has one query per lane, so rescaling is a per-lane
 //    scalar multiply.
-//  * K and V tiles go from global memory straight into LDS (global_load_lds_dwordx4,
-//    no staging registers). Rows are stored with their 16-byte chunks XOR-swizzled by
-//    the row index, so the operand reads of neighbouring lanes hit distinct banks;
-//    the swizzle is applied on the global side of the copy. Rows past the sequence
-//    end are clamped to the last row and masked in the scores.
+//  * K and V tiles go from global memory straight into LDS (buffer_load_dwordx4 with
+//    the LDS destination, no staging registers). Rows are stored with their 16-byte
+//    chunks XOR-swizzled by the row index, so the operand reads of neighbouring lanes
+//    hit distinct banks; the swizzle is applied on the global side of the copy. The
+//    buffer resource covers only the rows that exist, so rows past the sequence end
+//    read as zeros; their keys are masked in the scores.
 //  * Software pipeline, one barrier per key tile: iteration t computes the scores of
 //    tile t+1 (Q K^T) and the P V product of tile t-1 on the matrix cores while the
 //    vector ALUs run the softmax of tile t; the copies of K(t+2) and V(t) are in flight
-//    meanwhile (two LDS stages each for K and V).
+//    meanwhile (two LDS stages each for K and V). The body is one compile-time
+//    sequence of slots (a matrix instruction, an operand read ahead, a share of the
+//    softmax), with the wave's issue priority raised for its Q K^T half.
 //  * Exponentials in base 2 (v_exp_f32): scores are carried as S*log2(e); the factor
 //    is folded into the 1/sqrt(d) scale and into the exp argument's FMA.
 //  * Lazy reference: the recurrence is exact for any reference value that bounds the
@@ -41,11 +44,12 @@
 //    wave skips the tiles that lie entirely above its own 32 rows; element masks are
 //    applied only on tiles that cross the diagonal or the sequence end.
 //  * Split over keys (problems with too few query tiles to fill the CUs): a query
-//    tile's key tiles are cut into contiguous ranges of about equal work (the
+//    tile's key tiles are cut into contiguous ranges of about equal cost (the
 //    recurrence allows any partition of the keys into blocks). Each range writes its
-//    partial state (o, m, l) to scratch memory and a second, small kernel merges the
-//    ranges of each tile in range order (deterministic; no atomics):
-//    m = max_p m_p, l = sum_p 2^(m_p-m) l_p, o = sum_p 2^(m_p-m) o_p, O = o / l.
+//    partial state (its own normalised output o/l in bf16, m and l in fp32) to
+//    scratch memory and publishes it; merge blocks at the end of the same grid combine
+//    the ranges of each tile in range order (deterministic; no atomics):
+//    m = max_p m_p, l = sum_p 2^(m_p-m) l_p, O = sum_p (2^(m_p-m) l_p / l) (o_p/l_p).
 
 #include <type_traits>
 
@@ -66,8 +70,10 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
 // Cache policy of a buffer store (sc0 | sc1): system scope, so the L2 writes the data
-// through instead of keeping it dirty. The split partial states are read by the next
-// kernel only; written through, they need no write-back of the L2 at the kernel's end.
+// through instead of keeping it dirty. The split partial states are read by other
+// workgroups (merge blocks of the same kernel, on any XCD, or a following merge
+// kernel): written through, they have reached memory once the stores complete, and the
+// L2 needs no write-back of them at the kernel's end.
 constexpr int kStoreWriteThrough = 1 | 16;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -238,8 +244,8 @@ struct SmState {
 };
 
 // ---- merge of the partial states of split query tiles ----
-// One block merges RG = IT * RG1 rows of one query tile of one b*h: thread = (16-byte
-// dv chunk, IT rows RG1 apart), so the merge costs one memory round trip: every thread
+// One block merges RG = IT * RG1 rows of one query tile of one b*h: thread = (chunk of
+// 4 dv values, IT rows RG1 apart), so the merge costs one memory round trip: every thread
 // first issues the loads of its items in every range, while the first RG threads load
 // their row's (m_p, l_p), turn them into weights 2^(m_p - m) l_p / l (m = max_p m_p,
 // l = sum_p 2^(m_p - m) l_p) and stage them in LDS; then O = sum_p w_p (o_p / l_p) in
@@ -254,7 +260,7 @@ constexpr int kLoadAgentScope = 16;  // buffer load cache policy: sc1
 template <int DV, int IT, bool COHERENT>
 __device__ __forceinline__ void merge_rows(const Params& p, int qt, int bh, int rg, float* w_s, bool ok) {
   constexpr int BM = kMfmaBM;
-  constexpr int NC4 = DV / 4;      // 16-byte chunks of a row of o
+  constexpr int NC4 = DV / 4;      // chunks of 4 values in a row of o
   constexpr int RG1 = 256 / NC4;   // rows of one item per thread: 8 (dv = 128) or 16 (dv = 64)
   constexpr int RG = IT * RG1;     // rows per block
   static_assert(BM / RG == merge_groups(DV, IT), "merge grid and block shape disagree");
