@@ -257,84 +257,100 @@ struct SmState {
 // ok = false (the ranges never published their states) makes the block's rows NaN.
 constexpr int kLoadAgentScope = 16;  // buffer load cache policy: sc1
 
-template <int DV, int IT, bool COHERENT>
-__device__ __forceinline__ void merge_rows(const Params& p, int qt, int bh, int rg, float* w_s, bool ok) {
-  constexpr int BM = kMfmaBM;
-  constexpr int NC4 = DV / 4;      // chunks of 4 values in a row of o
-  constexpr int RG1 = 256 / NC4;   // rows of one item per thread: 8 (dv = 128) or 16 (dv = 64)
-  constexpr int RG = IT * RG1;     // rows per block
+// The merge items of one thread (IT chunks of 4 dv values, rows RG1 apart) in every
+// range of a split query tile, and the (m_p, l_p) of row rg*RG + tid for tid < RG.
+// Ranges j >= nch keep o = 0, m = -inf, l = 0, so they weigh nothing.
+template <int DV, int IT>
+struct MergeItems {
+  static constexpr int BM = kMfmaBM;
+  static constexpr int NC4 = DV / 4;     // chunks of 4 values in a row of o
+  static constexpr int RG1 = 256 / NC4;  // rows of one item per thread: 8 (dv = 128) or 16 (dv = 64)
+  static constexpr int RG = IT * RG1;    // rows per block
   static_assert(BM / RG == merge_groups(DV, IT), "merge grid and block shape disagree");
-  constexpr int kPolicy = COHERENT ? kLoadAgentScope : 0;
-  const int nch = p.nchq[qt];
-  const int slot0 = p.ubase[qt] + bh * nch;
-  const int b = bh / p.H, h = bh % p.H;
-  const int tid = threadIdx.x;
-  const int rr = tid % RG1;
-  const int c4 = tid / RG1;
-  // slot j holds [BM/32][dv/4][32][4] bf16: row r, chunk c4 at ((r/32)*NC4 + c4)*32 + r%32
-  const __amdgpu_buffer_rsrc_t ro =
-      __builtin_amdgcn_make_buffer_rsrc(p.part_o + (int64_t)slot0 * (BM * DV), 0, nch * BM * DV * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rml =
-      __builtin_amdgcn_make_buffer_rsrc(p.part_ml + (int64_t)slot0 * (2 * BM), 0, nch * 2 * BM * 4, kBufferWord3);
-  floatx4 v[IT][kMaxRanges];
+  __amdgpu_buffer_rsrc_t ro, rml;
+  int rg;
+  int off[IT];                 // byte offset of item k within a range's slot
+  u32x2 raw[IT][kMaxRanges];   // o_p / l_p, 4 bf16 values per item
+  float mp[kMaxRanges], lp[kMaxRanges];
+
+  __device__ __forceinline__ void init(const Params& p, int qt, int bh, int rg_, int nch) {
+    rg = rg_;
+    const int slot0 = p.ubase[qt] + bh * nch;
+    // slot j holds [BM/32][dv/4][32][4] bf16: row r, chunk c4 at ((r/32)*NC4 + c4)*32 + r%32
+    ro = __builtin_amdgcn_make_buffer_rsrc(p.part_o + (int64_t)slot0 * (BM * DV), 0, nch * BM * DV * 2, kBufferWord3);
+    rml = __builtin_amdgcn_make_buffer_rsrc(p.part_ml + (int64_t)slot0 * (2 * BM), 0, nch * 2 * BM * 4, kBufferWord3);
+    const int rr = threadIdx.x % RG1, c4 = threadIdx.x / RG1;
 #pragma unroll
-  for (int k = 0; k < IT; ++k) {
-    const int r = rg * RG + k * RG1 + rr;  // row within the query tile
-    const int off = (((r >> 5) * NC4 + c4) * 32 + (r & 31)) * 8;
+    for (int k = 0; k < IT; ++k) {
+      const int r = rg * RG + k * RG1 + rr;  // row within the query tile
+      off[k] = (((r >> 5) * NC4 + c4) * 32 + (r & 31)) * 8;
+    }
 #pragma unroll
     for (int j = 0; j < kMaxRanges; ++j) {
-      const bf16x4 h = j < nch ? __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(ro, off + j * (BM * DV * 2), 0, kPolicy))
-                               : bf16x4{};
-      v[k][j] = floatx4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+#pragma unroll
+      for (int k = 0; k < IT; ++k) raw[k][j] = u32x2{0u, 0u};
+      mp[j] = -INFINITY;
+      lp[j] = 0.f;
     }
   }
-  if (tid < RG) {
-    const int r = rg * RG + tid;
-    const int qr = qt * BM + r;
-    float mp[kMaxRanges], lp[kMaxRanges];
+  // issues the loads of range J (cache policy POL)
+  template <int J, int POL>
+  __device__ __forceinline__ void load() {
 #pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j) {
-      mp[j] = j < nch ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rml, (j * 2 * BM + r) * 4, 0, kPolicy))
-                      : -INFINITY;
-      lp[j] = j < nch ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rml, (j * 2 * BM + BM + r) * 4, 0, kPolicy))
-                      : 0.f;
+    for (int k = 0; k < IT; ++k) raw[k][J] = __builtin_amdgcn_raw_buffer_load_b64(ro, off[k] + J * (BM * DV * 2), 0, POL);
+    if ((int)threadIdx.x < RG) {
+      const int r = rg * RG + threadIdx.x;
+      mp[J] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rml, (J * 2 * BM + r) * 4, 0, POL));
+      lp[J] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rml, (J * 2 * BM + BM + r) * 4, 0, POL));
     }
-    float m = -INFINITY;
+  }
+  // Weights 2^(m_p - m) l_p / l (m = max_p m_p, l = sum_p 2^(m_p - m) l_p) staged in LDS by
+  // the first RG threads, then O = sum_p w_p (o_p / l_p) in range order (deterministic)
+  // and lse. ok = false (the ranges never published their states) makes the rows NaN.
+  __device__ __forceinline__ void combine(const Params& p, int qt, int bh, float* w_s, bool ok) {
+    const int b = bh / p.H, h = bh % p.H;
+    const int tid = threadIdx.x;
+    if (tid < RG) {
+      const int qr = qt * BM + rg * RG + tid;
+      float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j) m = fmaxf(m, mp[j]);
-    float l = 0.f;
-    if (m != -INFINITY) {
+      for (int j = 0; j < kMaxRanges; ++j) m = fmaxf(m, mp[j]);
+      float w[kMaxRanges], l = 0.f;
 #pragma unroll
       for (int j = 0; j < kMaxRanges; ++j) {
-        mp[j] = __builtin_amdgcn_exp2f(mp[j] - m);  // 0 for absent ranges
-        l += mp[j] * lp[j];
+        w[j] = m != -INFINITY ? __builtin_amdgcn_exp2f(mp[j] - m) : 0.f;  // 0 for absent ranges
+        l += w[j] * lp[j];
       }
+      const bool any = m != -INFINITY && l > 0.f;
+      const float inv = !ok ? __builtin_nanf("") : any ? 1.f / l : 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxRanges; ++j) w_s[j * RG + tid] = ok && !any ? 0.f : w[j] * lp[j] * inv;
+      if (p.lse && qr < p.N)
+        p.lse[b * p.l_sb + h * p.l_sh + qr] =
+            !ok ? __builtin_nanf("") : any ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
     }
-    const bool any = m != -INFINITY && l > 0.f;
-    const float inv = !ok ? __builtin_nanf("") : any ? 1.f / l : 0.f;
+    __syncthreads();
+    const int rr = tid % RG1, c4 = tid / RG1;
+    // chunk c4 = db*8 + r4*2 + g covers dv = db*32 + r4*8 + g*4 .. +4
+    const int dv0 = (c4 >> 3) * 32 + ((c4 >> 1) & 3) * 8 + (c4 & 1) * 4;
 #pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j) w_s[j * RG + tid] = ok && !any ? 0.f : mp[j] * lp[j] * inv;
-    if (p.lse && qr < p.N)
-      p.lse[b * p.l_sb + h * p.l_sh + qr] =
-          !ok ? __builtin_nanf("") : any ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+    for (int k = 0; k < IT; ++k) {
+      const int qr = qt * BM + rg * RG + k * RG1 + rr;
+      if (qr >= p.N) continue;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kMaxRanges; ++j) {
+        const bf16x4 hv = __builtin_bit_cast(bf16x4, raw[k][j]);
+        acc += w_s[j * RG + k * RG1 + rr] * floatx4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
+      }
+      bf16x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
+      __bf16* orow = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_sn;
+      *reinterpret_cast<bf16x4*>(orow + dv0) = o4;
+    }
   }
-  __syncthreads();
-  // chunk c4 = db*8 + r4*2 + g covers dv = db*32 + r4*8 + g*4 .. +4
-  const int dv0 = (c4 >> 3) * 32 + ((c4 >> 1) & 3) * 8 + (c4 & 1) * 4;
-#pragma unroll
-  for (int k = 0; k < IT; ++k) {
-    const int qr = qt * BM + rg * RG + k * RG1 + rr;
-    if (qr >= p.N) continue;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < kMaxRanges; ++j) acc += w_s[j * RG + k * RG1 + rr] * v[k][j];
-    bf16x4 o4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
-    __bf16* orow = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_sn;
-    *reinterpret_cast<bf16x4*>(orow + dv0) = o4;
-  }
-}
+};
 
 // Merge blocks of the forward kernel itself (blocks n_units on): split query tiles from
 // the last one, then b*h, then groups of rows. The units of the tile publish their
@@ -347,7 +363,7 @@ constexpr int kMaxMergePolls = 1 << 20;
 
 template <int DV>
 __device__ void merge_block(const Params& p, int m, float* w_s) {
-  constexpr int RG = kFusedMergeItems * 256 / (DV / 4);
+  using MI = MergeItems<DV, kFusedMergeItems>;
   constexpr int groups = merge_groups(DV, kFusedMergeItems);
   const int BH = p.B * p.H;
   const int rg = m % groups;
@@ -356,34 +372,49 @@ __device__ void merge_block(const Params& p, int m, float* w_s) {
   const int qt = p.n_qt - 1 - t / BH;
   const int nch = p.nchq[qt];
   const uint64_t* flag = p.part_flag + p.ubase[qt] + bh * nch;
-  int* ok_s = reinterpret_cast<int*>(w_s + kMaxRanges * RG);
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    bool done = false;
-    for (int it = 0; it < kMaxMergePolls; ++it) {
-      const bool mine = lane >= nch || __hip_atomic_load(flag + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.seq;
-      if (__builtin_amdgcn_ballot_w64(!mine) == 0) {
-        done = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(8);
+  int* ready_s = reinterpret_cast<int*>(w_s + kMaxRanges * MI::RG);
+  MI items;
+  items.init(p, qt, bh, rg, nch);
+  // Each range's loads are issued as soon as its flag holds this call's number, so a
+  // block that waits for the last ranges already holds the others.
+  const unsigned all = (1u << nch) - 1u;
+  unsigned loaded = 0;
+  for (int it = 0; it < kMaxMergePolls && loaded != all; ++it) {
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const bool mine = lane < nch && __hip_atomic_load(flag + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.seq;
+      const uint64_t ready = __builtin_amdgcn_ballot_w64(mine);
+      if (lane == 0) *ready_s = (int)(unsigned)ready;
     }
-    if (lane == 0) *ok_s = done;
+    __syncthreads();
+    const unsigned fresh = (unsigned)__builtin_amdgcn_readfirstlane(*ready_s) & ~loaded;
+    __syncthreads();  // every wave has read the mask before wave 0 writes the next one
+    static_for<0, kMaxRanges>([&](auto J) {
+      if (fresh >> decltype(J)::value & 1u) items.template load<decltype(J)::value, kLoadAgentScope>();
+    });
+    loaded |= fresh;
+    if (loaded != all) __builtin_amdgcn_s_sleep(8);
   }
-  __syncthreads();
-  merge_rows<DV, kFusedMergeItems, true>(p, qt, bh, rg, w_s, *ok_s != 0);
+  items.combine(p, qt, bh, w_s, loaded == all);
 }
 
 // Separate merge kernel (used where the forward kernel runs without merge blocks):
 // block = (group of rows, b*h, query tile) = (blockIdx.x, .y, .z).
 template <int DV>
 __global__ __launch_bounds__(256) void merge_split(Params p) {
-  __shared__ float w_s[kMaxRanges * (256 / (DV / 4))];
+  using MI = MergeItems<DV, 1>;
+  __shared__ float w_s[kMaxRanges * MI::RG];
   const int qt = blockIdx.z;
   // the argument cache lines used below and the tile's table entries in one round trip
   asm volatile("" ::"s"(p.out), "s"(p.o_sn), "s"(p.N), "s"(p.part_ml), "s"(p.ubase[qt]), "s"((int)p.nchq[qt]));
-  if (p.nchq[qt] == 1) return;  // written directly by the forward kernel
-  merge_rows<DV, 1, false>(p, qt, blockIdx.y, blockIdx.x, w_s, true);
+  const int nch = p.nchq[qt];
+  if (nch == 1) return;  // written directly by the forward kernel
+  MI items;
+  items.init(p, qt, blockIdx.y, blockIdx.x, nch);
+  static_for<0, kMaxRanges>([&](auto J) {
+    if (decltype(J)::value < nch) items.template load<decltype(J)::value, 0>();
+  });
+  items.combine(p, qt, blockIdx.y, w_s, true);
 }
 
 template <int D, int DV, bool BIAS>
