@@ -15,7 +15,8 @@ import os
 __all__ = [
     "FaError", "FA_OK", "FA_F32", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
     "STATUS", "lib", "library_path", "fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size",
-    "fa_status_string", "fa_version", "fa_shutdown", "make_strides", "FaStrides", "EXPORTED",
+    "fa_status_string", "fa_version", "fa_shutdown", "fa_plan_describe", "make_strides", "FaStrides",
+    "FaPlanInfo", "EXPORTED",
 ]
 
 FA_OK = 0
@@ -31,7 +32,7 @@ STATUS = {
 
 # every symbol include/fa.h declares
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
-            "fa_version", "fa_shutdown")
+            "fa_version", "fa_shutdown", "fa_plan_describe")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -50,6 +51,12 @@ class FaStrides(ctypes.Structure):
     _fields_ = [("q", ctypes.c_int64 * 3), ("k", ctypes.c_int64 * 3), ("v", ctypes.c_int64 * 3),
                 ("out", ctypes.c_int64 * 3), ("bias", ctypes.c_int64 * 3),
                 ("lse", ctypes.c_int64 * 2)]
+
+
+class FaPlanInfo(ctypes.Structure):
+    _fields_ = [("split", ctypes.c_int32), ("n_qtiles", ctypes.c_int32), ("qtile_rows", ctypes.c_int32),
+                ("key_tile", ctypes.c_int32), ("units", ctypes.c_int32), ("merge_blocks", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -80,6 +87,9 @@ def lib():
     L.fa_version.restype = ctypes.c_int
     L.fa_shutdown.argtypes = []
     L.fa_shutdown.restype = None
+    L.fa_plan_describe.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(FaPlanInfo), ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+    L.fa_plan_describe.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -94,6 +104,18 @@ def fa_version() -> int:
 
 def fa_shutdown() -> None:
     lib().fa_shutdown()
+
+
+def fa_plan_describe(B, H, N, d, dv, dtype, causal, compute_units, max_units=4096):
+    """The work plan of a problem on a device with `compute_units` CUs (no GPU needed):
+    (FaPlanInfo, list of packed unit-table words; empty unless the plan splits)."""
+    info = FaPlanInfo()
+    table = (ctypes.c_uint32 * max_units)()
+    st = lib().fa_plan_describe(B, H, N, d, dv, dtype, FA_MASK_CAUSAL if causal else FA_MASK_NONE,
+                                compute_units, ctypes.byref(info), table, max_units)
+    _check(st)
+    units = list(table[: min(info.units, max_units)]) if info.split else []
+    return info, units
 
 
 def _check(status: int) -> None:

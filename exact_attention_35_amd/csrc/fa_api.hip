@@ -28,6 +28,7 @@
 #include <utility>
 
 #include "fa.h"
+#include "fa_plan.h"
 #include "fa_internal.h"
 
 namespace {
@@ -259,6 +260,12 @@ int64_t cut_ranges(const Plan& pl, int64_t N, int64_t BH, bool causal, int cus, 
   return u;
 }
 
+// One unit table entry: query tile (bits 0-7), first key tile (8-16), key-tile count
+// (17-25), b*h (26-31).
+uint32_t pack_unit(int qt, int begin, int len, int64_t bh) {
+  return (uint32_t)qt | (uint32_t)begin << 8 | (uint32_t)len << 17 | (uint32_t)bh << 26;
+}
+
 Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask, int cus) {
   Plan pl;
   pl.mfma = dtype == FA_BF16;  // d, dv in {64, 128} already checked
@@ -367,8 +374,7 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
       p.nchq[qt] = (uint8_t)r.nch;
       for (int64_t bh = 0; bh < P.B * P.H; ++bh)
         for (int c = 0; c < r.nch; ++c)
-          p.unit_info[acc + bh * r.nch + c] =
-              (uint32_t)qt | (uint32_t)r.begin[c] << 8 | (uint32_t)r.len[c] << 17 | (uint32_t)bh << 26;
+          p.unit_info[acc + bh * r.nch + c] = pack_unit(qt, r.begin[c], r.len[c], bh);
       acc += (int32_t)(P.B * P.H * r.nch);
     }
     p.ubase[pl.n_qt] = acc;
@@ -506,6 +512,32 @@ const char* fa_status_string(int status) {
 }
 
 int fa_version(void) { return FA_VERSION; }
+
+int fa_plan_describe(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask_mode,
+                     int compute_units, fa_plan_info* info, uint32_t* unit_info, int max_units) {
+  if (!info || compute_units < 1) return FA_ERR_NULL;
+  const int st = check_shape(B, H, N, d, dv, dtype, mask_mode);
+  if (st != FA_OK) return st;
+  const std::shared_ptr<const Plan> plan = cached_plan(B, H, N, d, dv, dtype, mask_mode, compute_units);
+  const Plan& pl = *plan;
+  info->split = pl.split ? 1 : 0;
+  info->n_qtiles = pl.mfma ? pl.n_qt : 0;
+  info->qtile_rows = pl.mfma ? fa::kMfmaBM : fa::kGenericBM;
+  info->key_tile = fa::kMfmaBN;
+  info->units = pl.mfma ? pl.grid : 0;
+  info->merge_blocks = pl.merge_blocks;
+  info->workspace_bytes = pl.ws_bytes;
+  if (pl.split && unit_info) {
+    int u = 0;
+    for (int qt = pl.n_qt - 1; qt >= 0; --qt) {
+      const Plan::Ranges& r = pl.ranges[qt];
+      for (int64_t bh = 0; bh < B * H; ++bh)
+        for (int c = 0; c < r.nch; ++c, ++u)
+          if (u < max_units) unit_info[u] = pack_unit(qt, r.begin[c], r.len[c], bh);
+    }
+  }
+  return FA_OK;
+}
 
 void fa_shutdown(void) {
   std::lock_guard<std::mutex> lk(g_ws_mu);

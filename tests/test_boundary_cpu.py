@@ -23,7 +23,8 @@ BASE = 0x7f0000000000  # fake, 256-byte aligned device addresses
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(os.path.join(ROOT, "include", f)).read()
+                   for f in sorted(os.listdir(os.path.join(ROOT, "include"))) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
 

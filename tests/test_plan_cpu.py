@@ -1,0 +1,88 @@
+"""CPU: the work plan of fa_fwd (fa_plan_describe, no GPU needed).
+
+Every (batch*head, query tile) must see each of its key tiles in exactly one unit,
+the unit table must fit its packed fields and the kernel's limits, and the plan
+must keep the properties the kernels rely on (query tiles from the last one, the
+same cut for every b*h, at most 16 ranges per tile, one dispatch wave of units).
+"""
+
+import math
+import os
+
+import pytest
+
+from exact_attention_35_amd import capi
+
+pytestmark = pytest.mark.skipif(not os.path.exists(capi.library_path()),
+                                reason="libfa.so not built (run __graft_entry__.build())")
+
+
+def ntiles(N, qt, causal, bm=128, bn=64):
+    kv = min(N, (qt + 1) * bm) if causal else N
+    return (kv + bn - 1) // bn
+
+
+SHAPES = [  # (B, H, N, d, dv, causal)
+    (1, 1, 8192, 128, 128, True), (1, 1, 8192, 128, 128, False), (1, 1, 1000, 128, 128, True),
+    (1, 2, 1100, 128, 128, True), (1, 2, 1500, 128, 128, True), (1, 1, 16384, 128, 128, True),
+    (1, 1, 32640, 128, 128, True), (1, 1, 32640, 64, 64, False), (2, 16, 600, 64, 128, False),
+    (1, 64, 200, 64, 64, True), (1, 65, 200, 64, 64, True), (1, 1, 1, 64, 64, True),
+    (1, 1, 129, 128, 64, True), (3, 5, 1000, 128, 64, False), (1, 8, 3000, 128, 128, True),
+    (4, 32, 4096, 128, 128, True), (1, 8, 32768, 128, 128, True), (2, 16, 2048, 64, 128, False),
+]
+
+
+@pytest.mark.parametrize("cus", [256, 80])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s}" for s in SHAPES])
+def test_plan_covers_every_key_tile_once(shape, cus):
+    B, H, N, d, dv, causal = shape
+    info, table = capi.fa_plan_describe(B, H, N, d, dv, capi.FA_BF16, causal, cus)
+    BH = B * H
+    n_qt = math.ceil(N / 128)
+    assert (info.n_qtiles, info.qtile_rows, info.key_tile) == (n_qt, 128, 64)
+    if not info.split:
+        assert info.units == BH * n_qt and info.merge_blocks == 0 and info.workspace_bytes == 0
+        return
+    # split only where the query tiles leave CUs idle, within the table's limits
+    assert BH * n_qt < cus and BH <= 64 and n_qt <= 256
+    assert len(table) == info.units <= min(512, 2 * cus)
+    ranges, order = {}, []
+    for w in table:
+        qt, t0, n, bh = w & 0xFF, (w >> 8) & 0x1FF, (w >> 17) & 0x1FF, w >> 26
+        assert n >= 1 and qt < n_qt and bh < BH
+        ranges.setdefault((qt, bh), []).append((t0, n))
+        order.append(qt)
+    assert order == sorted(order, reverse=True)  # query tiles from the last one
+    n_split = 0
+    for qt in range(n_qt):
+        cuts = [ranges[(qt, bh)] for bh in range(BH)]
+        assert all(c == cuts[0] for c in cuts)  # the same cut for every b*h
+        assert 1 <= len(cuts[0]) <= 16
+        t = 0
+        for t0, n in cuts[0]:
+            assert t0 == t
+            t += n
+        assert t == ntiles(N, qt, causal)
+        n_split += len(cuts[0]) > 1
+    assert n_split > 0
+    assert info.merge_blocks == n_split * BH * (128 * dv // (1024 * 2))
+    assert info.workspace_bytes >= info.units * (8 + 2 * 128 * 4 + 128 * dv * 2)
+
+
+def test_headline_plan_fills_the_chip():
+    # the single causal head of N = 8192 is cut into about two units per CU
+    info, table = capi.fa_plan_describe(1, 1, 8192, 128, 128, capi.FA_BF16, True, 256)
+    assert info.split and 400 <= info.units <= 512
+    # the first workgroups of the CUs get more key tiles than the second ones
+    first = [(w >> 17) & 0x1FF for w in table[:256]]
+    second = [(w >> 17) & 0x1FF for w in table[256:]]
+    assert sum(first) / len(first) > sum(second) / len(second)
+
+
+def test_fp32_and_invalid_plans():
+    info, table = capi.fa_plan_describe(1, 1, 256, 64, 64, capi.FA_F32, False, 256)
+    assert (info.split, info.n_qtiles, info.units, info.qtile_rows) == (0, 0, 0, 64) and table == []
+    with pytest.raises(capi.FaError):
+        capi.fa_plan_describe(1, 1, 256, 96, 64, capi.FA_BF16, False, 256)
+    with pytest.raises(capi.FaError):
+        capi.fa_plan_describe(1, 1, 256, 64, 64, capi.FA_BF16, False, 0)
