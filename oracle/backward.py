@@ -1,0 +1,146 @@
+"""Plain fp64 CPU oracle for the gradients of the exact attention forward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links this
+module; only the tests and the benchmark's CPU-baseline leg do. It shares no code,
+constants or helpers with the HIP library.
+
+The page "编译器与内核" (Compilers and kernels), section "FlashAttention 围绕 IO 改写算法",
+notes that the backward pass can recompute the score and probability blocks instead of
+keeping them; it does not print the gradient formulas. They follow from the forward
+definition of the same section,
+
+    S = Q K^T / sqrt(d) + C,   P = rowsoftmax(S),   O = P V,
+
+by the chain rule, for an upstream gradient dO of O:
+
+    dV = P^T dO                               (O is linear in V)
+    dP = dO V^T                               (O is linear in P)
+    dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)   (Jacobian of one softmax row)
+    dQ = dS K / sqrt(d),   dK = dS^T Q / sqrt(d)
+
+C (bias and mask) is a constant of the problem: no gradient is formed for it. Keys a
+row may not use have P_ij = 0, so they receive nothing. The oracle forms P from the
+definition (it does not reuse a saved log-sum-exp), materialises S, P, dP and dS in
+float64 and never tiles keys. Rows are processed in chunks (their contributions to dK
+and dV are summed chunk after chunk in float64); rows are independent in the
+definition, so chunking only changes the fp64 rounding order of those sums.
+
+Readings (each is listed in the design notes): the same ones as the forward oracle
+(scale 1/sqrt(d) with d the Q/K width; C added after scaling; causal is top-left
+aligned; bias and mask add; bias broadcasts over batch or heads). A row with no
+allowed key has no gradient (dQ row = 0, and it adds nothing to dK, dV): a
+convention, parity unpinned.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .attention import EmptyRowError, _as_f64, _bias_slice
+
+__all__ = ["sdpa_backward_reference", "sdpa_backward_reference_sampled"]
+
+
+def _probabilities(qbh, kbh, c_rows, rows, causal, scale, allow_empty_rows):
+    """P for rows `rows` of one (batch, head), from the forward definition."""
+    s = (qbh[rows] @ kbh.T) * scale
+    if c_rows is not None:
+        s = s + c_rows
+    if causal:
+        keys = np.arange(kbh.shape[0])[None, :]
+        s = np.where(keys > rows[:, None], -np.inf, s)
+    m = s.max(axis=1)
+    empty = ~np.isfinite(m) & (m < 0)
+    if empty.any() and not allow_empty_rows:
+        raise EmptyRowError(f"{int(empty.sum())} query row(s) have no allowed key")
+    e = np.exp(s - np.where(empty, 0.0, m)[:, None])
+    ell = e.sum(axis=1)
+    p = e / np.where(empty, 1.0, ell)[:, None]
+    p[empty] = 0.0
+    return p
+
+
+def _row_block_grads(qbh, kbh, vbh, dobh, c_rows, rows, causal, scale, allow_empty_rows):
+    """dQ rows and the rows' contributions to dK, dV (all keys) for one (b, h)."""
+    p = _probabilities(qbh, kbh, c_rows, rows, causal, scale, allow_empty_rows)
+    do = dobh[rows]
+    dv_part = p.T @ do                                # dV = P^T dO
+    dp = do @ vbh.T                                   # dP = dO V^T
+    ds = p * (dp - (p * dp).sum(axis=1)[:, None])     # softmax Jacobian, row by row
+    dq = (ds @ kbh) * scale                           # dQ = dS K / sqrt(d)
+    dk_part = (ds.T @ qbh[rows]) * scale              # dK = dS^T Q / sqrt(d)
+    return dq, dk_part, dv_part
+
+
+def _check_shapes(q, k, v, dout, bias):
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    if k.shape != (B, H, N, d) or v.shape != (B, H, N, dv) or dout.shape != (B, H, N, dv):
+        raise ValueError("q, k, v, dout shapes disagree")
+    if bias is not None and (bias.ndim != 4 or bias.shape[2:] != (N, N)
+                             or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H)):
+        raise ValueError("bias must broadcast to [B, H, N, N]")
+    return B, H, N, d, dv
+
+
+def sdpa_backward_reference(q, k, v, dout, bias=None, causal=False, *, row_chunk=1024,
+                            allow_empty_rows=False):
+    """dQ, dK, dV of every (batch, head) in float64.
+
+    q: [B, H, N, d], k: [B, H, N, d], v and dout: [B, H, N, dv] (logical layout; any real
+    dtype, torch or numpy). bias and causal as in `sdpa_reference`.
+    Returns (dQ [B,H,N,d], dK [B,H,N,d], dV [B,H,N,dv]) as float64 numpy arrays.
+    """
+    q, k, v, dout = (_as_f64(x) for x in (q, k, v, dout))
+    bias = None if bias is None else _as_f64(bias)
+    B, H, N, d, dvw = _check_shapes(q, k, v, dout, bias)
+    scale = 1.0 / math.sqrt(d)
+    dq = np.zeros((B, H, N, d))
+    dk = np.zeros((B, H, N, d))
+    dv = np.zeros((B, H, N, dvw))
+    for b in range(B):
+        for h in range(H):
+            cbh = _bias_slice(bias, b, h)
+            for r0 in range(0, N, row_chunk):
+                rows = np.arange(r0, min(N, r0 + row_chunk))
+                c_rows = None if cbh is None else cbh[rows]
+                dq_, dk_, dv_ = _row_block_grads(q[b, h], k[b, h], v[b, h], dout[b, h], c_rows,
+                                                 rows, causal, scale, allow_empty_rows)
+                dq[b, h, rows] = dq_
+                dk[b, h] += dk_
+                dv[b, h] += dv_
+    return dq, dk, dv
+
+
+def sdpa_backward_reference_sampled(q, k, v, dout, bias, causal, b, h, rows, keys, *,
+                                    row_chunk=1024):
+    """dQ at query rows `rows` and dK, dV at key rows `keys` of one (batch, head).
+
+    For sizes where the full gradients are too large for the CPU: dQ of a row needs only
+    that row; dK and dV of a key need every row's probabilities, so all rows are formed
+    chunk by chunk (S and dP in full, O(N^2 (d + dv)) work) and only the sampled key
+    columns of P and dS are kept. Same definition as `sdpa_backward_reference`.
+    Returns (dQ [len(rows), d], dK [len(keys), d], dV [len(keys), dv]).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    qbh, kbh, vbh, dobh = (_as_f64(x[b, h]) for x in (q, k, v, dout))
+    N, d = qbh.shape
+    scale = 1.0 / math.sqrt(d)
+    sl = None
+    if bias is not None:
+        sl = bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0]
+    c_of = (lambda r: None) if sl is None else (lambda r: _as_f64(sl[r.tolist()]))
+    dq, _, _ = _row_block_grads(qbh, kbh, vbh, dobh, c_of(rows), rows, causal, scale, False)
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), vbh.shape[1]))
+    for r0 in range(0, N, row_chunk):
+        rr = np.arange(r0, min(N, r0 + row_chunk))
+        p = _probabilities(qbh, kbh, c_of(rr), rr, causal, scale, False)
+        dp = dobh[rr] @ vbh.T
+        ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+        dv += p[:, keys].T @ dobh[rr]
+        dk += (ds[:, keys].T @ qbh[rr]) * scale
+    return dq, dk, dv
