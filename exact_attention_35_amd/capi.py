@@ -1,4 +1,4 @@
-"""Thin Python binding of the C ABI in include/fa.h (argument marshalling only).
+"""Thin Python binding of the C ABI in include/*.h (argument marshalling only).
 
 Every function here has the name of the C entry point it wraps. Tensors are torch
 tensors in logical [B, H, N, *] layout with any strides whose innermost axis is
@@ -16,7 +16,7 @@ __all__ = [
     "FaError", "FA_OK", "FA_F32", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
     "STATUS", "lib", "library_path", "fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size",
     "fa_status_string", "fa_version", "fa_shutdown", "fa_plan_describe", "make_strides", "FaStrides",
-    "FaPlanInfo", "EXPORTED",
+    "FaPlanInfo", "EXPORTED", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "FaBwdStrides",
 ]
 
 FA_OK = 0
@@ -30,9 +30,10 @@ STATUS = {
     "FA_ERR_WORKSPACE": -8, "FA_ERR_LAUNCH": -9, "FA_ERR_DEVICE": -10, "FA_ERR_ALLOC": -11,
 }
 
-# every symbol include/fa.h declares
+# every symbol include/*.h declares
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
-            "fa_version", "fa_shutdown", "fa_plan_describe")
+            "fa_version", "fa_shutdown", "fa_plan_describe", "fa_bwd", "fa_bwd_ex",
+            "fa_bwd_workspace_size")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -51,6 +52,12 @@ class FaStrides(ctypes.Structure):
     _fields_ = [("q", ctypes.c_int64 * 3), ("k", ctypes.c_int64 * 3), ("v", ctypes.c_int64 * 3),
                 ("out", ctypes.c_int64 * 3), ("bias", ctypes.c_int64 * 3),
                 ("lse", ctypes.c_int64 * 2)]
+
+
+class FaBwdStrides(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64 * 3) for name in
+                ("q", "k", "v", "out", "grad_out", "grad_q", "grad_k", "grad_v", "bias")] + \
+               [("lse", ctypes.c_int64 * 2)]
 
 
 class FaPlanInfo(ctypes.Structure):
@@ -90,6 +97,14 @@ def lib():
     L.fa_plan_describe.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.POINTER(FaPlanInfo), ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
     L.fa_plan_describe.restype = ctypes.c_int
+    bwd_args = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, i64,
+                ctypes.POINTER(FaBwdStrides), ctypes.c_int, vp]
+    L.fa_bwd.argtypes = bwd_args
+    L.fa_bwd.restype = ctypes.c_int
+    L.fa_bwd_ex.argtypes = bwd_args + [vp, sz]
+    L.fa_bwd_ex.restype = ctypes.c_int
+    L.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    L.fa_bwd_workspace_size.restype = sz
     _lib = L
     return L
 
@@ -220,3 +235,62 @@ def fa_fwd_ex(q, k, v, workspace, bias=None, causal=False, out=None, lse=None, s
                          _stream_handle(stream, q.device), _ptr(workspace), nbytes)
     _check(st)
     return out, lse
+
+
+def _prepare_bwd(q, k, v, out, lse, grad_out, bias, causal, grad_q, grad_k, grad_v):
+    import torch
+
+    B, H, N, d, dv, dt, mask, bias, out, lse, _ = _prepare(q, k, v, bias, causal, out, lse)
+    if tuple(grad_out.shape) != (B, H, N, dv) or grad_out.dtype != q.dtype:
+        raise FaError(STATUS["FA_ERR_SHAPE"], "grad_out must match out")
+    if grad_q is None:
+        grad_q = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+    if grad_k is None:
+        grad_k = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+    if grad_v is None:
+        grad_v = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    s = FaBwdStrides()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("grad_out", grad_out),
+                    ("grad_q", grad_q), ("grad_k", grad_k), ("grad_v", grad_v)):
+        if t.numel() and t.stride(-1) != 1:
+            raise FaError(STATUS["FA_ERR_STRIDE"], f"{name}: innermost axis must be contiguous")
+        st = t.stride()
+        getattr(s, name)[:] = [st[0], st[1], st[2]]
+    if bias is not None:
+        st = bias.stride()
+        s.bias[:] = [st[0], st[1], st[2]]
+    st = lse.stride()
+    s.lse[:] = [st[0], st[1]]
+    return B, H, N, d, dv, dt, mask, bias, out, lse, grad_q, grad_k, grad_v, s
+
+
+def fa_bwd(q, k, v, out, lse, grad_out, bias=None, causal=False, grad_q=None, grad_k=None,
+           grad_v=None, stream=None):
+    """Gradients through fa_bwd: (grad_q, grad_k, grad_v) of fa_fwd's output for the
+    upstream gradient grad_out, from the forward's out and lse. bf16 tensors; outputs are
+    allocated when not given. Enqueued on `stream` (default: torch's current stream)."""
+    (B, H, N, d, dv, dt, mask, bias, out, lse, grad_q, grad_k, grad_v,
+     s) = _prepare_bwd(q, k, v, out, lse, grad_out, bias, causal, grad_q, grad_k, grad_v)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(grad_out), _ptr(bias), mask,
+                      _ptr(grad_q), _ptr(grad_k), _ptr(grad_v), B, H, N, d, dv, ctypes.byref(s), dt,
+                      _stream_handle(stream, q.device))
+    _check(st)
+    return grad_q, grad_k, grad_v
+
+
+def fa_bwd_workspace_size(B, H, N, d, dv, dtype_code, causal) -> int:
+    return int(lib().fa_bwd_workspace_size(B, H, N, d, dv, dtype_code,
+                                           FA_MASK_CAUSAL if causal else FA_MASK_NONE))
+
+
+def fa_bwd_ex(q, k, v, out, lse, grad_out, workspace, bias=None, causal=False, grad_q=None,
+              grad_k=None, grad_v=None, stream=None):
+    """fa_bwd with a caller-provided workspace (a uint8 device tensor)."""
+    (B, H, N, d, dv, dt, mask, bias, out, lse, grad_q, grad_k, grad_v,
+     s) = _prepare_bwd(q, k, v, out, lse, grad_out, bias, causal, grad_q, grad_k, grad_v)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(grad_out), _ptr(bias),
+                         mask, _ptr(grad_q), _ptr(grad_k), _ptr(grad_v), B, H, N, d, dv, ctypes.byref(s),
+                         dt, _stream_handle(stream, q.device), _ptr(workspace), nbytes)
+    _check(st)
+    return grad_q, grad_k, grad_v

@@ -1,5 +1,6 @@
-// Host side of the C ABI declared in include/fa.h: argument validation, the work
-// plan (query tiles and key splits), scratch workspaces, and kernel dispatch.
+// Host side of the C ABI declared in include/fa.h, include/fa_bwd.h and
+// include/fa_plan.h: argument validation, the work plan (query tiles and key splits),
+// scratch workspaces, and kernel dispatch.
 //
 // The contract follows the page "编译器与内核" (Compilers and kernels): a kernel
 // implements a bounded contract over shapes, strides, dtype, layout, aliasing,
@@ -28,6 +29,7 @@
 #include <utility>
 
 #include "fa.h"
+#include "fa_bwd.h"
 #include "fa_plan.h"
 #include "fa_internal.h"
 
@@ -440,6 +442,130 @@ int owned_workspace(int dev, hipStream_t stream, size_t need, void** out) {
   return FA_OK;
 }
 
+// ---------------------------------------------------------------- gradients
+struct BwdProblem {
+  const void *q, *k, *v, *out, *dout;
+  const float* lse;
+  const float* bias;
+  void *dq, *dk, *dv;
+  int64_t B, H, N, d, dvw;
+  int mask, dtype;
+  fa_bwd_strides st;
+};
+
+fa_bwd_strides contiguous_bwd_strides(int64_t H, int64_t N, int64_t d, int64_t dv) {
+  fa_bwd_strides s;
+  const int64_t wd[8] = {d, d, dv, dv, dv, d, d, dv};
+  int64_t* all[8] = {s.q, s.k, s.v, s.out, s.grad_out, s.grad_q, s.grad_k, s.grad_v};
+  for (int t = 0; t < 8; ++t) {
+    all[t][0] = H * N * wd[t];
+    all[t][1] = N * wd[t];
+    all[t][2] = wd[t];
+  }
+  s.bias[0] = H * N * N; s.bias[1] = N * N; s.bias[2] = N;
+  s.lse[0] = H * N; s.lse[1] = N;
+  return s;
+}
+
+// Groups of 64 rows per (b, h) in the row-statistics workspace.
+int64_t bwd_groups(int64_t N) { return (N + fa::kBwdQT - 1) / fa::kBwdQT * 2; }
+
+int check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask) {
+  const int st = check_shape(B, H, N, d, dv, dtype, mask);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  // rows of the statistics workspace are indexed with 32-bit integers
+  if ((B * H) * bwd_groups(N) * 64 >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+size_t bwd_ws_bytes(int64_t B, int64_t H, int64_t N) {
+  return round_up((size_t)(B * H) * (size_t)bwd_groups(N) * 128 * sizeof(float), 256);
+}
+
+int validate_bwd(const BwdProblem& P) {
+  int st = check_bwd_shape(P.B, P.H, P.N, P.d, P.dvw, P.dtype, P.mask);
+  if (st != FA_OK) return st;
+  if (P.B * P.H * P.N == 0) return FA_OK;
+  if (!P.q || !P.k || !P.v || !P.out || !P.dout || !P.lse || !P.dq || !P.dk || !P.dv) return FA_ERR_NULL;
+  const fa_bwd_strides& s = P.st;
+  const void* ptrs[8] = {P.q, P.k, P.v, P.out, P.dout, P.dq, P.dk, P.dv};
+  const int64_t* strd[8] = {s.q, s.k, s.v, s.out, s.grad_out, s.grad_q, s.grad_k, s.grad_v};
+  const int64_t width[8] = {P.d, P.d, P.dvw, P.dvw, P.dvw, P.d, P.d, P.dvw};
+  for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < 3; ++i)
+      if (strd[t][i] < 0) return FA_ERR_STRIDE;
+  for (int i = 0; i < 3; ++i)
+    if (s.bias[i] < 0) return FA_ERR_STRIDE;
+  if (s.lse[0] < 0 || s.lse[1] < 0) return FA_ERR_STRIDE;
+  // tiles of q, k, v and dO are addressed with 32-bit byte offsets
+  if (s.q[2] >= kMaxRowStride || s.k[2] >= kMaxRowStride || s.v[2] >= kMaxRowStride ||
+      s.grad_out[2] >= kMaxRowStride)
+    return FA_ERR_STRIDE;
+  const int64_t sz[3] = {P.B, P.H, P.N};
+  for (int t = 5; t < 8; ++t)
+    if (!non_overlapping(sz, strd[t], 3, width[t])) return FA_ERR_STRIDE;
+  for (int t = 0; t < 8; ++t) {
+    if (!aligned(ptrs[t], 16)) return FA_ERR_ALIGN;
+    for (int i = 0; i < 3; ++i)
+      if ((strd[t][i] * 2) % 16 != 0) return FA_ERR_ALIGN;
+  }
+  if (P.bias && !aligned(P.bias, 4)) return FA_ERR_ALIGN;
+  if (!aligned(P.lse, 4)) return FA_ERR_ALIGN;
+  // outputs overlap no input and no other output
+  Range r[10];
+  for (int t = 0; t < 8; ++t) r[t] = extent(ptrs[t], sz, strd[t], 3, width[t], 2);
+  r[8] = extent(P.lse, sz, s.lse, 2, P.N, 4);
+  r[9] = P.bias ? extent(P.bias, sz, s.bias, 3, P.N, 4) : Range{0, 0};
+  for (int o = 5; o < 8; ++o)
+    for (int t = 0; t < 10; ++t)
+      if (t != o && overlaps(r[o], r[t])) return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+BwdProblem make_bwd_problem(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, const float* bias, int mask_mode, void* dq, void* dk, void* dv,
+                            int64_t B, int64_t H, int64_t N, int64_t d, int64_t dvw,
+                            const fa_bwd_strides* strides, int dtype) {
+  BwdProblem P;
+  P.q = q; P.k = k; P.v = v; P.out = out; P.dout = dout; P.lse = lse; P.bias = bias;
+  P.dq = dq; P.dk = dk; P.dv = dv;
+  P.B = B; P.H = H; P.N = N; P.d = d; P.dvw = dvw; P.mask = mask_mode; P.dtype = dtype;
+  P.st = strides ? *strides : contiguous_bwd_strides(H, N, d, dvw);
+  return P;
+}
+
+int run_bwd(const BwdProblem& P, void* ws, hipStream_t stream) {
+  fa::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  const fa_bwd_strides& s = P.st;
+  p.q = P.q; p.k = P.k; p.v = P.v; p.out = P.out; p.dout = P.dout; p.lse = P.lse; p.bias = P.bias;
+  p.grad_q = P.dq; p.grad_k = P.dk; p.grad_v = P.dv;
+  p.rowstat = static_cast<float*>(ws);
+  p.q_sb = s.q[0]; p.q_sh = s.q[1]; p.q_sn = s.q[2];
+  p.k_sb = s.k[0]; p.k_sh = s.k[1]; p.k_sn = s.k[2];
+  p.v_sb = s.v[0]; p.v_sh = s.v[1]; p.v_sn = s.v[2];
+  p.o_sb = s.out[0]; p.o_sh = s.out[1]; p.o_sn = s.out[2];
+  p.do_sb = s.grad_out[0]; p.do_sh = s.grad_out[1]; p.do_sn = s.grad_out[2];
+  p.dq_sb = s.grad_q[0]; p.dq_sh = s.grad_q[1]; p.dq_sn = s.grad_q[2];
+  p.dk_sb = s.grad_k[0]; p.dk_sh = s.grad_k[1]; p.dk_sn = s.grad_k[2];
+  p.dv_sb = s.grad_v[0]; p.dv_sh = s.grad_v[1]; p.dv_sn = s.grad_v[2];
+  p.b_sb = s.bias[0]; p.b_sh = s.bias[1]; p.b_si = s.bias[2];
+  p.l_sb = s.lse[0]; p.l_sh = s.lse[1];
+  p.B = (int)P.B; p.H = (int)P.H; p.N = (int)P.N; p.d = (int)P.d; p.dv = (int)P.dvw;
+  p.n_grp = (int)bwd_groups(P.N);
+  p.causal = P.mask == FA_MASK_CAUSAL;
+  p.scale = (float)(1.0 / std::sqrt((double)P.d));
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.d));
+  p.n_kv_blocks = (int)(P.B * P.H * ((P.N + fa::kBwdKT - 1) / fa::kBwdKT));
+  const hipError_t e = fa::launch_bwd_bf16(p, stream);
+  if (env_int("FA_LOG"))
+    std::fprintf(stderr, "[fa] bwd B=%lld H=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d kv_blocks=%d ws=%zu\n",
+                 (long long)P.B, (long long)P.H, (long long)P.N, (long long)P.d, (long long)P.dvw, p.causal,
+                 P.bias != nullptr, p.n_kv_blocks, bwd_ws_bytes(P.B, P.H, P.N));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -537,6 +663,48 @@ int fa_plan_describe(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int
     }
   }
   return FA_OK;
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* out, const float* lse,
+              const void* grad_out, const float* bias, int mask_mode, void* grad_q, void* grad_k,
+              void* grad_v, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
+              const fa_bwd_strides* strides, int dtype, void* stream, void* workspace,
+              size_t workspace_bytes) {
+  const BwdProblem P = make_bwd_problem(q, k, v, out, lse, grad_out, bias, mask_mode, grad_q, grad_k, grad_v,
+                                        B, H, N, d, dv, strides, dtype);
+  int st = validate_bwd(P);
+  if (st != FA_OK) return st;
+  if (B * H * N == 0) return FA_OK;
+  int dev = 0;
+  DevInfo di;
+  if ((st = device_info(&dev, &di)) != FA_OK) return st;
+  if (!workspace || workspace_bytes < bwd_ws_bytes(B, H, N) || !aligned(workspace, 256)) return FA_ERR_WORKSPACE;
+  return run_bwd(P, workspace, static_cast<hipStream_t>(stream));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+           const void* grad_out, const float* bias, int mask_mode, void* grad_q, void* grad_k,
+           void* grad_v, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
+           const fa_bwd_strides* strides, int dtype, void* stream) {
+  const BwdProblem P = make_bwd_problem(q, k, v, out, lse, grad_out, bias, mask_mode, grad_q, grad_k, grad_v,
+                                        B, H, N, d, dv, strides, dtype);
+  int st = validate_bwd(P);
+  if (st != FA_OK) return st;
+  if (B * H * N == 0) return FA_OK;
+  int dev = 0;
+  DevInfo di;
+  if ((st = device_info(&dev, &di)) != FA_OK) return st;
+  void* ws = nullptr;
+  st = owned_workspace(dev, static_cast<hipStream_t>(stream), bwd_ws_bytes(B, H, N), &ws);
+  if (st != FA_OK) return st;
+  return run_bwd(P, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype,
+                             int mask_mode) {
+  if (check_bwd_shape(B, H, N, d, dv, dtype, mask_mode) != FA_OK) return 0;
+  if (B * H * N == 0) return 0;
+  return bwd_ws_bytes(B, H, N);
 }
 
 void fa_shutdown(void) {

@@ -1,0 +1,480 @@
+// Gradients of the bf16 attention forward on the gfx950 matrix cores (MFMA), fp32
+// accumulation.
+//
+// The page "编译器与内核" (Compilers and kernels), section "FlashAttention 围绕 IO 改写算法",
+// notes that the backward pass recomputes the score and probability blocks rather
+// than keeping them. The gradients themselves are the chain rule of the forward
+// definition S = Q K^T / sqrt(d) + C, P = rowsoftmax(S), O = P V:
+//     P_ij = exp(S_ij - lse_i),            D_i = dO_i . O_i  (= sum_j P_ij dP_ij)
+//     dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D),
+//     dQ = dS K / sqrt(d),   dK = dS^T Q / sqrt(d).
+// P is recomputed block by block from the forward's log-sum-exp, so neither the scores
+// nor the probabilities ever reach memory. C gets no gradient.
+//
+// Mapping onto CDNA4 (this file's own design):
+//  * A row-statistics kernel forms D_i = dO_i . O_i and lse_i * log2(e) for every row
+//    and stores them in groups of 64 rows (the lse of rows past N, or of rows with no
+//    allowed key, is stored as +inf so that their probabilities are exactly 0).
+//  * One grid holds two kinds of workgroups (4 waves each). dK/dV blocks own 128 keys
+//    (32 per wave) and stream the query rows in steps of 64; dQ blocks own 128 query
+//    rows (32 per wave) and stream the keys in steps of 64. Every sum is formed inside
+//    one workgroup in a fixed order: no atomics, bitwise reproducible.
+//  * dK/dV blocks: with the wave's K and V rows held as B operands in registers,
+//    S = Q K^T and dP = dO V^T come out with one key per lane (lane l: key l mod 32,
+//    16 of a 32-row query block); the bf16-rounded P and dS in these registers are
+//    directly the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands
+//    (dO^T, Q^T) are transposing LDS reads (ds_read_b64_tr_b16) of the same tiles that
+//    fed S and dP. lse and D of the lane's 16 rows are four 16-byte LDS reads each.
+//  * dQ blocks mirror the forward: S^T = K Q^T and dP^T = V dO^T with the wave's Q and
+//    dO rows held as B operands (one query per lane, so lse and D are per-lane
+//    scalars), then dQ^T += K^T dS^T with K^T read transposed from the K tile.
+//  * Tiles go from global memory straight into LDS (buffer loads with the LDS
+//    destination), two stages, one barrier per step. Q, dO (dK/dV blocks) and K (dQ
+//    blocks) are read both row-wise and transposed, so their rows use one XOR swizzle
+//    of the 16-byte chunks that keeps both reads free of bank conflicts: key(row) =
+//    s(row mod 4) ^ ((row / 4) mod 4), s = (0, 10, 4, 14).
+//  * Causal: a dK/dV block starts at the query step of its first key; a dQ block ends
+//    at the key tile of its last row; waves skip blocks that lie entirely in the
+//    masked triangle, and element masks use the same comparison as the forward.
+
+#include "fa_internal.h"
+#include "fa_mfma_common.h"
+
+namespace fa {
+namespace {
+
+template <int D, int DV>
+struct BwdCfg {
+  static constexpr int NT = 256;
+  static constexpr int KT = kBwdKT;  // keys of a dK/dV block
+  static constexpr int QS = 64;      // query rows per step of a dK/dV block
+  static constexpr int QT = kBwdQT;  // query rows of a dQ block
+  static constexpr int KS = 64;      // keys per step of a dQ block
+  static constexpr int QTILE = QS * D * 2;
+  static constexpr int OTILE = QS * DV * 2;
+  static constexpr int VEC = 2 * QS * 4;  // lse*log2(e) and D of a query step
+  static constexpr int KTILE = KS * D * 2;
+  static constexpr int VTILE = KS * DV * 2;
+  static constexpr int STAGE_KV = QTILE + OTILE + VEC;
+  static constexpr int STAGE_Q = KTILE + VTILE;
+  static constexpr int STAGE = STAGE_KV > STAGE_Q ? STAGE_KV : STAGE_Q;
+};
+
+// Chunk swizzle of tiles read both row-wise and transposed (see the header comment).
+__device__ __forceinline__ constexpr int dual_key(int row) {
+  return ((row & 1) * 10 + (row & 2) * 2) ^ ((row >> 2) & 3);
+}
+
+// Copy of rows r0 .. r0 + ROWS - 1 of a [N, W] bf16 matrix (row stride sn elements) into
+// an LDS tile of ROWS x W, 16 bytes per lane per instruction, chunk-swizzled by
+// dual_key. Lane `lane` of instruction i of wave `wave` fills the 16-byte slot
+// (wave*NLD + i)*64 + lane: row slot/CH, physical chunk slot%CH, which holds logical
+// chunk (slot%CH) ^ key(row). The buffer resource covers only the rows below N, so rows
+// past the end read as zeros.
+template <int W, int ROWS>
+struct TileCopy2 {
+  static constexpr int CH = W / 8;
+  static constexpr int NLD = ROWS * W * 2 / (256 * 16);
+  static_assert(NLD >= 1 && ROWS * W * 2 == NLD * 256 * 16, "tile must be a whole number of block copies");
+  int off[NLD];
+  __device__ __forceinline__ void init(int64_t sn, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int slot = (wave * NLD + i) * 64 + lane;
+      const int row = slot / CH;
+      off[i] = (int)(row * sn * 2) + ((slot % CH) ^ (dual_key(row) & (CH - 1))) * 16;
+    }
+  }
+  __device__ __forceinline__ void copy(unsigned char* dst, const __bf16* base, int64_t sn, int r0, int N,
+                                       int wave) const {
+    const int rows = min(ROWS, N - r0);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(base + (int64_t)r0 * sn), 0, rows * (int)sn * 2, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, dst + (wave * NLD + i) * 1024), 16, off[i], 0, 0, 0);
+  }
+};
+
+// Operand reads from a dual-swizzled LDS tile of W bf16 per row.
+template <int W>
+struct TileReads {
+  static constexpr int CH = W / 8;
+  int roff[W / 16];     // row-wise read: row l32 (+32*blk), logical chunk 2*kk + g
+  int toff[2][W / 32];  // transposing read: half hh, 32-column block db
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int kk = 0; kk < W / 16; ++kk) roff[kk] = l32 * (W * 2) + (((2 * kk + g) ^ (dual_key(l32) & (CH - 1))) * 16);
+    // Transposing read (A operand with k = 16 rows of group sg): within a 16-lane group
+    // G, lane L reads row 16*sg + 8*hh + 4*g + L/4 at columns c0 .. c0+3,
+    // c0 = 32*db + 16*(G&1) + 4*(L&3); the swizzle key of that row does not depend on sg.
+    const int G = lane >> 4, L = lane & 15;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = 8 * hh + 4 * g + (L >> 2);
+      const int key = dual_key(row) & (CH - 1);
+#pragma unroll
+      for (int db = 0; db < W / 32; ++db) {
+        const int col = 32 * db + 16 * (G & 1) + 4 * (L & 3);
+        toff[hh][db] = row * (W * 2) + (((col >> 3) ^ key) * 16) + (col & 7) * 2;
+      }
+    }
+  }
+  // A or B operand: row 32*blk + (lane mod 32), k = 16*kk + 8*g .. +7
+  __device__ __forceinline__ bf16x8 row(const unsigned char* t, int blk, int kk) const {
+    return *reinterpret_cast<const bf16x8*>(t + blk * 32 * (W * 2) + roff[kk]);
+  }
+  // A operand of a product over the tile's rows: column 32*db + (lane mod 32), with k
+  // running over the 16 rows of group sg in the order the accumulator layout holds them.
+  __device__ __forceinline__ bf16x8 tr(const unsigned char* t, int sg, int db) const {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, t + 16 * sg * (W * 2) + toff[0][db]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, t + 16 * sg * (W * 2) + toff[1][db]));
+    bf16x8 a;
+    a.lo = __builtin_bit_cast(bf16x4, lo);
+    a.hi = __builtin_bit_cast(bf16x4, hi);
+    return a;
+  }
+};
+
+// Row statistics: 16 threads per row. rowstat group layout: see BwdParams.
+template <int DV>
+__global__ __launch_bounds__(256) void bwd_rowstat(BwdParams p) {
+  constexpr int EL = DV / 16;  // elements per thread
+  const int row = blockIdx.x * 16 + threadIdx.x / 16;
+  const int part = threadIdx.x % 16;
+  const int Np = p.n_grp * 64;
+  const int bh = row / Np, i = row % Np;
+  const int b = bh / p.H, h = bh % p.H;
+  float acc = 0.f;
+  if (i < p.N) {
+    const __bf16* o = static_cast<const __bf16*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_sn + part * EL;
+    const __bf16* g = static_cast<const __bf16*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)i * p.do_sn + part * EL;
+    typedef __bf16 vec_t __attribute__((ext_vector_type(EL)));
+    const vec_t ov = *reinterpret_cast<const vec_t*>(o);
+    const vec_t gv = *reinterpret_cast<const vec_t*>(g);
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc = fmaf((float)ov[e], (float)gv[e], acc);
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (part == 0) {
+    float l2 = INFINITY;
+    if (i < p.N) {
+      const float l = p.lse[b * p.l_sb + h * p.l_sh + i];
+      l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
+    float* grp = p.rowstat + ((int64_t)bh * p.n_grp + i / 64) * 128;
+    grp[i % 64] = l2;
+    grp[64 + i % 64] = i < p.N ? acc : 0.f;
+  }
+}
+
+// ---- dK, dV of 128 keys of one (b, h) ----
+template <int D, int DV, bool BIAS>
+__device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsigned char* st1) {
+  using C = BwdCfg<D, DV>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int BH = p.B * p.H;
+  const int bh = blk % BH, kt = blk / BH;
+  const int b = bh / p.H, h = bh % p.H;
+  const int N = p.N;
+  const int k0 = kt * C::KT;
+  const int wk0 = k0 + wave * 32;
+  const int key = wk0 + l32;  // this lane's key
+  const bool kvalid = key < N;
+
+  const __bf16* qp = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const __bf16* gp = static_cast<const __bf16*>(p.dout) + b * p.do_sb + h * p.do_sh;
+  const __bf16* kp = static_cast<const __bf16*>(p.k) + b * p.k_sb + h * p.k_sh;
+  const __bf16* vp = static_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh;
+  const float* stat = p.rowstat + (int64_t)bh * p.n_grp * 128;
+
+  // K^T and V^T as B operands: lane holds its key, dims 16*kk + 8*g .. +7
+  bf16x8 kreg[D / 16], vreg[DV / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    kreg[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(kp + (int64_t)key * p.k_sn + kk * 16 + g * 8) : bf16x8{};
+#pragma unroll
+  for (int kk = 0; kk < DV / 16; ++kk)
+    vreg[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(vp + (int64_t)key * p.v_sn + kk * 16 + g * 8) : bf16x8{};
+
+  const float* bcol = nullptr;  // bias column of this lane's key (rows added per element)
+  if constexpr (BIAS) bcol = p.bias + b * p.b_sb + h * p.b_sh + min(key, N - 1);
+
+  TileCopy2<D, C::QS> qcp;
+  TileCopy2<DV, C::QS> gcp;
+  qcp.init(p.q_sn, wave, lane);
+  gcp.init(p.do_sn, wave, lane);
+  TileReads<D> qr;
+  TileReads<DV> gr;
+  qr.init(lane);
+  gr.init(lane);
+
+  // query steps: causal blocks start at the step that holds their first key
+  const int qs0 = p.causal ? (k0 / C::QS) * C::QS : 0;
+  const int nsteps = (N - qs0 + C::QS - 1) / C::QS;
+  auto copy_step = [&](unsigned char* st, int qs) {
+    qcp.copy(st, qp, p.q_sn, qs, N, wave);
+    gcp.copy(st + C::QTILE, gp, p.do_sn, qs, N, wave);
+    if (wave == 0 && lane < 32) {  // the step's 64 lse and 64 D values: one 512-byte group
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(stat + (qs / 64) * 128), 0, 512, kBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, st + C::QTILE + C::OTILE), 16, lane * 16, 0, 0, 0);
+    }
+  };
+
+  floatx16 dkacc[D / 32], dvacc[DV / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dkacc[i] = floatx16{};
+#pragma unroll
+  for (int i = 0; i < DV / 32; ++i) dvacc[i] = floatx16{};
+
+  const float cs = BIAS ? kLog2e : p.scale_log2;
+  if (nsteps > 0) copy_step(st0, qs0);
+  for (int s = 0; s < nsteps; ++s) {
+    unsigned char* cur = (s & 1) ? st1 : st0;
+    unsigned char* nxt = (s & 1) ? st0 : st1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // step s has landed; every wave is done with step s-1's stage
+    const int qs = qs0 + s * C::QS;
+    if (s + 1 < nsteps) copy_step(nxt, qs + C::QS);
+    const unsigned char* qt_ = cur;
+    const unsigned char* gt_ = cur + C::QTILE;
+    const float* vec = reinterpret_cast<const float*>(cur + C::QTILE + C::OTILE);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qb0 = qs + qb * 32;
+      if (p.causal && qb0 + 31 < wk0) continue;  // every (row, key) of the block is masked
+      if (qb0 >= N) continue;
+      float bv[BIAS ? 16 : 1];
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = qb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          bv[r] = bcol[(int64_t)min(q, N - 1) * p.b_si];
+        }
+      }
+      floatx16 sacc{}, dpacc{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(qr.row(qt_, qb, kk), kreg[kk], sacc);
+#pragma unroll
+      for (int kk = 0; kk < DV / 16; ++kk) dpacc = mfma32(gr.row(gt_, qb, kk), vreg[kk], dpacc);
+      // rows of register r: qb0 + 8*(r/4) + 4*g + r%4
+      floatx4 l4[4], d4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l4[j] = *reinterpret_cast<const floatx4*>(vec + qb * 32 + 8 * j + 4 * g);
+        d4[j] = *reinterpret_cast<const floatx4*>(vec + 64 + qb * 32 + 8 * j + 4 * g);
+      }
+      const bool edge = p.causal && qb0 < wk0 + 31;
+      bf16x8 pk[2], dsk[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = BIAS ? fmaf(sacc[r], p.scale, bv[r]) * cs : sacc[r] * cs;
+        float pr = __builtin_amdgcn_exp2f(x - l4[r >> 2][r & 3]);
+        if (edge && key > qb0 + 8 * (r >> 2) + 4 * g + (r & 3)) pr = 0.f;
+        const float ds = pr * (dpacc[r] - d4[r >> 2][r & 3]);
+        pk[r >> 3][r & 7] = (__bf16)pr;
+        dsk[r >> 3][r & 7] = (__bf16)ds;
+      }
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+#pragma unroll
+        for (int db = 0; db < DV / 32; ++db) dvacc[db] = mfma32(gr.tr(gt_, 2 * qb + kq, db), pk[kq], dvacc[db]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) dkacc[db] = mfma32(qr.tr(qt_, 2 * qb + kq, db), dsk[kq], dkacc[db]);
+      }
+    }
+  }
+
+  if (!kvalid) return;
+  // accumulator register r of block db holds column key, dim 32*db + 8*(r/4) + 4*g + r%4
+  __bf16* dkp = static_cast<__bf16*>(p.grad_k) + b * p.dk_sb + h * p.dk_sh + (int64_t)key * p.dk_sn;
+  __bf16* dvp = static_cast<__bf16*>(p.grad_v) + b * p.dv_sb + h * p.dv_sh + (int64_t)key * p.dv_sn;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      bf16x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(dkacc[db][r4 * 4 + e] * p.scale);
+      *reinterpret_cast<bf16x4*>(dkp + db * 32 + r4 * 8 + g * 4) = o4;
+    }
+#pragma unroll
+  for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      bf16x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)dvacc[db][r4 * 4 + e];
+      *reinterpret_cast<bf16x4*>(dvp + db * 32 + r4 * 8 + g * 4) = o4;
+    }
+}
+
+// ---- dQ of 128 query rows of one (b, h) ----
+template <int D, int DV, bool BIAS>
+__device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsigned char* st1) {
+  using C = BwdCfg<D, DV>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int BH = p.B * p.H;
+  const int n_qt = (p.N + C::QT - 1) / C::QT;
+  const int bh = blk % BH;
+  const int qt = p.causal ? n_qt - 1 - blk / BH : blk / BH;  // causal: longest rows first
+  const int b = bh / p.H, h = bh % p.H;
+  const int N = p.N;
+  const int wq0 = qt * C::QT + wave * 32;
+  const int qi = wq0 + l32;  // this lane's query row
+  const bool qvalid = qi < N;
+
+  const __bf16* qp = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const __bf16* gp = static_cast<const __bf16*>(p.dout) + b * p.do_sb + h * p.do_sh;
+  const __bf16* kp = static_cast<const __bf16*>(p.k) + b * p.k_sb + h * p.k_sh;
+  const __bf16* vp = static_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh;
+
+  // Q^T and dO^T as B operands: lane holds its row, dims 16*kk + 8*g .. +7
+  bf16x8 qreg[D / 16], greg[DV / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    qreg[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_sn + kk * 16 + g * 8) : bf16x8{};
+#pragma unroll
+  for (int kk = 0; kk < DV / 16; ++kk)
+    greg[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(gp + (int64_t)qi * p.do_sn + kk * 16 + g * 8) : bf16x8{};
+  const int qc = min(qi, N - 1);
+  const float* grp = p.rowstat + ((int64_t)bh * p.n_grp + qc / 64) * 128;
+  const float lse2 = qvalid ? grp[qc % 64] : INFINITY;
+  const float drow = qvalid ? grp[64 + qc % 64] : 0.f;
+  const float* brow = nullptr;
+  if constexpr (BIAS) brow = p.bias + b * p.b_sb + h * p.b_sh + (int64_t)qc * p.b_si;
+
+  TileCopy2<D, C::KS> kcp;
+  TileCopy2<DV, C::KS> vcp;
+  kcp.init(p.k_sn, wave, lane);
+  vcp.init(p.v_sn, wave, lane);
+  TileReads<D> kr;
+  TileReads<DV> vr;
+  kr.init(lane);
+  vr.init(lane);
+
+  const int nt = (N + C::KS - 1) / C::KS;
+  const int t_end = p.causal ? min(nt, (qt * C::QT + C::QT - 1) / C::KS + 1) : nt;
+  const int tw_end = p.causal ? min(t_end, (wq0 + 31) / C::KS + 1) : t_end;  // this wave's last tile + 1
+  auto copy_step = [&](unsigned char* st, int t) {
+    kcp.copy(st, kp, p.k_sn, t * C::KS, N, wave);
+    vcp.copy(st + C::KTILE, vp, p.v_sn, t * C::KS, N, wave);
+  };
+
+  floatx16 dqacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dqacc[i] = floatx16{};
+  const float cs = BIAS ? kLog2e : p.scale_log2;
+
+  if (t_end > 0) copy_step(st0, 0);
+  for (int t = 0; t < t_end; ++t) {
+    unsigned char* cur = (t & 1) ? st1 : st0;
+    unsigned char* nxt = (t & 1) ? st0 : st1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // tile t has landed; every wave is done with tile t-1's stage
+    if (t + 1 < t_end) copy_step(nxt, t + 1);
+    if (t >= tw_end) continue;
+    const unsigned char* kt_ = cur;
+    const unsigned char* vt_ = cur + C::KTILE;
+    const int kv0 = t * C::KS;
+    float bv[BIAS ? 32 : 1];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          bv[kb * 16 + r] = brow[min(kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3), N - 1)];
+    }
+    floatx16 sacc[2], dpacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = floatx16{};
+      dpacc[kb] = floatx16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) sacc[kb] = mfma32(kr.row(kt_, kb, kk), qreg[kk], sacc[kb]);
+#pragma unroll
+      for (int kk = 0; kk < DV / 16; ++kk) dpacc[kb] = mfma32(vr.row(vt_, kb, kk), greg[kk], dpacc[kb]);
+    }
+    const bool edge = kv0 + C::KS > N || (p.causal && kv0 + C::KS - 1 > wq0);
+    bf16x8 dsk[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = BIAS ? fmaf(sacc[kb][r], p.scale, bv[kb * 16 + r]) * cs : sacc[kb][r] * cs;
+        float pr = __builtin_amdgcn_exp2f(x - lse2);
+        const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (edge && (key >= N || (p.causal && key > qi))) pr = 0.f;
+        dsk[kb * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (dpacc[kb][r] - drow));
+      }
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) dqacc[db] = mfma32(kr.tr(kt_, sg, db), dsk[sg], dqacc[db]);
+  }
+
+  if (!qvalid) return;
+  __bf16* dqp = static_cast<__bf16*>(p.grad_q) + b * p.dq_sb + h * p.dq_sh + (int64_t)qi * p.dq_sn;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      bf16x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(dqacc[db][r4 * 4 + e] * p.scale);
+      *reinterpret_cast<bf16x4*>(dqp + db * 32 + r4 * 8 + g * 4) = o4;
+    }
+}
+
+template <int D, int DV, bool BIAS>
+__global__ __launch_bounds__(256, 2) void bwd_mfma(BwdParams p) {
+  using C = BwdCfg<D, DV>;
+  __shared__ __attribute__((aligned(16))) unsigned char st0[C::STAGE], st1[C::STAGE];
+  if ((int)blockIdx.x < p.n_kv_blocks)
+    dkdv_block<D, DV, BIAS>(p, blockIdx.x, st0, st1);
+  else
+    dq_block<D, DV, BIAS>(p, blockIdx.x - p.n_kv_blocks, st0, st1);
+}
+
+template __global__ void bwd_mfma<64, 64, false>(BwdParams);
+template __global__ void bwd_mfma<64, 64, true>(BwdParams);
+template __global__ void bwd_mfma<64, 128, false>(BwdParams);
+template __global__ void bwd_mfma<64, 128, true>(BwdParams);
+template __global__ void bwd_mfma<128, 64, false>(BwdParams);
+template __global__ void bwd_mfma<128, 64, true>(BwdParams);
+template __global__ void bwd_mfma<128, 128, false>(BwdParams);
+template __global__ void bwd_mfma<128, 128, true>(BwdParams);
+template __global__ void bwd_rowstat<64>(BwdParams);
+template __global__ void bwd_rowstat<128>(BwdParams);
+
+template <int D, int DV>
+hipError_t launch_bwd_dd(const BwdParams& p, hipStream_t stream) {
+  const int rows = p.B * p.H * p.n_grp * 64;
+  hipLaunchKernelGGL((bwd_rowstat<DV>), dim3(rows / 16), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_qt = (p.N + kBwdQT - 1) / kBwdQT;
+  const int grid = p.n_kv_blocks + p.B * p.H * n_qt;
+  if (p.bias)
+    hipLaunchKernelGGL((bwd_mfma<D, DV, true>), dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_mfma<D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+  if (p.d == 128 && p.dv == 128) return launch_bwd_dd<128, 128>(p, stream);
+  if (p.d == 64 && p.dv == 128) return launch_bwd_dd<64, 128>(p, stream);
+  if (p.d == 128 && p.dv == 64) return launch_bwd_dd<128, 64>(p, stream);
+  if (p.d == 64 && p.dv == 64) return launch_bwd_dd<64, 64>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -54,21 +54,11 @@
 #include <type_traits>
 
 #include "fa_internal.h"
+#include "fa_mfma_common.h"
 
 namespace fa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format, no swizzle).
-constexpr int kBufferWord3 = 0x00020000;
 // Cache policy of a buffer store (sc0 | sc1): system scope, so the L2 writes the data
 // through instead of keeping it dirty. The split partial states are read by other
 // workgroups (merge blocks of the same kernel, on any XCD, or a following merge
@@ -76,8 +66,6 @@ constexpr int kBufferWord3 = 0x00020000;
 // L2 needs no write-back of them at the kernel's end.
 constexpr int kStoreWriteThrough = 1 | 16;
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy-reference slack, log2 units
 
 template <int D, int DV>
@@ -95,10 +83,6 @@ struct Cfg {
   static constexpr int KLD = KTILE / (NT * 16);  // direct loads per thread per K tile
   static constexpr int VLD = VTILE / (NT * 16);
 };
-
-__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // Tile copies: rows kv0 .. kv0+BN-1 of a [N, W] bf16 matrix with row stride `sn`
 // go into an LDS stage, 16 bytes per lane per instruction, chunk-swizzled. Lane
@@ -179,14 +163,6 @@ __device__ __forceinline__ Unit decode_unit(const Params& p, int u, int BM, int 
 }
 
 // ---- compile-time helpers of the interleaved tile body ----
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 // The softmax of one tile as a list of micro-steps, in dependency order:
 //   [0, NPRE)            bias only: x = s / sqrt(d) + bias, one element each
 //   MSK                  edge tiles only: causal / sequence-end element mask

@@ -68,9 +68,49 @@ constexpr int kFusedMergeItems = 2;
 // Query-tile height of the general (vector ALU) kernel.
 constexpr int kGenericBM = 64;
 
+// Everything the gradient kernels need, passed by value as the kernel argument.
+// Strides are in elements; the innermost axis of every tensor is contiguous.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;    // O of the forward
+  const void* dout;   // upstream gradient dO
+  const float* lse;   // natural-log log-sum-exp of the forward, [B, H, N]
+  const float* bias;  // nullptr: no bias
+  void* grad_q;
+  void* grad_k;
+  void* grad_v;
+  // Workspace: per (b, h) and group of 64 rows, 64 values of lse * log2(e) (+inf for
+  // rows past N or rows without an allowed key) then 64 values of D_i = dO_i . O_i.
+  float* rowstat;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t do_sb, do_sh, do_sn;
+  int64_t dq_sb, dq_sh, dq_sn;
+  int64_t dk_sb, dk_sh, dk_sn;
+  int64_t dv_sb, dv_sh, dv_sn;
+  int64_t b_sb, b_sh, b_si;
+  int64_t l_sb, l_sh;
+  int B, H, N, d, dv;
+  int n_grp;          // groups of 64 rows per (b, h) in rowstat: ceil(N / 128) * 2
+  int causal;
+  float scale_log2;   // log2(e) / sqrt(d)
+  float scale;        // 1 / sqrt(d)
+  int n_kv_blocks;    // blocks 0 .. n_kv_blocks-1 form dK, dV; the rest form dQ
+};
+
+// Key rows per dK/dV workgroup and query rows per dQ workgroup of the gradient kernel.
+constexpr int kBwdKT = 128;
+constexpr int kBwdQT = 128;
+
 // Launchers (each returns the hipError_t of the launch).
 // grid: forward units; merge: whether split query tiles need the merge kernel.
 hipError_t launch_mfma_bf16(const Params& p, int grid, bool merge, hipStream_t stream);
 hipError_t launch_generic(const Params& p, bool is_bf16, hipStream_t stream);
+// Gradients dQ, dK, dV (bf16): row statistics, then one grid of dK/dV and dQ blocks.
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -1,0 +1,41 @@
+// Device helpers shared by the gfx950 matrix-core kernels (forward and gradients).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// v_mfma_f32_32x32x16_bf16: C(32x32) += A(32x16) B(16x32). Lane l holds row (l mod 32)
+// of A and column (l mod 32) of B, k = 8*(l/32) .. +7 of each; accumulator register r
+// of lane l is C[8*(r/4) + 4*(l/32) + r%4][l mod 32].
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I = I0 .. N-1.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+}  // namespace fa

@@ -1,4 +1,4 @@
-"""Seeded synthetic workloads for the attention forward.
+"""Seeded synthetic workloads for the attention forward and its gradients.
 
 This module only draws inputs: it holds no part of the attention arithmetic, so the
 tests can hand the very same tensors to the HIP path and to the CPU oracle.
@@ -11,7 +11,9 @@ Recipe (the same for every workload):
     even, via torch) — the oracle receives the rounded values;
   * the sparse mask sets a bias entry to -inf with probability `mask_p`,
     independently per (h, i, j) with i != j; diagonal entries keep their value, so
-    every query row keeps at least one allowed key.
+    every query row keeps at least one allowed key;
+  * the upstream gradient dO of the gradient workloads is drawn separately
+    (seed + 500000), N(0, 1) in the same storage layout and dtype as V.
 
 The five workloads are the single fp32 head (N=256, d=64), the single bf16 causal head
 of length 8192 and width 128 that the traffic accounting on the page
@@ -26,7 +28,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "workload"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_grad_out", "workload"]
 
 
 @dataclass(frozen=True)
@@ -123,3 +125,14 @@ def make_inputs(w: Workload, device="cpu"):
             vals[kill] = -np.inf
         out["bias"] = torch.from_numpy(vals).to(device)
     return out
+
+
+def make_grad_out(w: Workload, device="cpu"):
+    """dO for the gradient workloads: logical [B, H, N, dv], same layout and dtype as V."""
+    import torch
+
+    rng = np.random.default_rng(w.seed + 500000)
+    shape = (w.B, w.H, w.N, w.dv) if w.layout == "bhnd" else (w.B, w.N, w.H, w.dv)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    t = torch.from_numpy(_draw(rng, shape, 1.0)).to(tdt).to(device)
+    return t if w.layout == "bhnd" else t.permute(0, 2, 1, 3)

@@ -62,8 +62,12 @@ def _probabilities(qbh, kbh, c_rows, rows, causal, scale, allow_empty_rows):
     return p
 
 
-def _row_block_grads(qbh, kbh, vbh, dobh, c_rows, rows, causal, scale, allow_empty_rows):
-    """dQ rows and the rows' contributions to dK, dV (all keys) for one (b, h)."""
+def _row_block_grads(qbh, kbh, vbh, dobh, c_rows, rows, causal, scale, allow_empty_rows,
+                     with_scales=False):
+    """dQ rows and the rows' contributions to dK, dV (all keys) for one (b, h).
+
+    with_scales: also the rows' contributions to the rounding-error scales (see
+    `_error_scales`), returned as a fourth item (sq rows, sk2 part, sv2 part)."""
     p = _probabilities(qbh, kbh, c_rows, rows, causal, scale, allow_empty_rows)
     do = dobh[rows]
     dv_part = p.T @ do                                # dV = P^T dO
@@ -71,7 +75,32 @@ def _row_block_grads(qbh, kbh, vbh, dobh, c_rows, rows, causal, scale, allow_emp
     ds = p * (dp - (p * dp).sum(axis=1)[:, None])     # softmax Jacobian, row by row
     dq = (ds @ kbh) * scale                           # dQ = dS K / sqrt(d)
     dk_part = (ds.T @ qbh[rows]) * scale              # dK = dS^T Q / sqrt(d)
-    return dq, dk_part, dv_part
+    if not with_scales:
+        return dq, dk_part, dv_part
+    return dq, dk_part, dv_part, _error_scales(p, ds, qbh[rows], kbh, vbh, do, scale)
+
+
+def _error_scales(p, ds, q_rows, kbh, vbh, do, scale, cols=None):
+    """Scales of the rounding errors of a bf16 gradient computation (tolerances only).
+
+    Not part of the result. A rounded operand adds to a sum an error proportional to
+    its term; independent roundings add in quadrature, so each gradient element gets
+    the root-sum-square of its terms, plus the term of D_i = dO_i . O_i, whose error
+    (O is given in bf16) is proportional to A_i = sum_k |dO_ik O_ik| and is shared by
+    every key of row i (so it enters dQ_i in full, and dK_j in quadrature over rows):
+        sv^2 = (P^2)^T (dO^2),
+        sk^2 = scale^2 (dS^2 + (P A)^2)^T (Q^2),
+        sq   = scale (sqrt((dS^2) (K^2)) + A |P K|).
+    Returns sq (rows), and the rows' contributions to sk^2 and sv^2 (of the key
+    columns `cols` only, when given)."""
+    o = p @ vbh
+    a = (np.abs(do) * np.abs(o)).sum(axis=1)
+    sq = scale * (np.sqrt((ds ** 2) @ kbh ** 2) + a[:, None] * np.abs(p @ kbh))
+    if cols is not None:
+        p, ds = p[:, cols], ds[:, cols]
+    sk2 = scale ** 2 * ((ds ** 2 + (p * a[:, None]) ** 2).T @ q_rows ** 2)
+    sv2 = (p ** 2).T @ do ** 2
+    return sq, sk2, sv2
 
 
 def _check_shapes(q, k, v, dout, bias):
@@ -86,12 +115,14 @@ def _check_shapes(q, k, v, dout, bias):
 
 
 def sdpa_backward_reference(q, k, v, dout, bias=None, causal=False, *, row_chunk=1024,
-                            allow_empty_rows=False):
+                            allow_empty_rows=False, with_scales=False):
     """dQ, dK, dV of every (batch, head) in float64.
 
     q: [B, H, N, d], k: [B, H, N, d], v and dout: [B, H, N, dv] (logical layout; any real
     dtype, torch or numpy). bias and causal as in `sdpa_reference`.
-    Returns (dQ [B,H,N,d], dK [B,H,N,d], dV [B,H,N,dv]) as float64 numpy arrays.
+    Returns (dQ [B,H,N,d], dK [B,H,N,d], dV [B,H,N,dv]) as float64 numpy arrays, and with
+    `with_scales` a fourth item: the rounding-error scales (sq, sk, sv) of the same
+    shapes, used only to size test tolerances (see `_error_scales`).
     """
     q, k, v, dout = (_as_f64(x) for x in (q, k, v, dout))
     bias = None if bias is None else _as_f64(bias)
@@ -100,22 +131,30 @@ def sdpa_backward_reference(q, k, v, dout, bias=None, causal=False, *, row_chunk
     dq = np.zeros((B, H, N, d))
     dk = np.zeros((B, H, N, d))
     dv = np.zeros((B, H, N, dvw))
+    if with_scales:
+        sq, sk2, sv2 = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
     for b in range(B):
         for h in range(H):
             cbh = _bias_slice(bias, b, h)
             for r0 in range(0, N, row_chunk):
                 rows = np.arange(r0, min(N, r0 + row_chunk))
                 c_rows = None if cbh is None else cbh[rows]
-                dq_, dk_, dv_ = _row_block_grads(q[b, h], k[b, h], v[b, h], dout[b, h], c_rows,
-                                                 rows, causal, scale, allow_empty_rows)
-                dq[b, h, rows] = dq_
-                dk[b, h] += dk_
-                dv[b, h] += dv_
+                res = _row_block_grads(q[b, h], k[b, h], v[b, h], dout[b, h], c_rows,
+                                       rows, causal, scale, allow_empty_rows, with_scales)
+                dq[b, h, rows] = res[0]
+                dk[b, h] += res[1]
+                dv[b, h] += res[2]
+                if with_scales:
+                    sq[b, h, rows] = res[3][0]
+                    sk2[b, h] += res[3][1]
+                    sv2[b, h] += res[3][2]
+    if with_scales:
+        return dq, dk, dv, (sq, np.sqrt(sk2), np.sqrt(sv2))
     return dq, dk, dv
 
 
 def sdpa_backward_reference_sampled(q, k, v, dout, bias, causal, b, h, rows, keys, *,
-                                    row_chunk=1024):
+                                    row_chunk=1024, with_scales=False):
     """dQ at query rows `rows` and dK, dV at key rows `keys` of one (batch, head).
 
     For sizes where the full gradients are too large for the CPU: dQ of a row needs only
@@ -133,9 +172,11 @@ def sdpa_backward_reference_sampled(q, k, v, dout, bias, causal, b, h, rows, key
     if bias is not None:
         sl = bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0]
     c_of = (lambda r: None) if sl is None else (lambda r: _as_f64(sl[r.tolist()]))
-    dq, _, _ = _row_block_grads(qbh, kbh, vbh, dobh, c_of(rows), rows, causal, scale, False)
+    res = _row_block_grads(qbh, kbh, vbh, dobh, c_of(rows), rows, causal, scale, False, with_scales)
+    dq = res[0]
     dk = np.zeros((len(keys), d))
     dv = np.zeros((len(keys), vbh.shape[1]))
+    sk2, sv2 = np.zeros_like(dk), np.zeros_like(dv)
     for r0 in range(0, N, row_chunk):
         rr = np.arange(r0, min(N, r0 + row_chunk))
         p = _probabilities(qbh, kbh, c_of(rr), rr, causal, scale, False)
@@ -143,4 +184,10 @@ def sdpa_backward_reference_sampled(q, k, v, dout, bias, causal, b, h, rows, key
         ds = p * (dp - (p * dp).sum(axis=1)[:, None])
         dv += p[:, keys].T @ dobh[rr]
         dk += (ds[:, keys].T @ qbh[rr]) * scale
+        if with_scales:
+            _, k2, v2 = _error_scales(p, ds, qbh[rr], kbh, vbh, dobh[rr], scale, cols=keys)
+            sk2 += k2
+            sv2 += v2
+    if with_scales:
+        return dq, dk, dv, (res[3][0], np.sqrt(sk2), np.sqrt(sv2))
     return dq, dk, dv

@@ -42,3 +42,29 @@ def check_lse(l_gpu, l_ref, where=""):
     worst = float(err.max()) if err.size else 0.0
     assert worst <= LSE_ATOL, f"max |dlse| = {worst:.3g} > {LSE_ATOL} {where}"
     return worst
+
+
+
+# Gradients (bf16 path). A gradient element is a long sum whose terms may cancel, so
+# its error is sized by the oracle's rounding-error scale S of that element (the
+# root-sum-square of the terms that bf16 roundings multiply, plus the shared error of
+# D_i = dO_i . O_i; see oracle/backward.py): |dG| <= 2^-6 * S + 1e-2 * |G_ref|.
+# 2^-6 is eight bf16 half-ulps (2^-9): independent roundings of P, dS, O and the
+# forward's own O error, at six standard deviations over up to 10^7 elements; the
+# relative term covers the final bf16 rounding of the gradient itself.
+GRAD_SCALE_TOL = 2.0 ** -6
+GRAD_RTOL = 1e-2
+
+
+def check_grad(g_gpu, g_ref, scale, where=""):
+    g = to_np(g_gpu) if not isinstance(g_gpu, np.ndarray) else g_gpu
+    assert np.isfinite(g).all(), f"non-finite gradient {where}"
+    if g_ref.size == 0:
+        return 0.0
+    err = np.abs(g - g_ref)
+    floor = 1e-6 * float(scale.max())
+    bound = GRAD_SCALE_TOL * scale + GRAD_RTOL * np.abs(g_ref) + floor
+    bad = err > bound
+    assert not bad.any(), (f"{int(bad.sum())} elements out of tolerance {where}; "
+                           f"worst |dG| / bound = {float((err / bound).max()):.3g}")
+    return float((err / bound).max())

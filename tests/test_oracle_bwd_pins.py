@@ -134,3 +134,19 @@ def test_sampled_and_chunked_match_full():
     np.testing.assert_allclose(dq, full[0][1, 0, rows], rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(dk, full[1][1, 0, keys], rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(dvv, full[2][1, 0, keys], rtol=1e-13, atol=1e-14)
+
+
+def test_error_scales_sampled_match_full_and_bound_terms():
+    # the tolerance scales: the sampled variant equals the full one, and each scale is
+    # at least the root-sum-square of the plain terms of its gradient
+    q, k, v, do, c = _case(18, B=1, H=2, N=40, d=8, dv=6, bias=True, causal=True)
+    dq, dk, dvv, (sq, sk, sv) = sdpa_backward_reference(q, k, v, do, c, True, with_scales=True)
+    rows, keys = [0, 7, 39], [0, 13, 39]
+    res = sdpa_backward_reference_sampled(q, k, v, do, c, True, 0, 1, rows, keys, row_chunk=11,
+                                          with_scales=True)
+    np.testing.assert_allclose(res[3][0], sq[0, 1, rows], rtol=1e-12)
+    np.testing.assert_allclose(res[3][1], sk[0, 1, keys], rtol=1e-12)
+    np.testing.assert_allclose(res[3][2], sv[0, 1, keys], rtol=1e-12)
+    assert (sq >= 0).all() and (sk >= 0).all() and (sv >= 0).all()
+    # |dV_j| <= sum_i P_ij |dO_i| <= sqrt(n) * sv_j (Cauchy-Schwarz), with n = 40 rows
+    assert (np.abs(dvv) <= math.sqrt(40) * sv + 1e-12).all()
