@@ -12,6 +12,7 @@ dominant kernel (its average launch duration measured with HIP events on the str
 it is launched on), and the CPU oracle timed on this host as a reported baseline.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+  python bench.py --pass bwd [...]  # the gradients (fa_bwd) of the same workload instead
   python bench.py --copy-probe      # plain copy kernel of known size (counter calibration)
 """
 
@@ -130,6 +131,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the gradients of the workload")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -159,6 +162,8 @@ def main() -> int:
             gpu[n] = t.to(dev)
     out = torch.empty(w.B, w.H, w.N, w.dv, dtype=gpu["q"].dtype, device=dev)
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    if args.which == "bwd":
+        return bench_bwd(args, w, inp, gpu, out, lse)
 
     # One validated call through the binding, then the same C entry point with its
     # arguments marshalled once, so the timed loop is the library call itself.
@@ -246,6 +251,117 @@ def main() -> int:
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+BWD_METRIC = "attention bwd (dQ, dK, dV) TFLOP/s; % of MI355X MFMA peak"
+BWD_SRC = os.path.join(ROOT, "exact_attention_35_amd", "csrc", "fa_bwd_mfma.hip")
+
+
+def cpu_baseline_bwd(w, inp, budget_s=10.0):
+    """Time the fp64 gradient oracle on this host for about `budget_s` seconds: the whole
+    workload when its dense score matrix is small, else head (0, 0) alone, repeated."""
+    from exact_attention_35_amd import roofline as rf
+    from oracle import sdpa_backward_reference
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        threads = None
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    whole = w.B * w.H == 1 or 2.0 * (3 * w.d + 2 * w.dv) * w.N * w.N * w.B * w.H <= 60e9
+    sl = (slice(None),) * 2 if whole else (slice(0, 1), slice(0, 1))
+    bias = inp["bias"]
+    if bias is not None and not whole:
+        bias = bias[:1, :1]
+    args = [inp[n][sl] for n in ("q", "k", "v", "do")]
+    calls, total = 0, 0.0
+    while total < budget_s and calls < 50:
+        t0 = time.perf_counter()
+        sdpa_backward_reference(*args, bias, w.causal)
+        total += time.perf_counter() - t0
+        calls += 1
+    bh = w.B * w.H if whole else 1
+    flops = rf.alg_flops_bwd(1, bh, w.N, w.d, w.dv, w.causal) * calls
+    what = f"whole workload ({w.name})" if whole else f"head (0, 0) of {w.name}"
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{what}, {calls} call{'s' if calls != 1 else ''}, fp64 numpy, {total:.1f} s",
+            "seconds": total}
+
+
+def bench_bwd(args, w, inp, gpu, out, lse) -> int:
+    """A step is one fa_bwd call (row statistics + gradient kernel) on the workload,
+    with O and lse from one fa_fwd call and a seeded dO, all resident in HBM."""
+    import torch
+
+    from exact_attention_35_amd import capi, roofline as rf, workloads
+
+    if w.dtype != "bf16":
+        print("the gradients are implemented for bf16 workloads only", file=sys.stderr)
+        return 2
+    dev = gpu["q"].device
+    inp["do"] = workloads.make_grad_out(w, device="cpu")
+    do = inp["do"]
+    if w.layout == "bnhd":
+        do = do.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+    else:
+        do = do.to(dev)
+    capi.fa_fwd(gpu["q"], gpu["k"], gpu["v"], bias=gpu["bias"], causal=w.causal, out=out, lse=lse)
+    dq = torch.empty_like(gpu["q"])
+    dk = torch.empty_like(gpu["k"])
+    dv = torch.empty_like(gpu["v"])
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        capi.fa_bwd(gpu["q"], gpu["k"], gpu["v"], out, lse, do, bias=gpu["bias"], causal=w.causal,
+                    grad_q=dq, grad_k=dk, grad_v=dv, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_call_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+
+    flops = rf.alg_flops_bwd(w.B, w.H, w.N, w.d, w.dv, w.causal)
+    peak = rf.MI355X_PEAK_BF16_FLOPS / 1e12
+    achieved = flops / avg_call_s / 1e12
+    bias_bytes = (w.H * w.N * w.N * 4) if w.bias else 0
+    res = {
+        "metric": BWD_METRIC,
+        "value": flops * args.steps / wall / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs and dO of the workload's shape)",
+        "config": {"workload": w.name, "pass": "bwd", "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv,
+                   "causal": w.causal, "bias": w.bias, "layout": w.layout, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "kernel": "bwd_rowstat + bwd_mfma (one fa_bwd call)",
+                     "avg_launch_us": avg_call_s * 1e6, "alg_flops_per_launch": flops,
+                     "min_bytes_per_launch": rf.min_bytes_bwd(w.B, w.H, w.N, w.d, w.dv, 2, bias_bytes),
+                     "kernel_source_sha256_16": hashlib.sha256(open(BWD_SRC, "rb").read()).hexdigest()[:16]},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_bwd(w, inp)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -27,6 +27,7 @@
 #include <mutex>
 #include <random>
 #include <utility>
+#include <vector>
 
 #include "fa.h"
 #include "fa_bwd.h"
@@ -479,8 +480,100 @@ int check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int 
   return FA_OK;
 }
 
-size_t bwd_ws_bytes(int64_t B, int64_t H, int64_t N) {
-  return round_up((size_t)(B * H) * (size_t)bwd_groups(N) * 128 * sizeof(float), 256);
+// Work plan of the gradients. Without a split, one dK/dV unit per (key tile, b*h) and
+// one dQ unit per (query tile, b*h). With few tiles (fewer dK/dV units than CUs), each
+// tile's loop (query steps of 64 rows for a key tile, key tiles of 64 for a query tile)
+// is cut into chunks of about equal length so that the grid has about 1.5 units per CU;
+// dK/dV steps cost about 4/3 of a dQ step (four products against three), so the
+// dK/dV kind gets 4/7 of the units.
+struct BwdPlan {
+  bool split = false;
+  int n_tiles = 0;
+  int units_kv = 0, units_q = 0;
+  std::vector<uint32_t> unit;  // dK/dV units, then dQ units
+  int16_t ubase_kv[fa::kMaxBwdTiles + 1] = {}, ubase_q[fa::kMaxBwdTiles + 1] = {};
+  uint8_t nch_kv[fa::kMaxBwdTiles] = {}, nch_q[fa::kMaxBwdTiles] = {};
+  size_t stat_bytes = 0, part_kv_floats = 0, part_q_floats = 0, ws_bytes = 0;
+};
+
+int64_t bwd_kv_steps(int64_t N, int kt, bool causal) { return (N - (causal ? (int64_t)kt * fa::kBwdKT : 0) + 63) / 64; }
+int64_t bwd_q_steps(int64_t N, int qt, bool causal) {
+  const int64_t nt = (N + 63) / 64;
+  return causal ? std::min<int64_t>(nt, ((int64_t)qt * fa::kBwdQT + fa::kBwdQT - 1) / 64 + 1) : nt;
+}
+
+BwdPlan make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, bool causal, int cus) {
+  BwdPlan pl;
+  const int64_t BH = B * H;
+  const int64_t nt = (N + fa::kBwdKT - 1) / fa::kBwdKT;
+  pl.n_tiles = (int)nt;
+  pl.stat_bytes = round_up((size_t)BH * (size_t)bwd_groups(N) * 128 * sizeof(float), 256);
+  const int env_units = env_int("FA_BWD_UNITS");
+  const int64_t target = std::min<int64_t>(fa::kMaxBwdUnits, env_units > 0 ? env_units : cus * 3 / 2);
+  pl.split = BH * nt < cus && BH <= 64 && nt <= fa::kMaxBwdTiles && nt > 0 && target >= 2 * BH * nt;
+  if (!pl.split) {
+    pl.units_kv = pl.units_q = (int)(BH * nt);
+    pl.ws_bytes = pl.stat_bytes;
+    return pl;
+  }
+  // chunk lengths: the dK/dV kind gets 4/7 of the target units, dQ the rest
+  std::vector<int64_t> skv(nt), sq(nt);
+  int64_t tot_kv = 0, tot_q = 0;
+  for (int t = 0; t < nt; ++t) {
+    skv[t] = bwd_kv_steps(N, t, causal);
+    sq[t] = bwd_q_steps(N, t, causal);
+    tot_kv += BH * skv[t];
+    tot_q += BH * sq[t];
+  }
+  int64_t len_kv = std::max<int64_t>(1, (tot_kv + target * 4 / 7 - 1) / (target * 4 / 7));
+  int64_t len_q = std::max<int64_t>(1, (tot_q + (target - target * 4 / 7) - 1) / (target - target * 4 / 7));
+  auto count = [&](const std::vector<int64_t>& st, int64_t len) {
+    int64_t u = 0;
+    for (int t = 0; t < nt; ++t) u += BH * std::min<int64_t>(fa::kMaxBwdChunks, (st[t] + len - 1) / len);
+    return u;
+  };
+  while (count(skv, len_kv) + count(sq, len_q) > fa::kMaxBwdUnits) {
+    ++len_kv;
+    ++len_q;
+  }
+  // units: key tiles from the first (longest under a causal mask), query tiles from the
+  // last; b*h, then chunks; chunk c of n covers steps [c*s/n, (c+1)*s/n)
+  auto emit = [&](const std::vector<int64_t>& st, int64_t len, bool rev, int16_t* ubase, uint8_t* nch) {
+    int u0 = (int)pl.unit.size(), k = 0;
+    for (int i = 0; i < nt; ++i) {
+      const int t = rev ? (int)nt - 1 - i : i;
+      const int n = (int)std::min<int64_t>(fa::kMaxBwdChunks, (st[t] + len - 1) / len);
+      nch[t] = (uint8_t)n;
+      ubase[t] = (int16_t)k;
+      for (int64_t bh = 0; bh < BH; ++bh)
+        for (int c = 0; c < n; ++c, ++k) {
+          const int64_t b0 = c * st[t] / n, b1 = (c + 1) * st[t] / n;
+          pl.unit.push_back((uint32_t)t | ((uint32_t)b0 << 8) | ((uint32_t)(b1 - b0) << 17) | ((uint32_t)bh << 26));
+        }
+    }
+    return (int)pl.unit.size() - u0;
+  };
+  pl.units_kv = emit(skv, len_kv, false, pl.ubase_kv, pl.nch_kv);
+  pl.units_q = emit(sq, len_q, causal, pl.ubase_q, pl.nch_q);
+  pl.part_kv_floats = (size_t)pl.units_kv * fa::kBwdKT * (size_t)(d + dv);
+  pl.part_q_floats = (size_t)pl.units_q * fa::kBwdQT * (size_t)d;
+  pl.ws_bytes = pl.stat_bytes + round_up((pl.part_kv_floats + pl.part_q_floats) * sizeof(float), 256);
+  return pl;
+}
+
+std::mutex g_bwd_plan_mu;
+std::map<std::array<int64_t, 7>, std::shared_ptr<const BwdPlan>> g_bwd_plans;
+
+std::shared_ptr<const BwdPlan> cached_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, bool causal,
+                                               int cus) {
+  const std::array<int64_t, 7> key{B, H, N, d, dv, causal ? 1 : 0, cus};
+  std::lock_guard<std::mutex> lk(g_bwd_plan_mu);
+  auto it = g_bwd_plans.find(key);
+  if (it != g_bwd_plans.end()) return it->second;
+  if (g_bwd_plans.size() > 256) g_bwd_plans.clear();
+  auto pl = std::make_shared<const BwdPlan>(make_bwd_plan(B, H, N, d, dv, causal, cus));
+  g_bwd_plans[key] = pl;
+  return pl;
 }
 
 int validate_bwd(const BwdProblem& P) {
@@ -535,7 +628,7 @@ BwdProblem make_bwd_problem(const void* q, const void* k, const void* v, const v
   return P;
 }
 
-int run_bwd(const BwdProblem& P, void* ws, hipStream_t stream) {
+int run_bwd(const BwdProblem& P, const BwdPlan& pl, void* ws, hipStream_t stream) {
   fa::BwdParams p;
   std::memset(&p, 0, sizeof(p));
   const fa_bwd_strides& s = P.st;
@@ -557,12 +650,24 @@ int run_bwd(const BwdProblem& P, void* ws, hipStream_t stream) {
   p.causal = P.mask == FA_MASK_CAUSAL;
   p.scale = (float)(1.0 / std::sqrt((double)P.d));
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.d));
-  p.n_kv_blocks = (int)(P.B * P.H * ((P.N + fa::kBwdKT - 1) / fa::kBwdKT));
-  const hipError_t e = fa::launch_bwd_bf16(p, stream);
+  p.sqrt_d = (float)std::sqrt((double)P.d);
+  p.n_kv_blocks = pl.units_kv;
+  p.split = pl.split ? 1 : 0;
+  p.n_tiles = pl.n_tiles;
+  if (pl.split) {
+    p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.stat_bytes);
+    p.part_q_off = (int64_t)pl.part_kv_floats;
+    std::copy(pl.unit.begin(), pl.unit.end(), p.unit);
+    std::copy(pl.ubase_kv, pl.ubase_kv + fa::kMaxBwdTiles + 1, p.ubase_kv);
+    std::copy(pl.ubase_q, pl.ubase_q + fa::kMaxBwdTiles + 1, p.ubase_q);
+    std::copy(pl.nch_kv, pl.nch_kv + fa::kMaxBwdTiles, p.nch_kv);
+    std::copy(pl.nch_q, pl.nch_q + fa::kMaxBwdTiles, p.nch_q);
+  }
+  const hipError_t e = fa::launch_bwd_bf16(p, pl.units_kv + pl.units_q, stream);
   if (env_int("FA_LOG"))
-    std::fprintf(stderr, "[fa] bwd B=%lld H=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d kv_blocks=%d ws=%zu\n",
+    std::fprintf(stderr, "[fa] bwd B=%lld H=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d split=%d units=%d+%d ws=%zu\n",
                  (long long)P.B, (long long)P.H, (long long)P.N, (long long)P.d, (long long)P.dvw, p.causal,
-                 P.bias != nullptr, p.n_kv_blocks, bwd_ws_bytes(P.B, P.H, P.N));
+                 P.bias != nullptr, p.split, pl.units_kv, pl.units_q, pl.ws_bytes);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -678,8 +783,9 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* out, cons
   int dev = 0;
   DevInfo di;
   if ((st = device_info(&dev, &di)) != FA_OK) return st;
-  if (!workspace || workspace_bytes < bwd_ws_bytes(B, H, N) || !aligned(workspace, 256)) return FA_ERR_WORKSPACE;
-  return run_bwd(P, workspace, static_cast<hipStream_t>(stream));
+  const std::shared_ptr<const BwdPlan> plan = cached_bwd_plan(B, H, N, d, dv, mask_mode == FA_MASK_CAUSAL, di.cus);
+  if (!workspace || workspace_bytes < plan->ws_bytes || !aligned(workspace, 256)) return FA_ERR_WORKSPACE;
+  return run_bwd(P, *plan, workspace, static_cast<hipStream_t>(stream));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -694,17 +800,21 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
   int dev = 0;
   DevInfo di;
   if ((st = device_info(&dev, &di)) != FA_OK) return st;
+  const std::shared_ptr<const BwdPlan> plan = cached_bwd_plan(B, H, N, d, dv, mask_mode == FA_MASK_CAUSAL, di.cus);
   void* ws = nullptr;
-  st = owned_workspace(dev, static_cast<hipStream_t>(stream), bwd_ws_bytes(B, H, N), &ws);
+  st = owned_workspace(dev, static_cast<hipStream_t>(stream), plan->ws_bytes, &ws);
   if (st != FA_OK) return st;
-  return run_bwd(P, ws, static_cast<hipStream_t>(stream));
+  return run_bwd(P, *plan, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype,
                              int mask_mode) {
   if (check_bwd_shape(B, H, N, d, dv, dtype, mask_mode) != FA_OK) return 0;
   if (B * H * N == 0) return 0;
-  return bwd_ws_bytes(B, H, N);
+  int dev = 0;
+  DevInfo di;
+  if (device_info(&dev, &di) != FA_OK) return 0;
+  return cached_bwd_plan(B, H, N, d, dv, mask_mode == FA_MASK_CAUSAL, di.cus)->ws_bytes;
 }
 
 void fa_shutdown(void) {

@@ -12,9 +12,12 @@
 // nor the probabilities ever reach memory. C gets no gradient.
 //
 // Mapping onto CDNA4 (this file's own design):
-//  * A row-statistics kernel forms D_i = dO_i . O_i and lse_i * log2(e) for every row
-//    and stores them in groups of 64 rows (the lse of rows past N, or of rows with no
-//    allowed key, is stored as +inf so that their probabilities are exactly 0).
+//  * A row-statistics kernel forms -lse_i * sqrt(d) and -D_i (D_i = dO_i . O_i) for
+//    every row and stores them in groups of 64 rows (-inf for rows past N or rows with
+//    no allowed key, so that their probabilities are exactly 0). They are the start
+//    values of the score and dP accumulators: the matrix cores then deliver
+//    sqrt(d) (S - lse) and dP - D, and P, dS cost one exponential and two multiplies.
+//    (S here includes C: S - lse = Q K^T / sqrt(d) + C - lse.)
 //  * One grid holds two kinds of workgroups (4 waves each). dK/dV blocks own 128 keys
 //    (32 per wave) and stream the query rows in steps of 64; dQ blocks own 128 query
 //    rows (32 per wave) and stream the keys in steps of 64. Every sum is formed inside
@@ -28,11 +31,16 @@
 //  * dQ blocks mirror the forward: S^T = K Q^T and dP^T = V dO^T with the wave's Q and
 //    dO rows held as B operands (one query per lane, so lse and D are per-lane
 //    scalars), then dQ^T += K^T dS^T with K^T read transposed from the K tile.
+//  * A bias enters the same start value (sqrt(d) C_ij is added to -lse_i sqrt(d)), so
+//    the base-2 exponent of P is always the accumulator times log2(e)/sqrt(d).
 //  * Tiles go from global memory straight into LDS (buffer loads with the LDS
 //    destination), two stages, one barrier per step. Q, dO (dK/dV blocks) and K (dQ
 //    blocks) are read both row-wise and transposed, so their rows use one XOR swizzle
 //    of the 16-byte chunks that keeps both reads free of bank conflicts: key(row) =
 //    s(row mod 4) ^ ((row / 4) mod 4), s = (0, 10, 4, 14).
+//  * Few tiles (fewer dK/dV blocks than CUs): each tile's loop is cut into chunks of
+//    about equal length, one workgroup each; chunks write fp32 partial sums and a
+//    reduction kernel adds them in chunk order (deterministic) into the gradients.
 //  * Causal: a dK/dV block starts at the query step of its first key; a dQ block ends
 //    at the key tile of its last row; waves skip blocks that lie entirely in the
 //    masked triangle, and element masks use the same comparison as the forward.
@@ -96,40 +104,43 @@ struct TileCopy2 {
   }
 };
 
-// Operand reads from a dual-swizzled LDS tile of W bf16 per row.
+// Operand reads from a dual-swizzled LDS tile of W bf16 per row. A read's byte offset
+// within the tile is a per-lane base XOR a compile-time constant (the swizzled chunk
+// index is an XOR, and the fields it touches are disjoint from the row's), so one
+// register per kind of read serves every k-step and column block.
 template <int W>
 struct TileReads {
   static constexpr int CH = W / 8;
-  int roff[W / 16];     // row-wise read: row l32 (+32*blk), logical chunk 2*kk + g
-  int toff[2][W / 32];  // transposing read: half hh, 32-column block db
+  int rbase;     // row-wise read: row l32 (+32*blk), logical chunk 2*kk + g -> rbase ^ 32*kk
+  int tbase[2];  // transposing read, half hh: column block db -> tbase[hh] ^ 64*db
   __device__ __forceinline__ void init(int lane) {
     const int g = lane >> 5, l32 = lane & 31;
-#pragma unroll
-    for (int kk = 0; kk < W / 16; ++kk) roff[kk] = l32 * (W * 2) + (((2 * kk + g) ^ (dual_key(l32) & (CH - 1))) * 16);
+    // (2kk + g) ^ key = 2kk ^ (g ^ key): offset (l32*W*2 | 16 (g ^ key)) ^ 32 kk
+    rbase = (l32 * (W * 2)) | (((g ^ dual_key(l32)) & (CH - 1)) * 16);
     // Transposing read (A operand with k = 16 rows of group sg): within a 16-lane group
     // G, lane L reads row 16*sg + 8*hh + 4*g + L/4 at columns c0 .. c0+3,
-    // c0 = 32*db + 16*(G&1) + 4*(L&3); the swizzle key of that row does not depend on sg.
+    // c0 = 32*db + c1, c1 = 16*(G&1) + 4*(L&3); the row's swizzle key does not depend
+    // on sg, and (4*db + c1/8) ^ key = 4*db ^ (c1/8 ^ key).
     const int G = lane >> 4, L = lane & 15;
+    const int c1 = 16 * (G & 1) + 4 * (L & 3);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int row = 8 * hh + 4 * g + (L >> 2);
       const int key = dual_key(row) & (CH - 1);
-#pragma unroll
-      for (int db = 0; db < W / 32; ++db) {
-        const int col = 32 * db + 16 * (G & 1) + 4 * (L & 3);
-        toff[hh][db] = row * (W * 2) + (((col >> 3) ^ key) * 16) + (col & 7) * 2;
-      }
+      tbase[hh] = (row * (W * 2)) | ((((c1 >> 3) ^ key) & (CH - 1)) * 16) | ((c1 & 7) * 2);
     }
   }
   // A or B operand: row 32*blk + (lane mod 32), k = 16*kk + 8*g .. +7
   __device__ __forceinline__ bf16x8 row(const unsigned char* t, int blk, int kk) const {
-    return *reinterpret_cast<const bf16x8*>(t + blk * 32 * (W * 2) + roff[kk]);
+    return *reinterpret_cast<const bf16x8*>(t + blk * 32 * (W * 2) + (rbase ^ (32 * kk)));
   }
   // A operand of a product over the tile's rows: column 32*db + (lane mod 32), with k
   // running over the 16 rows of group sg in the order the accumulator layout holds them.
   __device__ __forceinline__ bf16x8 tr(const unsigned char* t, int sg, int db) const {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, t + 16 * sg * (W * 2) + toff[0][db]));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, t + 16 * sg * (W * 2) + toff[1][db]));
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        LDS_PTR(i16x4, t + 16 * sg * (W * 2) + (tbase[0] ^ (64 * db))));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        LDS_PTR(i16x4, t + 16 * sg * (W * 2) + (tbase[1] ^ (64 * db))));
     bf16x8 a;
     a.lo = __builtin_bit_cast(bf16x4, lo);
     a.hi = __builtin_bit_cast(bf16x4, hi);
@@ -159,15 +170,60 @@ __global__ __launch_bounds__(256) void bwd_rowstat(BwdParams p) {
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
   if (part == 0) {
-    float l2 = INFINITY;
+    // -lse * sqrt(d): the start value of a score accumulator, so that it ends holding
+    // sqrt(d) * (S_ij - lse_i) without C; -inf where no probability may arise
+    float m = -INFINITY;
     if (i < p.N) {
       const float l = p.lse[b * p.l_sb + h * p.l_sh + i];
-      l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+      m = l == -INFINITY ? -INFINITY : -l * p.sqrt_d;
     }
     float* grp = p.rowstat + ((int64_t)bh * p.n_grp + i / 64) * 128;
-    grp[i % 64] = l2;
-    grp[64 + i % 64] = i < p.N ? acc : 0.f;
+    grp[i % 64] = m;
+    grp[64 + i % 64] = i < p.N ? -acc : 0.f;  // -D: the start value of a dP accumulator
   }
+}
+
+// One unit of the gradient grid: tile `tile` of b*h `bh`, steps [s_begin, s_end) of its
+// loop; `partial`: the tile is cut into several chunks, so the unit writes fp32
+// partial sums into its slot instead of the bf16 gradient.
+struct BwdUnit {
+  int bh, tile, s_begin, s_end, slot;
+  bool partial;
+};
+
+// query steps (of QS = 64 rows) of key tile kt, from the first one its keys can see
+__device__ __forceinline__ int kv_steps(const BwdParams& p, int kt) {
+  const int qs0 = p.causal ? kt * kBwdKT : 0;
+  return (p.N - qs0 + 63) / 64;
+}
+// key tiles (of 64 keys) of query tile qt
+__device__ __forceinline__ int q_steps(const BwdParams& p, int qt) {
+  const int nt = (p.N + 63) / 64;
+  return p.causal ? min(nt, (qt * kBwdQT + kBwdQT - 1) / 64 + 1) : nt;
+}
+
+// Unit u of a kind (dK/dV or dQ units, numbered from 0 within the kind). Without a split
+// the units are (tile, b*h) pairs, longest tiles first; with one they come from the table.
+__device__ __forceinline__ BwdUnit bwd_unit(const BwdParams& p, int u, bool kv) {
+  const int BH = p.B * p.H;
+  BwdUnit w;
+  w.slot = u;
+  if (!p.split) {
+    w.bh = u % BH;
+    const int r = u / BH;
+    w.tile = kv || !p.causal ? r : p.n_tiles - 1 - r;
+    w.s_begin = 0;
+    w.s_end = kv ? kv_steps(p, w.tile) : q_steps(p, w.tile);
+    w.partial = false;
+    return w;
+  }
+  const unsigned info = p.unit[(kv ? u : p.n_kv_blocks + u) % kMaxBwdUnits];
+  w.tile = (int)(info & 0xff);
+  w.s_begin = (int)((info >> 8) & 0x1ff);
+  w.s_end = w.s_begin + (int)((info >> 17) & 0x1ff);
+  w.bh = (int)(info >> 26);
+  w.partial = (kv ? p.nch_kv[w.tile] : p.nch_q[w.tile]) > 1;
+  return w;
 }
 
 // ---- dK, dV of 128 keys of one (b, h) ----
@@ -176,8 +232,8 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
   using C = BwdCfg<D, DV>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int BH = p.B * p.H;
-  const int bh = blk % BH, kt = blk / BH;
+  const BwdUnit U = bwd_unit(p, blk, true);
+  const int bh = U.bh, kt = U.tile;
   const int b = bh / p.H, h = bh % p.H;
   const int N = p.N;
   const int k0 = kt * C::KT;
@@ -212,9 +268,10 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
   qr.init(lane);
   gr.init(lane);
 
-  // query steps: causal blocks start at the step that holds their first key
-  const int qs0 = p.causal ? (k0 / C::QS) * C::QS : 0;
-  const int nsteps = (N - qs0 + C::QS - 1) / C::QS;
+  // query steps: causal blocks start at the step that holds their first key; this
+  // unit runs steps U.s_begin .. U.s_end - 1 of them
+  const int qs0 = (p.causal ? (k0 / C::QS) * C::QS : 0) + U.s_begin * C::QS;
+  const int nsteps = U.s_end - U.s_begin;
   auto copy_step = [&](unsigned char* st, int qs) {
     qcp.copy(st, qp, p.q_sn, qs, N, wave);
     gcp.copy(st + C::QTILE, gp, p.do_sn, qs, N, wave);
@@ -231,7 +288,6 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
 #pragma unroll
   for (int i = 0; i < DV / 32; ++i) dvacc[i] = floatx16{};
 
-  const float cs = BIAS ? kLog2e : p.scale_log2;
   if (nsteps > 0) copy_step(st0, qs0);
   for (int s = 0; s < nsteps; ++s) {
     unsigned char* cur = (s & 1) ? st1 : st0;
@@ -248,36 +304,39 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
       const int qb0 = qs + qb * 32;
       if (p.causal && qb0 + 31 < wk0) continue;  // every (row, key) of the block is masked
       if (qb0 >= N) continue;
-      float bv[BIAS ? 16 : 1];
+      // The accumulators start from the rows' statistics (register r holds row
+      // qb0 + 8*(r/4) + 4*g + r%4): S from sqrt(d) (C - lse), dP from -D.
+      floatx16 sacc, dpacc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const floatx4 m4 = *reinterpret_cast<const floatx4*>(vec + qb * 32 + 8 * j + 4 * g);
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(vec + 64 + qb * 32 + 8 * j + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sacc[4 * j + e] = m4[e];
+          dpacc[4 * j + e] = d4[e];
+        }
+      }
       if constexpr (BIAS) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int q = qb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          bv[r] = bcol[(int64_t)min(q, N - 1) * p.b_si];
+          sacc[r] = fmaf(bcol[(int64_t)min(q, N - 1) * p.b_si], p.sqrt_d, sacc[r]);
         }
       }
-      floatx16 sacc{}, dpacc{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(qr.row(qt_, qb, kk), kreg[kk], sacc);
 #pragma unroll
       for (int kk = 0; kk < DV / 16; ++kk) dpacc = mfma32(gr.row(gt_, qb, kk), vreg[kk], dpacc);
-      // rows of register r: qb0 + 8*(r/4) + 4*g + r%4
-      floatx4 l4[4], d4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        l4[j] = *reinterpret_cast<const floatx4*>(vec + qb * 32 + 8 * j + 4 * g);
-        d4[j] = *reinterpret_cast<const floatx4*>(vec + 64 + qb * 32 + 8 * j + 4 * g);
-      }
       const bool edge = p.causal && qb0 < wk0 + 31;
       bf16x8 pk[2], dsk[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float x = BIAS ? fmaf(sacc[r], p.scale, bv[r]) * cs : sacc[r] * cs;
-        float pr = __builtin_amdgcn_exp2f(x - l4[r >> 2][r & 3]);
+        // base-2 exponent of P: sqrt(d) (S - lse) * log2(e) / sqrt(d)
+        float pr = __builtin_amdgcn_exp2f(sacc[r] * p.scale_log2);
         if (edge && key > qb0 + 8 * (r >> 2) + 4 * g + (r & 3)) pr = 0.f;
-        const float ds = pr * (dpacc[r] - d4[r >> 2][r & 3]);
         pk[r >> 3][r & 7] = (__bf16)pr;
-        dsk[r >> 3][r & 7] = (__bf16)ds;
+        dsk[r >> 3][r & 7] = (__bf16)(pr * dpacc[r]);
       }
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
@@ -291,6 +350,22 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
 
   if (!kvalid) return;
   // accumulator register r of block db holds column key, dim 32*db + 8*(r/4) + 4*g + r%4
+  if (U.partial) {  // raw sums into the unit's slot: [128 keys][d + dv] fp32
+    float* pp = p.part + ((int64_t)U.slot * C::KT + (key - k0)) * (D + DV);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<floatx4*>(pp + db * 32 + r4 * 8 + g * 4) =
+            floatx4{dkacc[db][r4 * 4], dkacc[db][r4 * 4 + 1], dkacc[db][r4 * 4 + 2], dkacc[db][r4 * 4 + 3]};
+#pragma unroll
+    for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<floatx4*>(pp + D + db * 32 + r4 * 8 + g * 4) =
+            floatx4{dvacc[db][r4 * 4], dvacc[db][r4 * 4 + 1], dvacc[db][r4 * 4 + 2], dvacc[db][r4 * 4 + 3]};
+    return;
+  }
   __bf16* dkp = static_cast<__bf16*>(p.grad_k) + b * p.dk_sb + h * p.dk_sh + (int64_t)key * p.dk_sn;
   __bf16* dvp = static_cast<__bf16*>(p.grad_v) + b * p.dv_sb + h * p.dv_sh + (int64_t)key * p.dv_sn;
 #pragma unroll
@@ -319,10 +394,8 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
   using C = BwdCfg<D, DV>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int BH = p.B * p.H;
-  const int n_qt = (p.N + C::QT - 1) / C::QT;
-  const int bh = blk % BH;
-  const int qt = p.causal ? n_qt - 1 - blk / BH : blk / BH;  // causal: longest rows first
+  const BwdUnit U = bwd_unit(p, blk, false);
+  const int bh = U.bh, qt = U.tile;
   const int b = bh / p.H, h = bh % p.H;
   const int N = p.N;
   const int wq0 = qt * C::QT + wave * 32;
@@ -344,8 +417,8 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
     greg[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(gp + (int64_t)qi * p.do_sn + kk * 16 + g * 8) : bf16x8{};
   const int qc = min(qi, N - 1);
   const float* grp = p.rowstat + ((int64_t)bh * p.n_grp + qc / 64) * 128;
-  const float lse2 = qvalid ? grp[qc % 64] : INFINITY;
-  const float drow = qvalid ? grp[64 + qc % 64] : 0.f;
+  const float mrow = qvalid ? grp[qc % 64] : -INFINITY;  // -lse*sqrt(d)
+  const float ndrow = qvalid ? grp[64 + qc % 64] : 0.f;    // -D
   const float* brow = nullptr;
   if constexpr (BIAS) brow = p.bias + b * p.b_sb + h * p.b_sh + (int64_t)qc * p.b_si;
 
@@ -358,9 +431,9 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
   kr.init(lane);
   vr.init(lane);
 
-  const int nt = (N + C::KS - 1) / C::KS;
-  const int t_end = p.causal ? min(nt, (qt * C::QT + C::QT - 1) / C::KS + 1) : nt;
-  const int tw_end = p.causal ? min(t_end, (wq0 + 31) / C::KS + 1) : t_end;  // this wave's last tile + 1
+  // key tiles U.s_begin .. U.s_end - 1; a wave skips those above its own rows
+  const int t_begin = U.s_begin, t_end = U.s_end;
+  const int tw_end = p.causal ? min(t_end, (wq0 + 31) / C::KS + 1) : t_end;
   auto copy_step = [&](unsigned char* st, int t) {
     kcp.copy(st, kp, p.k_sn, t * C::KS, N, wave);
     vcp.copy(st + C::KTILE, vp, p.v_sn, t * C::KS, N, wave);
@@ -369,12 +442,11 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
   floatx16 dqacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dqacc[i] = floatx16{};
-  const float cs = BIAS ? kLog2e : p.scale_log2;
 
-  if (t_end > 0) copy_step(st0, 0);
-  for (int t = 0; t < t_end; ++t) {
-    unsigned char* cur = (t & 1) ? st1 : st0;
-    unsigned char* nxt = (t & 1) ? st0 : st1;
+  if (t_begin < t_end) copy_step(st0, t_begin);
+  for (int t = t_begin; t < t_end; ++t) {
+    unsigned char* cur = ((t - t_begin) & 1) ? st1 : st0;
+    unsigned char* nxt = ((t - t_begin) & 1) ? st0 : st1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // tile t has landed; every wave is done with tile t-1's stage
     if (t + 1 < t_end) copy_step(nxt, t + 1);
@@ -382,19 +454,17 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
     const unsigned char* kt_ = cur;
     const unsigned char* vt_ = cur + C::KTILE;
     const int kv0 = t * C::KS;
-    float bv[BIAS ? 32 : 1];
-    if constexpr (BIAS) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          bv[kb * 16 + r] = brow[min(kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3), N - 1)];
-    }
+    // accumulators start from sqrt(d) (C - lse) and -D (see dkdv_block)
     floatx16 sacc[2], dpacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = floatx16{};
-      dpacc[kb] = floatx16{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[kb][r] = mrow;
+        if constexpr (BIAS)
+          sacc[kb][r] = fmaf(brow[min(kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3), N - 1)], p.sqrt_d, mrow);
+        dpacc[kb][r] = ndrow;
+      }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) sacc[kb] = mfma32(kr.row(kt_, kb, kk), qreg[kk], sacc[kb]);
 #pragma unroll
@@ -406,11 +476,10 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float x = BIAS ? fmaf(sacc[kb][r], p.scale, bv[kb * 16 + r]) * cs : sacc[kb][r] * cs;
-        float pr = __builtin_amdgcn_exp2f(x - lse2);
+        float pr = __builtin_amdgcn_exp2f(sacc[kb][r] * p.scale_log2);
         const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
         if (edge && (key >= N || (p.causal && key > qi))) pr = 0.f;
-        dsk[kb * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (dpacc[kb][r] - drow));
+        dsk[kb * 2 + (r >> 3)][r & 7] = (__bf16)(pr * dpacc[kb][r]);
       }
 #pragma unroll
     for (int sg = 0; sg < 4; ++sg)
@@ -419,6 +488,16 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
   }
 
   if (!qvalid) return;
+  if (U.partial) {  // raw sums into the unit's slot: [128 rows][d] fp32
+    float* pp = p.part + p.part_q_off + ((int64_t)U.slot * C::QT + (qi - qt * C::QT)) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<floatx4*>(pp + db * 32 + r4 * 8 + g * 4) =
+            floatx4{dqacc[db][r4 * 4], dqacc[db][r4 * 4 + 1], dqacc[db][r4 * 4 + 2], dqacc[db][r4 * 4 + 3]};
+    return;
+  }
   __bf16* dqp = static_cast<__bf16*>(p.grad_q) + b * p.dq_sb + h * p.dq_sh + (int64_t)qi * p.dq_sn;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -441,6 +520,44 @@ __global__ __launch_bounds__(256, 2) void bwd_mfma(BwdParams p) {
     dq_block<D, DV, BIAS>(p, blockIdx.x - p.n_kv_blocks, st0, st1);
 }
 
+// Sum of the chunk partials of split tiles, in chunk order, into the bf16 gradients.
+// Block (row group of 32, b*h, tile): tile < n_tiles is a key tile (dK, dV), else a
+// query tile (dQ). Tiles with a single chunk were written by their unit.
+template <int D, int DV>
+__global__ __launch_bounds__(256) void bwd_reduce(BwdParams p) {
+  const int bh = blockIdx.y;
+  const bool kv = (int)blockIdx.z < p.n_tiles;
+  const int tile = kv ? blockIdx.z : blockIdx.z - p.n_tiles;
+  const int nch = kv ? p.nch_kv[tile] : p.nch_q[tile];
+  if (nch <= 1) return;
+  const int b = bh / p.H, h = bh % p.H;
+  const int W = kv ? D + DV : D;  // floats per row of a slot
+  const int slot0 = (kv ? p.ubase_kv[tile] : p.ubase_q[tile]) + bh * nch;
+  const float* base = p.part + (kv ? 0 : p.part_q_off) + (int64_t)slot0 * 128 * W;
+  const int n4 = 32 * W / 4;  // float4 items of the block's 32 rows
+  for (int it = threadIdx.x; it < n4; it += 256) {
+    const int r = blockIdx.x * 32 + it / (W / 4);  // row within the tile
+    const int c = (it % (W / 4)) * 4;              // column within the slot row
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < nch; ++j) acc += *reinterpret_cast<const floatx4*>(base + ((int64_t)j * 128 + r) * W + c);
+    const int n = tile * 128 + r;
+    if (n >= p.N) continue;
+    bf16x4 o4;
+    __bf16* dst;
+    if (kv && c >= D) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
+      dst = static_cast<__bf16*>(p.grad_v) + b * p.dv_sb + h * p.dv_sh + (int64_t)n * p.dv_sn + (c - D);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * p.scale);
+      dst = kv ? static_cast<__bf16*>(p.grad_k) + b * p.dk_sb + h * p.dk_sh + (int64_t)n * p.dk_sn + c
+               : static_cast<__bf16*>(p.grad_q) + b * p.dq_sb + h * p.dq_sh + (int64_t)n * p.dq_sn + c;
+    }
+    *reinterpret_cast<bf16x4*>(dst) = o4;
+  }
+}
+
 template __global__ void bwd_mfma<64, 64, false>(BwdParams);
 template __global__ void bwd_mfma<64, 64, true>(BwdParams);
 template __global__ void bwd_mfma<64, 128, false>(BwdParams);
@@ -451,29 +568,34 @@ template __global__ void bwd_mfma<128, 128, false>(BwdParams);
 template __global__ void bwd_mfma<128, 128, true>(BwdParams);
 template __global__ void bwd_rowstat<64>(BwdParams);
 template __global__ void bwd_rowstat<128>(BwdParams);
+template __global__ void bwd_reduce<64, 64>(BwdParams);
+template __global__ void bwd_reduce<64, 128>(BwdParams);
+template __global__ void bwd_reduce<128, 64>(BwdParams);
+template __global__ void bwd_reduce<128, 128>(BwdParams);
 
 template <int D, int DV>
-hipError_t launch_bwd_dd(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd_dd(const BwdParams& p, int grid, hipStream_t stream) {
   const int rows = p.B * p.H * p.n_grp * 64;
   hipLaunchKernelGGL((bwd_rowstat<DV>), dim3(rows / 16), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_qt = (p.N + kBwdQT - 1) / kBwdQT;
-  const int grid = p.n_kv_blocks + p.B * p.H * n_qt;
   if (p.bias)
     hipLaunchKernelGGL((bwd_mfma<D, DV, true>), dim3(grid), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((bwd_mfma<D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || !p.split) return e;
+  hipLaunchKernelGGL((bwd_reduce<D, DV>), dim3(4, p.B * p.H, 2 * p.n_tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
-  if (p.d == 128 && p.dv == 128) return launch_bwd_dd<128, 128>(p, stream);
-  if (p.d == 64 && p.dv == 128) return launch_bwd_dd<64, 128>(p, stream);
-  if (p.d == 128 && p.dv == 64) return launch_bwd_dd<128, 64>(p, stream);
-  if (p.d == 64 && p.dv == 64) return launch_bwd_dd<64, 64>(p, stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int grid, hipStream_t stream) {
+  if (p.d == 128 && p.dv == 128) return launch_bwd_dd<128, 128>(p, grid, stream);
+  if (p.d == 64 && p.dv == 128) return launch_bwd_dd<64, 128>(p, grid, stream);
+  if (p.d == 128 && p.dv == 64) return launch_bwd_dd<128, 64>(p, grid, stream);
+  if (p.d == 64 && p.dv == 64) return launch_bwd_dd<64, 64>(p, grid, stream);
   return hipErrorInvalidValue;
 }
 

@@ -68,6 +68,11 @@ constexpr int kFusedMergeItems = 2;
 // Query-tile height of the general (vector ALU) kernel.
 constexpr int kGenericBM = 64;
 
+// Gradient split plans: most units, most tiles per (b, h), most chunks per tile.
+constexpr int kMaxBwdUnits = 384;
+constexpr int kMaxBwdTiles = 256;
+constexpr int kMaxBwdChunks = 16;
+
 // Everything the gradient kernels need, passed by value as the kernel argument.
 // Strides are in elements; the innermost axis of every tensor is contiguous.
 struct BwdParams {
@@ -81,8 +86,8 @@ struct BwdParams {
   void* grad_q;
   void* grad_k;
   void* grad_v;
-  // Workspace: per (b, h) and group of 64 rows, 64 values of lse * log2(e) (+inf for
-  // rows past N or rows without an allowed key) then 64 values of D_i = dO_i . O_i.
+  // Workspace: per (b, h) and group of 64 rows, 64 values of -lse * sqrt(d) (-inf for
+  // rows past N or rows without an allowed key) then 64 values of -D_i = -dO_i . O_i.
   float* rowstat;
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
@@ -99,8 +104,26 @@ struct BwdParams {
   int causal;
   float scale_log2;   // log2(e) / sqrt(d)
   float scale;        // 1 / sqrt(d)
+  float sqrt_d;
   int n_kv_blocks;    // blocks 0 .. n_kv_blocks-1 form dK, dV; the rest form dQ
+  // Split plans (few tiles): a tile's steps (query steps of a key tile, key tiles of a
+  // query tile) are cut into consecutive chunks, one unit each. Units of a tile with
+  // more than one chunk write fp32 partial sums that a reduction kernel adds in chunk
+  // order. Unit u (dK/dV units first, then dQ units) is tile (unit[u] & 0xff), steps
+  // from ((>> 8) & 0x1ff), count ((>> 17) & 0x1ff), b*h (>> 26); the units of tile t
+  // are ubase[t] + bh * nch[t] + chunk.
+  int split;
+  int n_tiles;        // key tiles = query tiles per (b, h)
+  float* part;        // dK/dV units: [slot][128][d + dv], then dQ units: [slot][128][d]
+  int64_t part_q_off; // float offset of the dQ partials
+  uint32_t unit[kMaxBwdUnits];
+  int16_t ubase_kv[kMaxBwdTiles + 1], ubase_q[kMaxBwdTiles + 1];
+  uint8_t nch_kv[kMaxBwdTiles], nch_q[kMaxBwdTiles];
 };
+
+// Kernel arguments are passed by value; keep them within the 4 KiB argument block.
+static_assert(sizeof(Params) <= 4096, "forward kernel arguments exceed 4 KiB");
+static_assert(sizeof(BwdParams) <= 4096, "gradient kernel arguments exceed 4 KiB");
 
 // Key rows per dK/dV workgroup and query rows per dQ workgroup of the gradient kernel.
 constexpr int kBwdKT = 128;
@@ -110,7 +133,8 @@ constexpr int kBwdQT = 128;
 // grid: forward units; merge: whether split query tiles need the merge kernel.
 hipError_t launch_mfma_bf16(const Params& p, int grid, bool merge, hipStream_t stream);
 hipError_t launch_generic(const Params& p, bool is_bf16, hipStream_t stream);
-// Gradients dQ, dK, dV (bf16): row statistics, then one grid of dK/dV and dQ blocks.
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+// Gradients dQ, dK, dV (bf16): row statistics, one grid of `grid` dK/dV and dQ units,
+// then (split plans) the reduction of the chunk partials.
+hipError_t launch_bwd_bf16(const BwdParams& p, int grid, hipStream_t stream);
 
 }  // namespace fa

@@ -18,7 +18,7 @@ from __future__ import annotations
 
 __all__ = [
     "MI355X_PEAK_BF16_FLOPS", "MI355X_PEAK_F32_FLOPS", "MI355X_HBM_BYTES_PER_S",
-    "allowed_pairs", "alg_flops", "min_bytes", "materialised_sp_bytes",
+    "allowed_pairs", "alg_flops", "alg_flops_bwd", "min_bytes", "min_bytes_bwd", "materialised_sp_bytes",
     "intensity", "roofline_bound", "ridge",
 ]
 
@@ -41,6 +41,21 @@ def alg_flops(B, H, N, d, dv, causal, pairs=None) -> int:
     """
     p = allowed_pairs(N, causal) if pairs is None else pairs
     return 2 * (d + dv) * p * B * H
+
+
+def alg_flops_bwd(B, H, N, d, dv, causal, pairs=None) -> int:
+    """Algorithmic FLOPs of the gradients: the five products per allowed pair,
+    S = Q K^T (2d), dP = dO V^T (2dv), dV += P^T dO (2dv), dQ += dS K (2d) and
+    dK += dS^T Q (2d), i.e. 2*(3d + 2dv); recomputing S and dP a second time (as a
+    split into dK/dV and dQ passes does) is not counted."""
+    p = allowed_pairs(N, causal) if pairs is None else pairs
+    return 2 * (3 * d + 2 * dv) * p * B * H
+
+
+def min_bytes_bwd(B, H, N, d, dv, elem_bytes, bias_bytes=0) -> int:
+    """Minimum HBM bytes of the gradients: Q, K, V, O, dO and lse read once, dQ, dK,
+    dV written once, and an optional bias read once."""
+    return B * H * N * ((2 * d + 3 * dv) * elem_bytes + 4 + (2 * d + dv) * elem_bytes) + bias_bytes
 
 
 def min_bytes(B, H, N, d, dv, elem_bytes, bias_bytes=0, lse_bytes=4) -> int:

@@ -48,6 +48,8 @@ SMALL = [
     (3, dict(B=2, H=3, N=555)),
     (4, dict(H=2, N=1500)),
     (1, dict(N=700, causal=False)),
+    (3, dict(B=2, H=64, N=300)),   # more b*h than a split plan takes: one unit per tile
+    (2, dict(B=1, H=1, N=4000)),   # long single head: tiles cut into chunks
 ]
 
 
