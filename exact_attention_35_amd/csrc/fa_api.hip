@@ -483,7 +483,7 @@ int check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int 
 // Work plan of the gradients. Without a split, one dK/dV unit per (key tile, b*h) and
 // one dQ unit per (query tile, b*h). With few tiles (fewer dK/dV units than CUs), each
 // tile's loop (query steps of 64 rows for a key tile, key tiles of 64 for a query tile)
-// is cut into chunks of about equal length so that the grid has about 1.5 units per CU;
+// is cut into chunks of about equal length so that the grid has about 2 units per CU;
 // dK/dV steps cost about 4/3 of a dQ step (four products against three), so the
 // dK/dV kind gets 4/7 of the units.
 struct BwdPlan {
@@ -491,7 +491,6 @@ struct BwdPlan {
   int n_tiles = 0;
   int units_kv = 0, units_q = 0;
   std::vector<uint32_t> unit;  // dK/dV units, then dQ units
-  int16_t ubase_kv[fa::kMaxBwdTiles + 1] = {}, ubase_q[fa::kMaxBwdTiles + 1] = {};
   uint8_t nch_kv[fa::kMaxBwdTiles] = {}, nch_q[fa::kMaxBwdTiles] = {};
   size_t stat_bytes = 0, part_kv_floats = 0, part_q_floats = 0, ws_bytes = 0;
 };
@@ -509,7 +508,7 @@ BwdPlan make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, bo
   pl.n_tiles = (int)nt;
   pl.stat_bytes = round_up((size_t)BH * (size_t)bwd_groups(N) * 128 * sizeof(float), 256);
   const int env_units = env_int("FA_BWD_UNITS");
-  const int64_t target = std::min<int64_t>(fa::kMaxBwdUnits, env_units > 0 ? env_units : cus * 3 / 2);
+  const int64_t target = std::min<int64_t>(fa::kMaxBwdUnits, env_units > 0 ? env_units : cus * 2);
   pl.split = BH * nt < cus && BH <= 64 && nt <= fa::kMaxBwdTiles && nt > 0 && target >= 2 * BH * nt;
   if (!pl.split) {
     pl.units_kv = pl.units_q = (int)(BH * nt);
@@ -538,23 +537,22 @@ BwdPlan make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, bo
   }
   // units: key tiles from the first (longest under a causal mask), query tiles from the
   // last; b*h, then chunks; chunk c of n covers steps [c*s/n, (c+1)*s/n)
-  auto emit = [&](const std::vector<int64_t>& st, int64_t len, bool rev, int16_t* ubase, uint8_t* nch) {
-    int u0 = (int)pl.unit.size(), k = 0;
+  auto emit = [&](const std::vector<int64_t>& st, int64_t len, bool rev, uint8_t* nch) {
+    int u0 = (int)pl.unit.size();
     for (int i = 0; i < nt; ++i) {
       const int t = rev ? (int)nt - 1 - i : i;
       const int n = (int)std::min<int64_t>(fa::kMaxBwdChunks, (st[t] + len - 1) / len);
       nch[t] = (uint8_t)n;
-      ubase[t] = (int16_t)k;
       for (int64_t bh = 0; bh < BH; ++bh)
-        for (int c = 0; c < n; ++c, ++k) {
+        for (int c = 0; c < n; ++c) {
           const int64_t b0 = c * st[t] / n, b1 = (c + 1) * st[t] / n;
           pl.unit.push_back((uint32_t)t | ((uint32_t)b0 << 8) | ((uint32_t)(b1 - b0) << 17) | ((uint32_t)bh << 26));
         }
     }
     return (int)pl.unit.size() - u0;
   };
-  pl.units_kv = emit(skv, len_kv, false, pl.ubase_kv, pl.nch_kv);
-  pl.units_q = emit(sq, len_q, causal, pl.ubase_q, pl.nch_q);
+  pl.units_kv = emit(skv, len_kv, false, pl.nch_kv);
+  pl.units_q = emit(sq, len_q, causal, pl.nch_q);
   pl.part_kv_floats = (size_t)pl.units_kv * fa::kBwdKT * (size_t)(d + dv);
   pl.part_q_floats = (size_t)pl.units_q * fa::kBwdQT * (size_t)d;
   pl.ws_bytes = pl.stat_bytes + round_up((pl.part_kv_floats + pl.part_q_floats) * sizeof(float), 256);
@@ -658,8 +656,6 @@ int run_bwd(const BwdProblem& P, const BwdPlan& pl, void* ws, hipStream_t stream
     p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.stat_bytes);
     p.part_q_off = (int64_t)pl.part_kv_floats;
     std::copy(pl.unit.begin(), pl.unit.end(), p.unit);
-    std::copy(pl.ubase_kv, pl.ubase_kv + fa::kMaxBwdTiles + 1, p.ubase_kv);
-    std::copy(pl.ubase_q, pl.ubase_q + fa::kMaxBwdTiles + 1, p.ubase_q);
     std::copy(pl.nch_kv, pl.nch_kv + fa::kMaxBwdTiles, p.nch_kv);
     std::copy(pl.nch_q, pl.nch_q + fa::kMaxBwdTiles, p.nch_q);
   }

@@ -532,14 +532,26 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdParams p) {
   if (nch <= 1) return;
   const int b = bh / p.H, h = bh % p.H;
   const int W = kv ? D + DV : D;  // floats per row of a slot
-  const int slot0 = (kv ? p.ubase_kv[tile] : p.ubase_q[tile]) + bh * nch;
+  // first slot of the tile: the units of the tiles launched before it, then b*h
+  const uint8_t* nch_of = kv ? p.nch_kv : p.nch_q;
+  const bool rev = !kv && p.causal;
+  int before = 0;
+  for (int t = rev ? p.n_tiles - 1 : 0; t != tile; t += rev ? -1 : 1) before += nch_of[t];
+  const int slot0 = before * p.B * p.H + bh * nch;
   const float* base = p.part + (kv ? 0 : p.part_q_off) + (int64_t)slot0 * 128 * W;
   const int n4 = 32 * W / 4;  // float4 items of the block's 32 rows
   for (int it = threadIdx.x; it < n4; it += 256) {
     const int r = blockIdx.x * 32 + it / (W / 4);  // row within the tile
     const int c = (it % (W / 4)) * 4;              // column within the slot row
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < nch; ++j) acc += *reinterpret_cast<const floatx4*>(base + ((int64_t)j * 128 + r) * W + c);
+    // every chunk's load is issued before the sum (fixed order j = 0, 1, ...)
+    floatx4 v[kMaxBwdChunks];
+#pragma unroll
+    for (int j = 0; j < kMaxBwdChunks; ++j)
+      if (j < nch) v[j] = *reinterpret_cast<const floatx4*>(base + ((int64_t)j * 128 + r) * W + c);
+    floatx4 acc = v[0];
+#pragma unroll
+    for (int j = 1; j < kMaxBwdChunks; ++j)
+      if (j < nch) acc += v[j];
     const int n = tile * 128 + r;
     if (n >= p.N) continue;
     bf16x4 o4;

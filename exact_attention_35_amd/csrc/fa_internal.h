@@ -69,7 +69,7 @@ constexpr int kFusedMergeItems = 2;
 constexpr int kGenericBM = 64;
 
 // Gradient split plans: most units, most tiles per (b, h), most chunks per tile.
-constexpr int kMaxBwdUnits = 384;
+constexpr int kMaxBwdUnits = 512;
 constexpr int kMaxBwdTiles = 256;
 constexpr int kMaxBwdChunks = 16;
 
@@ -110,15 +110,15 @@ struct BwdParams {
   // query tile) are cut into consecutive chunks, one unit each. Units of a tile with
   // more than one chunk write fp32 partial sums that a reduction kernel adds in chunk
   // order. Unit u (dK/dV units first, then dQ units) is tile (unit[u] & 0xff), steps
-  // from ((>> 8) & 0x1ff), count ((>> 17) & 0x1ff), b*h (>> 26); the units of tile t
-  // are ubase[t] + bh * nch[t] + chunk.
+  // from ((>> 8) & 0x1ff), count ((>> 17) & 0x1ff), b*h (>> 26). Within a kind the
+  // units run over tiles in launch order (key tiles from the first, query tiles from
+  // the last under a causal mask, else from the first), then b*h, then chunks.
   int split;
   int n_tiles;        // key tiles = query tiles per (b, h)
   float* part;        // dK/dV units: [slot][128][d + dv], then dQ units: [slot][128][d]
   int64_t part_q_off; // float offset of the dQ partials
   uint32_t unit[kMaxBwdUnits];
-  int16_t ubase_kv[kMaxBwdTiles + 1], ubase_q[kMaxBwdTiles + 1];
-  uint8_t nch_kv[kMaxBwdTiles], nch_q[kMaxBwdTiles];
+  uint8_t nch_kv[kMaxBwdTiles], nch_q[kMaxBwdTiles];  // chunks per tile
 };
 
 // Kernel arguments are passed by value; keep them within the 4 KiB argument block.
