@@ -45,6 +45,9 @@
 //    at the key tile of its last row; waves skip blocks that lie entirely in the
 //    masked triangle, and element masks use the same comparison as the forward.
 
+#include <climits>
+#include <type_traits>
+
 #include "fa_internal.h"
 #include "fa_mfma_common.h"
 
@@ -328,13 +331,16 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
       for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(qr.row(qt_, qb, kk), kreg[kk], sacc);
 #pragma unroll
       for (int kk = 0; kk < DV / 16; ++kk) dpacc = mfma32(gr.row(gt_, qb, kk), vreg[kk], dpacc);
-      const bool edge = p.causal && qb0 < wk0 + 31;
       bf16x8 pk[2], dsk[2];
+      // P and dS of the block. Causal mask: key > row, i.e. kd > 8*(r/4) + r%4 with
+      // kd = key - qb0 - 4g; it never fires on blocks below the diagonal, and kd is made
+      // the smallest int without a causal mask.
+      const int kd = p.causal ? key - qb0 - 4 * g : INT_MIN;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         // base-2 exponent of P: sqrt(d) (S - lse) * log2(e) / sqrt(d)
         float pr = __builtin_amdgcn_exp2f(sacc[r] * p.scale_log2);
-        if (edge && key > qb0 + 8 * (r >> 2) + 4 * g + (r & 3)) pr = 0.f;
+        pr = kd > 8 * (r >> 2) + (r & 3) ? 0.f : pr;
         pk[r >> 3][r & 7] = (__bf16)pr;
         dsk[r >> 3][r & 7] = (__bf16)(pr * dpacc[r]);
       }
@@ -417,8 +423,9 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
     greg[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(gp + (int64_t)qi * p.do_sn + kk * 16 + g * 8) : bf16x8{};
   const int qc = min(qi, N - 1);
   const float* grp = p.rowstat + ((int64_t)bh * p.n_grp + qc / 64) * 128;
-  const float mrow = qvalid ? grp[qc % 64] : -INFINITY;  // -lse*sqrt(d)
-  const float ndrow = qvalid ? grp[64 + qc % 64] : 0.f;    // -D
+  // base-2 exponent of P: (sqrt(d) (Q K^T/sqrt(d) + C) - lse sqrt(d)) log2(e)/sqrt(d)
+  const float mcs = qvalid ? grp[qc % 64] * p.scale_log2 : -INFINITY;  // -lse log2(e)
+  const float ndrow = qvalid ? grp[64 + qc % 64] : 0.f;                 // -D
   const float* brow = nullptr;
   if constexpr (BIAS) brow = p.bias + b * p.b_sb + h * p.b_sh + (int64_t)qc * p.b_si;
 
@@ -454,33 +461,42 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
     const unsigned char* kt_ = cur;
     const unsigned char* vt_ = cur + C::KTILE;
     const int kv0 = t * C::KS;
-    // accumulators start from sqrt(d) (C - lse) and -D (see dkdv_block)
+    // The row's lse and D are per-lane scalars here, so the accumulators start from 0
+    // (sqrt(d) C with a bias) and the statistics enter in the element loop; start
+    // values that are the same in every register would hold 32 registers for the loop.
     floatx16 sacc[2], dpacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sacc[kb][r] = mrow;
-        if constexpr (BIAS)
-          sacc[kb][r] = fmaf(brow[min(kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3), N - 1)], p.sqrt_d, mrow);
-        dpacc[kb][r] = ndrow;
+        sacc[kb][r] = 0.f;
+        if constexpr (BIAS) sacc[kb][r] = brow[min(kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3), N - 1)] * p.sqrt_d;
+        dpacc[kb][r] = 0.f;
       }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) sacc[kb] = mfma32(kr.row(kt_, kb, kk), qreg[kk], sacc[kb]);
 #pragma unroll
       for (int kk = 0; kk < DV / 16; ++kk) dpacc[kb] = mfma32(vr.row(vt_, kb, kk), greg[kk], dpacc[kb]);
     }
-    const bool edge = kv0 + C::KS > N || (p.causal && kv0 + C::KS - 1 > wq0);
     bf16x8 dsk[4];
+    // dS of the tile; tiles that cross the diagonal or the sequence end mask keys
+    auto dscores = [&](auto MASKc) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(sacc[kb][r] * p.scale_log2);
-        const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (edge && (key >= N || (p.causal && key > qi))) pr = 0.f;
-        dsk[kb * 2 + (r >> 3)][r & 7] = (__bf16)(pr * dpacc[kb][r]);
-      }
+        for (int r = 0; r < 16; ++r) {
+          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, mcs));
+          if constexpr (decltype(MASKc)::value) {
+            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= N || (p.causal && key > qi)) pr = 0.f;
+          }
+          dsk[kb * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (dpacc[kb][r] + ndrow));
+        }
+    };
+    if (kv0 + C::KS > N || (p.causal && kv0 + C::KS - 1 > wq0))
+      dscores(std::true_type{});
+    else
+      dscores(std::false_type{});
 #pragma unroll
     for (int sg = 0; sg < 4; ++sg)
 #pragma unroll
