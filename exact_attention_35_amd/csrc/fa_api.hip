@@ -645,6 +645,7 @@ int run_bwd(const BwdProblem& P, const BwdPlan& pl, void* ws, hipStream_t stream
   p.l_sb = s.lse[0]; p.l_sh = s.lse[1];
   p.B = (int)P.B; p.H = (int)P.H; p.N = (int)P.N; p.d = (int)P.d; p.dv = (int)P.dvw;
   p.n_grp = (int)bwd_groups(P.N);
+  p.bias_vec4 = P.bias && aligned(P.bias, 16) && s.bias[0] % 4 == 0 && s.bias[1] % 4 == 0 && s.bias[2] % 4 == 0;
   p.causal = P.mask == FA_MASK_CAUSAL;
   p.scale = (float)(1.0 / std::sqrt((double)P.d));
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.d));

@@ -465,13 +465,28 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
     // (sqrt(d) C with a bias) and the statistics enter in the element loop; start
     // values that are the same in every register would hold 32 registers for the loop.
     floatx16 sacc[2], dpacc[2];
+    const bool bvec = BIAS && p.bias_vec4 && kv0 + C::KS <= N;  // 4 keys per 16-byte load
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sacc[kb][r] = 0.f;
-        if constexpr (BIAS) sacc[kb][r] = brow[min(kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3), N - 1)] * p.sqrt_d;
         dpacc[kb][r] = 0.f;
+      }
+      if constexpr (BIAS) {
+        // register r holds key kv0 + 32 kb + 8 (r/4) + 4 g + r%4
+        if (bvec) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const floatx4 b4 = *reinterpret_cast<const floatx4*>(brow + kv0 + kb * 32 + 8 * r4 + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[kb][4 * r4 + e] = b4[e] * p.sqrt_d;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[kb][r] = brow[min(kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3), N - 1)] * p.sqrt_d;
+        }
       }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) sacc[kb] = mfma32(kr.row(kt_, kb, kk), qreg[kk], sacc[kb]);

@@ -102,6 +102,7 @@ struct BwdParams {
   int B, H, N, d, dv;
   int n_grp;          // groups of 64 rows per (b, h) in rowstat: ceil(N / 128) * 2
   int causal;
+  int bias_vec4;      // bias base 16-byte aligned and every bias stride a multiple of 4
   float scale_log2;   // log2(e) / sqrt(d)
   float scale;        // 1 / sqrt(d)
   float sqrt_d;
