@@ -552,8 +552,11 @@ __global__ __launch_bounds__(256, 2) void bwd_mfma(BwdParams p) {
 }
 
 // Sum of the chunk partials of split tiles, in chunk order, into the bf16 gradients.
-// Block (row group of 32, b*h, tile): tile < n_tiles is a key tile (dK, dV), else a
-// query tile (dQ). Tiles with a single chunk were written by their unit.
+// Block (row group of kReduceRows, b*h, tile): tile < n_tiles is a key tile (dK, dV),
+// else a query tile (dQ). Tiles with a single chunk were written by their unit. Small
+// row groups give each thread one or two items, whose chunk loads are all in flight
+// together.
+constexpr int kReduceRows = 8;
 template <int D, int DV>
 __global__ __launch_bounds__(256) void bwd_reduce(BwdParams p) {
   const int bh = blockIdx.y;
@@ -570,9 +573,9 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdParams p) {
   for (int t = rev ? p.n_tiles - 1 : 0; t != tile; t += rev ? -1 : 1) before += nch_of[t];
   const int slot0 = before * p.B * p.H + bh * nch;
   const float* base = p.part + (kv ? 0 : p.part_q_off) + (int64_t)slot0 * 128 * W;
-  const int n4 = 32 * W / 4;  // float4 items of the block's 32 rows
+  const int n4 = kReduceRows * W / 4;  // float4 items of the block's rows
   for (int it = threadIdx.x; it < n4; it += 256) {
-    const int r = blockIdx.x * 32 + it / (W / 4);  // row within the tile
+    const int r = blockIdx.x * kReduceRows + it / (W / 4);  // row within the tile
     const int c = (it % (W / 4)) * 4;              // column within the slot row
     // every chunk's load is issued before the sum (fixed order j = 0, 1, ...)
     floatx4 v[kMaxBwdChunks];
@@ -628,7 +631,8 @@ hipError_t launch_bwd_dd(const BwdParams& p, int grid, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_mfma<D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || !p.split) return e;
-  hipLaunchKernelGGL((bwd_reduce<D, DV>), dim3(4, p.B * p.H, 2 * p.n_tiles), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_reduce<D, DV>), dim3(kBwdKT / kReduceRows, p.B * p.H, 2 * p.n_tiles), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
