@@ -22,8 +22,10 @@ Readings taken where the page is silent (each is listed in the design notes):
     scaled and biased scores;
   * d (the Q/K width) sets the scale even when d != d_v;
   * C is added after scaling and is not itself scaled;
-  * causal means C_ij = -inf for j > i (top-left aligned, square N x N), and a bias
-    and the causal mask add;
+  * causal means C_ij = -inf for j > i + (N_k - N_q): with N_q = N_k = N the square
+    mask above the diagonal; with N_q query rows against N_k keys the rows are aligned
+    to the end of the key sequence (query i is position N_k - N_q + i, so one query
+    row against a long key sequence sees every key); a bias and the causal mask add;
   * a bias tensor may broadcast over batch (stride 0) or over heads;
   * a row with no allowed key violates the page's precondition; by default the oracle
     raises, and with ``allow_empty_rows=True`` it returns the convention O = 0,
@@ -61,15 +63,16 @@ def _as_f64(x) -> np.ndarray:
 def _row_block(qbh, kbh, vbh, c_rows, rows, causal, scale, allow_empty_rows):
     """Rows `rows` of one (batch, head): the definition, written out in float64.
 
-    c_rows is None or the bias rows already selected ([len(rows), N]).
+    c_rows is None or the bias rows already selected ([len(rows), N_k]).
     """
+    n_q = qbh.shape[0]
     # S = Q K^T / sqrt(d) + C  (C = bias + causal mask)
     s = (qbh[rows] @ kbh.T) * scale
     if c_rows is not None:
         s = s + c_rows
     if causal:
         keys = np.arange(kbh.shape[0])[None, :]
-        s = np.where(keys > rows[:, None], -np.inf, s)
+        s = np.where(keys > rows[:, None] + (kbh.shape[0] - n_q), -np.inf, s)
     # m_i = max_j S_ij
     m = s.max(axis=1)
     empty = ~np.isfinite(m) & (m < 0)
@@ -93,7 +96,7 @@ def _row_block(qbh, kbh, vbh, c_rows, rows, causal, scale, allow_empty_rows):
 def _bias_slice(bias, b, h):
     if bias is None:
         return None
-    # bias broadcasts to [B, H, N, N]
+    # bias broadcasts to [B, H, N_q, N_k]
     bb = bias.shape[0]
     bh = bias.shape[1]
     return bias[b if bb > 1 else 0, h if bh > 1 else 0]
@@ -103,10 +106,11 @@ def sdpa_reference(q, k, v, bias=None, causal=False, *, row_chunk=2048,
                    allow_empty_rows=False):
     """Exact attention forward of every (batch, head) in float64.
 
-    q: [B, H, N, d], k: [B, H, N, d], v: [B, H, N, dv] (logical layout; any real
-    dtype, torch or numpy). bias: None or [Bb, Hb, N, N] with Bb in {1, B} and
-    Hb in {1, H}; -inf entries forbid keys. causal: add -inf above the diagonal.
-    Returns (O [B, H, N, dv], lse [B, H, N]) as float64 numpy arrays.
+    q: [B, H, N_q, d], k: [B, H, N_k, d], v: [B, H, N_k, dv] (logical layout; any real
+    dtype, torch or numpy; N_q = N_k = N in the square case). bias: None or
+    [Bb, Hb, N_q, N_k] with Bb in {1, B} and Hb in {1, H}; -inf entries forbid keys.
+    causal: add -inf for keys j > i + (N_k - N_q).
+    Returns (O [B, H, N_q, dv], lse [B, H, N_q]) as float64 numpy arrays.
     Query rows are processed in chunks of `row_chunk`; rows are independent in the
     definition, so chunking rows changes nothing.
     """
@@ -115,12 +119,13 @@ def sdpa_reference(q, k, v, bias=None, causal=False, *, row_chunk=2048,
     v = _as_f64(v)
     bias = None if bias is None else _as_f64(bias)
     B, H, N, d = q.shape
+    nk = k.shape[2]
     dv = v.shape[-1]
-    if k.shape != (B, H, N, d) or v.shape != (B, H, N, dv):
+    if k.shape != (B, H, nk, d) or v.shape != (B, H, nk, dv):
         raise ValueError("q, k, v shapes disagree")
-    if bias is not None and (bias.ndim != 4 or bias.shape[2:] != (N, N)
+    if bias is not None and (bias.ndim != 4 or bias.shape[2:] != (N, nk)
                              or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H)):
-        raise ValueError("bias must broadcast to [B, H, N, N]")
+        raise ValueError("bias must broadcast to [B, H, N_q, N_k]")
     scale = 1.0 / math.sqrt(d)
     out = np.empty((B, H, N, dv), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
@@ -140,9 +145,9 @@ def sdpa_reference(q, k, v, bias=None, causal=False, *, row_chunk=2048,
 def sdpa_reference_rows(q, k, v, bias, causal, b, h, rows, *, allow_empty_rows=False):
     """The same definition for selected query rows of one (batch, head).
 
-    Used at sizes where the full N x N problem is too large for the CPU: each
+    Used at sizes where the full N_q x N_k problem is too large for the CPU: each
     sampled row is computed on its own, exactly as in `sdpa_reference`.
-    q, k, v are [B, H, N, *] (torch or numpy, any layout; only the needed slices are
+    q is [B, H, N_q, *], k and v are [B, H, N_k, *] (torch or numpy, any layout; only the needed slices are
     converted); bias as in `sdpa_reference`. Returns (O [len(rows), dv], lse [len(rows)]).
     """
     rows = np.asarray(rows, dtype=np.int64)

@@ -433,3 +433,71 @@ def test_bf16_inputs_are_upcast_exactly():
     x = torch.tensor([[[[1.0 + 2 ** -7, -3.0 - 2 ** -6]]]], dtype=torch.bfloat16)
     o, _ = sdpa_reference(x, x, x, None, False)
     assert o[0, 0, 0, 0] == 1.0 + 2 ** -7 and o[0, 0, 0, 1] == -3.0 - 2 ** -6
+
+
+# ---------------------------------------------------------------------------
+# N_q != N_k: the reading of the causal mask (queries aligned to the end of the keys)
+# ---------------------------------------------------------------------------
+
+def _rect(seed, nq, nk, d=5, dv=3, bias=False):
+    rng = _rng(seed)
+    q = rng.normal(size=(1, 2, nq, d))
+    k = rng.normal(size=(1, 2, nk, d))
+    v = rng.normal(size=(1, 2, nk, dv))
+    c = rng.normal(size=(1, 2, nq, nk)) if bias else None
+    return q, k, v, c
+
+
+@pytest.mark.parametrize("nq,nk", [(3, 7), (7, 3), (1, 9), (5, 5)])
+def test_rectangular_noncausal_brute_force(nq, nk):
+    # without a mask every key is allowed: the plain definition, looped in pure Python
+    q, k, v, c = _rect(40 + nq, nq, nk, bias=True)
+    o, lse = sdpa_reference(q, k, v, c, False)
+    for h in range(2):
+        for i in range(nq):
+            s = [math.fsum(q[0, h, i, t] * k[0, h, j, t] for t in range(5)) / math.sqrt(5) + c[0, h, i, j]
+                 for j in range(nk)]
+            w = [math.exp(x) for x in s]
+            tot = math.fsum(w)
+            want = [math.fsum(w[j] * v[0, h, j, t] for j in range(nk)) / tot for t in range(3)]
+            np.testing.assert_allclose(o[0, h, i], want, rtol=1e-13, atol=1e-14)
+            assert abs(lse[0, h, i] - math.log(tot)) < 1e-12
+
+
+def test_single_query_row_sees_every_key():
+    # one query row against N_k keys (decode): the causal mask forbids nothing
+    q, k, v, c = _rect(50, 1, 12, bias=True)
+    oc, lc = sdpa_reference(q, k, v, c, True)
+    on, ln = sdpa_reference(q, k, v, c, False)
+    np.testing.assert_array_equal(oc, on)
+    np.testing.assert_array_equal(lc, ln)
+
+
+@pytest.mark.parametrize("nq", [1, 4, 11])
+def test_query_rows_are_the_last_positions_of_the_sequence(nq):
+    # N_q rows against N_k keys under the causal mask equal the last N_q rows of the
+    # square causal problem whose queries end with them
+    nk = 11
+    rng = _rng(60 + nq)
+    qf = rng.normal(size=(1, 2, nk, 4))
+    k = rng.normal(size=(1, 2, nk, 4))
+    v = rng.normal(size=(1, 2, nk, 3))
+    cf = rng.normal(size=(1, 2, nk, nk))
+    of, lf = sdpa_reference(qf, k, v, cf, True)
+    o, lse = sdpa_reference(qf[:, :, nk - nq:], k, v, cf[:, :, nk - nq:], True)
+    np.testing.assert_allclose(o, of[:, :, nk - nq:], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse, lf[:, :, nk - nq:], rtol=1e-14, atol=1e-15)
+
+
+def test_more_query_rows_than_keys():
+    # N_q > N_k under the causal mask: the first N_q - N_k rows see no key (precondition
+    # violated: the oracle raises, or returns the O = 0, lse = -inf convention); the
+    # others are the square problem
+    q, k, v, _ = _rect(70, 9, 4)
+    with pytest.raises(EmptyRowError):
+        sdpa_reference(q, k, v, None, True)
+    o, lse = sdpa_reference(q, k, v, None, True, allow_empty_rows=True)
+    assert (o[:, :, :5] == 0).all() and np.isneginf(lse[:, :, :5]).all()
+    o2, l2 = sdpa_reference(q[:, :, 5:], k, v, None, True)
+    np.testing.assert_array_equal(o[:, :, 5:], o2)
+    np.testing.assert_array_equal(lse[:, :, 5:], l2)
