@@ -97,7 +97,7 @@ def cpu_baseline(w, inp, budget_s=10.0):
         pass
     if threads is None:
         threads = len(os.sched_getaffinity(0))
-    dense = 2.0 * (w.d + w.dv) * w.N * w.N * w.B * w.H
+    dense = 2.0 * (w.d + w.dv) * w.n_q * w.N * w.B * w.H
     if dense <= 60e9:  # whole workload
         calls, total = 0, 0.0
         while total < budget_s and calls < 50:
@@ -105,7 +105,7 @@ def cpu_baseline(w, inp, budget_s=10.0):
             sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
             total += time.perf_counter() - t0
             calls += 1
-        flops = rf.alg_flops(w.B, w.H, w.N, w.d, w.dv, w.causal) * calls
+        flops = rf.alg_flops(w.B, w.H, w.N, w.d, w.dv, w.causal, Nq=w.n_q) * calls
         sample = f"whole workload ({w.name}), {calls} call{'s' if calls != 1 else ''}, fp64 numpy, {total:.1f} s"
     else:  # whole rows of head (0, 0), spread over the sequence
         rng = np.random.default_rng(0)
@@ -160,29 +160,36 @@ def main() -> int:
             gpu[n] = t.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
         else:
             gpu[n] = t.to(dev)
-    out = torch.empty(w.B, w.H, w.N, w.dv, dtype=gpu["q"].dtype, device=dev)
-    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    out = torch.empty(w.B, w.H, w.n_q, w.dv, dtype=gpu["q"].dtype, device=dev)
+    lse = torch.empty(w.B, w.H, w.n_q, dtype=torch.float32, device=dev)
     if args.which == "bwd":
         return bench_bwd(args, w, inp, gpu, out, lse)
 
     # One validated call through the binding, then the same C entry point with its
-    # arguments marshalled once, so the timed loop is the library call itself.
-    capi.fa_fwd(gpu["q"], gpu["k"], gpu["v"], bias=gpu["bias"], causal=w.causal, out=out, lse=lse)
+    # arguments marshalled once, so the timed loop is the library call itself. Workloads
+    # with N_q query rows against N keys go through fa_fwd_qk.
+    rect = w.n_q != w.N
+    if rect:
+        capi.fa_fwd_qk(gpu["q"], gpu["k"], gpu["v"], bias=gpu["bias"], causal=w.causal, out=out, lse=lse)
+    else:
+        capi.fa_fwd(gpu["q"], gpu["k"], gpu["v"], bias=gpu["bias"], causal=w.causal, out=out, lse=lse)
     stream = torch.cuda.current_stream(dev)   # fa_fwd launches on this stream
     L = capi.lib()
     strides = capi.make_strides(gpu["q"], gpu["k"], gpu["v"], out,
-                                None if gpu["bias"] is None else gpu["bias"].expand(w.B, w.H, w.N, w.N),
+                                None if gpu["bias"] is None else gpu["bias"].expand(w.B, w.H, w.n_q, w.N),
                                 lse)
     vp = ctypes.c_void_p
+    sizes = (w.B, w.H, w.n_q, w.N) if rect else (w.B, w.H, w.N)
     call = (vp(gpu["q"].data_ptr()), vp(gpu["k"].data_ptr()), vp(gpu["v"].data_ptr()),
             vp(0 if gpu["bias"] is None else gpu["bias"].data_ptr()),
             capi.FA_MASK_CAUSAL if w.causal else capi.FA_MASK_NONE,
-            vp(out.data_ptr()), vp(lse.data_ptr()), w.B, w.H, w.N, w.d, w.dv,
+            vp(out.data_ptr()), vp(lse.data_ptr()), *sizes, w.d, w.dv,
             ctypes.byref(strides), capi.FA_BF16 if w.dtype == "bf16" else capi.FA_F32,
             vp(stream.cuda_stream))
+    entry = L.fa_fwd_qk if rect else L.fa_fwd
 
     def step():
-        st = L.fa_fwd(*call)
+        st = entry(*call)
         if st:
             raise capi.FaError(st, capi.fa_status_string(st))
 
@@ -204,20 +211,21 @@ def main() -> int:
     # divided by the launch count is the average launch duration (plus launch gaps).
     avg_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
 
-    flops = rf.alg_flops(w.B, w.H, w.N, w.d, w.dv, w.causal)
+    flops = rf.alg_flops(w.B, w.H, w.N, w.d, w.dv, w.causal, Nq=w.n_q)
     elem = 2 if w.dtype == "bf16" else 4
-    bias_bytes = (w.H * w.N * w.N * 4) if w.bias else 0
-    min_b = rf.min_bytes(w.B, w.H, w.N, w.d, w.dv, elem, bias_bytes=bias_bytes)
+    bias_bytes = (w.H * w.n_q * w.N * 4) if w.bias else 0
+    min_b = rf.min_bytes(w.B, w.H, w.N, w.d, w.dv, elem, bias_bytes=bias_bytes, Nq=w.n_q)
     value = flops * args.steps / wall / 1e12
     achieved = flops / avg_launch_s / 1e12
     if w.dtype == "bf16":
         peak, bound = rf.MI355X_PEAK_BF16_FLOPS / 1e12, "mfma"
     else:
         peak, bound = rf.MI355X_PEAK_F32_FLOPS / 1e12, "mfma"
-    if w.bias:  # the bias stream makes this workload memory-bound at I = F/Q
-        attain, _, which = rf.roofline_bound(flops, min_b, peak * 1e12, rf.MI355X_HBM_BYTES_PER_S)
-        if which == "memory":
-            bound = "hbm"
+    # which ceiling binds at I = F/Q: the bias stream (and a decoding step, which reads
+    # every key and value for one row) make a workload memory-bound
+    _, _, which = rf.roofline_bound(flops, min_b, peak * 1e12, rf.MI355X_HBM_BYTES_PER_S)
+    if which == "memory":
+        bound = "hbm"
     traffic = read_traffic(w.name)
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": min_b / avg_launch_s / 1e9, "peak": 8000.0,
@@ -245,7 +253,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv,
                    "causal": w.causal, "bias": w.bias, "layout": w.layout,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", **({"N_q": w.n_q} if rect else {})},
         "pct_of_peak": 100.0 * value / (rf.MI355X_PEAK_BF16_FLOPS / 1e12),
         "roofline": roof,
     }

@@ -17,6 +17,7 @@ __all__ = [
     "STATUS", "lib", "library_path", "fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size",
     "fa_status_string", "fa_version", "fa_shutdown", "fa_plan_describe", "make_strides", "FaStrides",
     "FaPlanInfo", "EXPORTED", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "FaBwdStrides",
+    "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size",
 ]
 
 FA_OK = 0
@@ -33,7 +34,7 @@ STATUS = {
 # every symbol include/*.h declares
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
             "fa_version", "fa_shutdown", "fa_plan_describe", "fa_bwd", "fa_bwd_ex",
-            "fa_bwd_workspace_size")
+            "fa_bwd_workspace_size", "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -88,6 +89,14 @@ def lib():
     L.fa_fwd_ex.restype = ctypes.c_int
     L.fa_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     L.fa_fwd_workspace_size.restype = sz
+    qk_args = [vp, vp, vp, vp, ctypes.c_int, vp, vp, i64, i64, i64, i64, i64, i64,
+               ctypes.POINTER(FaStrides), ctypes.c_int, vp]
+    L.fa_fwd_qk.argtypes = qk_args
+    L.fa_fwd_qk.restype = ctypes.c_int
+    L.fa_fwd_qk_ex.argtypes = qk_args + [vp, sz]
+    L.fa_fwd_qk_ex.restype = ctypes.c_int
+    L.fa_fwd_qk_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    L.fa_fwd_qk_workspace_size.restype = sz
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -162,14 +171,15 @@ def make_strides(q, k, v, out, bias=None, lse=None) -> FaStrides:
     return s
 
 
-def _prepare(q, k, v, bias, causal, out, lse):
+def _prepare(q, k, v, bias, causal, out, lse, rect=False):
     import torch
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise FaError(STATUS["FA_ERR_SHAPE"], "q, k, v must be 4-D [B, H, N, *]")
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     dv = v.shape[-1]
-    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape[:3]) != (B, H, N):
+    if (not rect and Nk != N) or tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape[:3]) != (B, H, Nk):
         raise FaError(STATUS["FA_ERR_SHAPE"], "q, k, v shapes disagree")
     dt = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -182,8 +192,8 @@ def _prepare(q, k, v, bias, causal, out, lse):
             raise FaError(STATUS["FA_ERR_DTYPE"], "bias must be float32")
         if bias.dim() == 3:
             bias = bias.unsqueeze(0)
-        bias = bias.expand(B, H, N, N)
-        if N and bias.stride(-1) != 1:
+        bias = bias.expand(B, H, N, Nk)
+        if N and Nk and bias.stride(-1) != 1:
             raise FaError(STATUS["FA_ERR_STRIDE"], "bias key axis must be contiguous")
     if out is None:
         out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
@@ -191,6 +201,8 @@ def _prepare(q, k, v, bias, causal, out, lse):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     mask = FA_MASK_CAUSAL if causal else FA_MASK_NONE
     strides = make_strides(q, k, v, out, bias, lse)
+    if rect:
+        return (B, H, N, Nk, d, dv, dt, mask, bias, out, lse, strides)
     return (B, H, N, d, dv, dt, mask, bias, out, lse, strides)
 
 
@@ -217,6 +229,36 @@ def fa_fwd(q, k, v, bias=None, causal=False, out=None, lse=None, stream=None):
     B, H, N, d, dv, dt, mask, bias, out, lse, strides = _prepare(q, k, v, bias, causal, out, lse)
     st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), mask, _ptr(out), _ptr(lse),
                       B, H, N, d, dv, ctypes.byref(strides), dt, _stream_handle(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def fa_fwd_qk(q, k, v, bias=None, causal=False, out=None, lse=None, stream=None):
+    """Attention forward of N_q query rows against N_k keys through fa_fwd_qk.
+
+    q: [B, H, N_q, d]; k: [B, H, N_k, d]; v: [B, H, N_k, dv]; bias: None or fp32
+    broadcastable to [B, H, N_q, N_k]. The causal mask aligns the query rows to the end
+    of the keys (key j allowed for row i iff j <= i + N_k - N_q). Returns (out, lse).
+    """
+    B, H, Nq, Nk, d, dv, dt, mask, bias, out, lse, strides = _prepare(q, k, v, bias, causal, out, lse, rect=True)
+    st = lib().fa_fwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), mask, _ptr(out), _ptr(lse),
+                         B, H, Nq, Nk, d, dv, ctypes.byref(strides), dt, _stream_handle(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def fa_fwd_qk_workspace_size(B, H, Nq, Nk, d, dv, dtype_code, causal) -> int:
+    return int(lib().fa_fwd_qk_workspace_size(B, H, Nq, Nk, d, dv, dtype_code,
+                                              FA_MASK_CAUSAL if causal else FA_MASK_NONE))
+
+
+def fa_fwd_qk_ex(q, k, v, workspace, bias=None, causal=False, out=None, lse=None, stream=None):
+    """fa_fwd_qk with a caller-provided workspace (a uint8 device tensor, or None)."""
+    B, H, Nq, Nk, d, dv, dt, mask, bias, out, lse, strides = _prepare(q, k, v, bias, causal, out, lse, rect=True)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa_fwd_qk_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), mask, _ptr(out), _ptr(lse),
+                            B, H, Nq, Nk, d, dv, ctypes.byref(strides), dt,
+                            _stream_handle(stream, q.device), _ptr(workspace), nbytes)
     _check(st)
     return out, lse
 

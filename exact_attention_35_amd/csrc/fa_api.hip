@@ -78,41 +78,47 @@ struct Problem {
   const float* bias;
   void* out;
   float* lse;
-  int64_t B, H, N, d, dv;
+  int64_t B, H, N, d, dv;  // N: keys (rows of K, V)
+  int64_t Nq;              // query rows (rows of Q, O, lse)
   int mask, dtype;
   fa_strides st;
 };
 
-fa_strides contiguous_strides(int64_t H, int64_t N, int64_t d, int64_t dv) {
+fa_strides contiguous_strides(int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t dv) {
   fa_strides s;
-  s.q[0] = H * N * d; s.q[1] = N * d; s.q[2] = d;
+  s.q[0] = H * Nq * d; s.q[1] = Nq * d; s.q[2] = d;
   s.k[0] = H * N * d; s.k[1] = N * d; s.k[2] = d;
   s.v[0] = H * N * dv; s.v[1] = N * dv; s.v[2] = dv;
-  s.out[0] = H * N * dv; s.out[1] = N * dv; s.out[2] = dv;
-  s.bias[0] = H * N * N; s.bias[1] = N * N; s.bias[2] = N;
-  s.lse[0] = H * N; s.lse[1] = N;
+  s.out[0] = H * Nq * dv; s.out[1] = Nq * dv; s.out[2] = dv;
+  s.bias[0] = H * Nq * N; s.bias[1] = Nq * N; s.bias[2] = N;
+  s.lse[0] = H * Nq; s.lse[1] = Nq;
   return s;
 }
 
 bool supported_width(int64_t x) { return x == 64 || x == 128; }
 
-// Size/shape/dtype/mask checks shared by the size query and the forward calls.
-int check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask) {
+// Size/shape/dtype/mask checks shared by the size queries and the forward calls
+// (Nq query rows against N keys).
+int check_shape_qk(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t dv, int dtype, int mask) {
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (B < 0 || H < 0 || N < 0 || Nq < 0) return FA_ERR_SHAPE;
   if (!supported_width(d) || !supported_width(dv)) return FA_ERR_SHAPE;
   const int64_t lim = (int64_t)1 << 30;
-  if (B > lim || H > lim || N > lim) return FA_ERR_SHAPE;
-  if (B * H > lim || (B * H) * ((N + 63) / 64) > lim) return FA_ERR_SHAPE;
+  if (B > lim || H > lim || N > lim || Nq > lim) return FA_ERR_SHAPE;
+  if (B * H > lim || (B * H) * ((std::max(N, Nq) + 63) / 64) > lim) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
+int check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask) {
+  return check_shape_qk(B, H, N, N, d, dv, dtype, mask);
+}
+
 int validate(const Problem& P) {
-  int st = check_shape(P.B, P.H, P.N, P.d, P.dv, P.dtype, P.mask);
+  int st = check_shape_qk(P.B, P.H, P.Nq, P.N, P.d, P.dv, P.dtype, P.mask);
   if (st != FA_OK) return st;
-  if (P.B * P.H * P.N == 0) return FA_OK;
-  if (!P.q || !P.k || !P.v || !P.out) return FA_ERR_NULL;
+  if (P.B * P.H * P.Nq == 0) return FA_OK;  // no output rows: nothing to do
+  if (!P.q || !P.out || (P.N > 0 && (!P.k || !P.v))) return FA_ERR_NULL;
   const fa_strides& s = P.st;
   const int64_t* all[] = {s.q, s.k, s.v, s.out, s.bias};
   for (int t = 0; t < 5; ++t)
@@ -121,9 +127,10 @@ int validate(const Problem& P) {
   if (s.lse[0] < 0 || s.lse[1] < 0) return FA_ERR_STRIDE;
   // the bf16 kernel addresses a 64-row key tile with 32-bit byte offsets
   if (P.dtype == FA_BF16 && (s.k[2] >= kMaxRowStride || s.v[2] >= kMaxRowStride)) return FA_ERR_STRIDE;
-  const int64_t sz[3] = {P.B, P.H, P.N};
+  const int64_t sz[3] = {P.B, P.H, P.Nq};   // q, out, lse, bias rows
+  const int64_t szk[3] = {P.B, P.H, P.N};   // k, v
   if (!non_overlapping(sz, s.out, 3, P.dv)) return FA_ERR_STRIDE;
-  if (P.lse && !non_overlapping(sz, s.lse, 2, P.N)) return FA_ERR_STRIDE;
+  if (P.lse && !non_overlapping(sz, s.lse, 2, P.Nq)) return FA_ERR_STRIDE;
 
   const int es = P.dtype == FA_BF16 ? 2 : 4;
   const void* ptrs[4] = {P.q, P.k, P.v, P.out};
@@ -138,18 +145,17 @@ int validate(const Problem& P) {
 
   // aliasing: outputs must not overlap inputs or each other
   const Range rq = extent(P.q, sz, s.q, 3, P.d, es);
-  const Range rk = extent(P.k, sz, s.k, 3, P.d, es);
-  const Range rv = extent(P.v, sz, s.v, 3, P.dv, es);
+  const Range rk = P.N ? extent(P.k, szk, s.k, 3, P.d, es) : Range{0, 0};
+  const Range rv = P.N ? extent(P.v, szk, s.v, 3, P.dv, es) : Range{0, 0};
   const Range ro = extent(P.out, sz, s.out, 3, P.dv, es);
   if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv)) return FA_ERR_ALIAS;
   Range rb{0, 0};
-  if (P.bias) {
-    const int64_t bsz[3] = {P.B, P.H, P.N};
-    rb = extent(P.bias, bsz, s.bias, 3, P.N, 4);
+  if (P.bias && P.N) {
+    rb = extent(P.bias, sz, s.bias, 3, P.N, 4);
     if (overlaps(ro, rb)) return FA_ERR_ALIAS;
   }
   if (P.lse) {
-    const Range rl = extent(P.lse, sz, s.lse, 2, P.N, 4);
+    const Range rl = extent(P.lse, sz, s.lse, 2, P.Nq, 4);
     if (overlaps(rl, rq) || overlaps(rl, rk) || overlaps(rl, rv) || overlaps(rl, ro)) return FA_ERR_ALIAS;
     if (P.bias && overlaps(rl, rb)) return FA_ERR_ALIAS;
   }
@@ -206,11 +212,12 @@ int env_int(const char* name) {
   return e ? std::atoi(e) : 0;
 }
 
-// Key tiles of query tile qt (causal tiles stop at the diagonal).
-int64_t qtile_ntiles(int64_t N, int qt, bool causal) {
+// Key tiles of query tile qt (causal tiles stop at the last key the tile's last row may
+// see, qt*BM + BM - 1 + coff; coff = N - Nq).
+int64_t qtile_ntiles(int64_t N, int64_t coff, int qt, bool causal) {
   const int64_t bm = fa::kMfmaBM, bn = fa::kMfmaBN;
-  const int64_t kv = causal ? std::min(N, (qt + 1) * bm) : N;
-  return (kv + bn - 1) / bn;
+  const int64_t kv = causal ? std::min(N, (qt + 1) * bm + coff) : N;
+  return (std::max<int64_t>(kv, 0) + bn - 1) / bn;
 }
 
 // Cost model of the split plans, in key tiles: the second workgroup on a CU runs its
@@ -250,10 +257,18 @@ double cut_even(int nt, int nch, int64_t u0, int cus, double diag, Plan::Ranges*
 // Cuts every query tile, from the last one, into the fewest equal-cost ranges whose
 // cost is at most `cap`. Returns the number of units, or -1 when a tile would need more
 // than kMaxRanges ranges.
-int64_t cut_ranges(const Plan& pl, int64_t N, int64_t BH, bool causal, int cus, double cap, Plan::Ranges* out) {
+int64_t cut_ranges(const Plan& pl, int64_t N, int64_t coff, int64_t BH, bool causal, int cus, double cap,
+                   Plan::Ranges* out) {
   int64_t u = 0;
   for (int qt = pl.n_qt - 1; qt >= 0; --qt) {
-    const int nt = (int)qtile_ntiles(N, qt, causal);
+    const int nt = (int)qtile_ntiles(N, coff, qt, causal);
+    if (nt == 0) {  // rows that see no key: one unit writes O = 0 and lse = -inf
+      out[qt].nch = 1;
+      out[qt].begin[0] = 0;
+      out[qt].len[0] = 0;
+      u += BH;
+      continue;
+    }
     const double diag = causal ? kDiagonalCost : 0.0;
     int nch = 1;
     while (cut_even(nt, nch, u, cus, diag, &out[qt]) > cap && nch < std::min(nt, fa::kMaxRanges)) ++nch;
@@ -269,13 +284,14 @@ uint32_t pack_unit(int qt, int begin, int len, int64_t bh) {
   return (uint32_t)qt | (uint32_t)begin << 8 | (uint32_t)len << 17 | (uint32_t)bh << 26;
 }
 
-Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask, int cus) {
+Plan make_plan(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t dv, int dtype, int mask, int cus) {
   Plan pl;
   pl.mfma = dtype == FA_BF16;  // d, dv in {64, 128} already checked
   if (!pl.mfma) return pl;
   const bool causal = mask == FA_MASK_CAUSAL;
+  const int64_t coff = N - Nq;
   const int bm = fa::kMfmaBM;
-  pl.n_qt = (int)((N + bm - 1) / bm);
+  pl.n_qt = (int)((Nq + bm - 1) / bm);
   const int64_t BH = B * H;
   const int64_t tiles = BH * pl.n_qt;
   pl.grid = (int)tiles;
@@ -286,15 +302,15 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype
   // hold at once (two workgroups per CU): the smallest cost cap whose cut fits.
   const int64_t target = std::min<int64_t>(fa::kMaxSplitUnits,
                                            env_int("FA_SPLIT_UNITS") > 0 ? env_int("FA_SPLIT_UNITS") : 2 * (int64_t)cus);
-  double lo = 0.5, hi = (double)qtile_ntiles(N, pl.n_qt - 1, causal) * kSecondSlotCost + kDiagonalCost + 1.0;
-  if (cut_ranges(pl, N, BH, causal, cus, hi, pl.ranges) < 0) return pl;
+  double lo = 0.5, hi = (double)qtile_ntiles(N, coff, pl.n_qt - 1, causal) * kSecondSlotCost + kDiagonalCost + 1.0;
+  if (cut_ranges(pl, N, coff, BH, causal, cus, hi, pl.ranges) < 0) return pl;
   for (int it = 0; it < 24; ++it) {
     const double mid = 0.5 * (lo + hi);
-    const int64_t u = cut_ranges(pl, N, BH, causal, cus, mid, pl.ranges);
+    const int64_t u = cut_ranges(pl, N, coff, BH, causal, cus, mid, pl.ranges);
     if (u >= 0 && u <= target) hi = mid;
     else lo = mid;
   }
-  const int64_t units = cut_ranges(pl, N, BH, causal, cus, hi, pl.ranges);
+  const int64_t units = cut_ranges(pl, N, coff, BH, causal, cus, hi, pl.ranges);
   int64_t n_split = 0;
   for (int qt = 0; qt < pl.n_qt; ++qt) n_split += pl.ranges[qt].nch > 1;
   if (n_split == 0) return pl;
@@ -312,18 +328,18 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype
 // The plan of a problem depends only on its shape and the CU count; cutting the ranges
 // of a split plan takes a while on the host, so plans are kept (a bounded map; a
 // caller holds its plan by shared pointer, so clearing the map never frees one in use).
-std::shared_ptr<const Plan> cached_plan(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype,
-                                        int mask, int cus) {
-  using Key = std::array<int64_t, 8>;
+std::shared_ptr<const Plan> cached_plan(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t dv,
+                                        int dtype, int mask, int cus) {
+  using Key = std::array<int64_t, 9>;
   static std::mutex mu;
   static std::map<Key, std::shared_ptr<const Plan>> cache;
-  const Key key{B, H, N, d, dv, dtype, mask, cus};
+  const Key key{B, H, Nq, N, d, dv, dtype, mask, cus};
   {
     std::lock_guard<std::mutex> lk(mu);
     auto it = cache.find(key);
     if (it != cache.end()) return it->second;
   }
-  auto pl = std::make_shared<const Plan>(make_plan(B, H, N, d, dv, dtype, mask, cus));
+  auto pl = std::make_shared<const Plan>(make_plan(B, H, Nq, N, d, dv, dtype, mask, cus));
   std::lock_guard<std::mutex> lk(mu);
   if (cache.size() >= 256) cache.clear();
   cache.emplace(key, pl);
@@ -363,6 +379,8 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
   p.b_sb = s.bias[0]; p.b_sh = s.bias[1]; p.b_si = s.bias[2];
   p.l_sb = s.lse[0]; p.l_sh = s.lse[1];
   p.B = (int)P.B; p.H = (int)P.H; p.N = (int)P.N; p.d = (int)P.d; p.dv = (int)P.dv;
+  p.Nq = (int)P.Nq;
+  p.coff = (int)(P.N - P.Nq);
   p.causal = P.mask == FA_MASK_CAUSAL;
   p.bias_vec4 = P.bias && aligned(P.bias, 16) && s.bias[0] % 4 == 0 && s.bias[1] % 4 == 0 && s.bias[2] % 4 == 0;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.d));
@@ -399,20 +417,20 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
   hipError_t e = pl.mfma ? fa::launch_mfma_bf16(p, grid, split && !in_kernel_merge, stream)
                          : fa::launch_generic(p, P.dtype == FA_BF16, stream);
   if (std::getenv("FA_LOG"))
-    std::fprintf(stderr, "[fa] %s B=%lld H=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d n_qt=%d split=%d grid=%d merge=%d ws=%zu\n",
+    std::fprintf(stderr, "[fa] %s B=%lld H=%lld Nq=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d n_qt=%d split=%d grid=%d merge=%d ws=%zu\n",
                  pl.mfma ? "mfma_bf16" : (P.dtype == FA_BF16 ? "generic_bf16" : "generic_f32"),
-                 (long long)P.B, (long long)P.H, (long long)P.N, (long long)P.d, (long long)P.dv,
+                 (long long)P.B, (long long)P.H, (long long)P.Nq, (long long)P.N, (long long)P.d, (long long)P.dv,
                  p.causal, P.bias != nullptr, pl.n_qt, (int)pl.split, grid, pl.merge_grid, pl.ws_bytes);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 Problem make_problem(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
-                     void* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
+                     void* out, float* lse, int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t dv,
                      const fa_strides* strides, int dtype) {
   Problem P;
   P.q = q; P.k = k; P.v = v; P.bias = bias; P.out = out; P.lse = lse;
-  P.B = B; P.H = H; P.N = N; P.d = d; P.dv = dv; P.mask = mask_mode; P.dtype = dtype;
-  P.st = strides ? *strides : contiguous_strides(H, N, d, dv);
+  P.B = B; P.H = H; P.N = N; P.Nq = Nq; P.d = d; P.dv = dv; P.mask = mask_mode; P.dtype = dtype;
+  P.st = strides ? *strides : contiguous_strides(H, Nq, N, d, dv);
   return P;
 }
 
@@ -672,18 +690,17 @@ int run_bwd(const BwdProblem& P, const BwdPlan& pl, void* ws, hipStream_t stream
 
 extern "C" {
 
-int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
-              void* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
-              const fa_strides* strides, int dtype, void* stream, void* workspace,
-              size_t workspace_bytes) {
-  const Problem P = make_problem(q, k, v, bias, mask_mode, out, lse, B, H, N, d, dv, strides, dtype);
+int fa_fwd_qk_ex(const void* q, const void* k, const void* v, const float* bias, int mask_mode, void* out,
+                 float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv,
+                 const fa_strides* strides, int dtype, void* stream, void* workspace, size_t workspace_bytes) {
+  const Problem P = make_problem(q, k, v, bias, mask_mode, out, lse, B, H, Nq, Nk, d, dv, strides, dtype);
   int st = validate(P);
   if (st != FA_OK) return st;
-  if (B * H * N == 0) return FA_OK;
+  if (B * H * Nq == 0) return FA_OK;
   int dev = 0;
   DevInfo di;
   if ((st = device_info(&dev, &di)) != FA_OK) return st;
-  const std::shared_ptr<const Plan> plan = cached_plan(B, H, N, d, dv, dtype, mask_mode, di.cus);
+  const std::shared_ptr<const Plan> plan = cached_plan(B, H, Nq, Nk, d, dv, dtype, mask_mode, di.cus);
   const Plan& pl = *plan;
   if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes || !aligned(workspace, 256)) return FA_ERR_WORKSPACE;
@@ -691,17 +708,17 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias, in
   return run(P, pl, workspace, static_cast<hipStream_t>(stream));
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
-           void* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
-           const fa_strides* strides, int dtype, void* stream) {
-  const Problem P = make_problem(q, k, v, bias, mask_mode, out, lse, B, H, N, d, dv, strides, dtype);
+int fa_fwd_qk(const void* q, const void* k, const void* v, const float* bias, int mask_mode, void* out,
+              float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv,
+              const fa_strides* strides, int dtype, void* stream) {
+  const Problem P = make_problem(q, k, v, bias, mask_mode, out, lse, B, H, Nq, Nk, d, dv, strides, dtype);
   int st = validate(P);
   if (st != FA_OK) return st;
-  if (B * H * N == 0) return FA_OK;
+  if (B * H * Nq == 0) return FA_OK;
   int dev = 0;
   DevInfo di;
   if ((st = device_info(&dev, &di)) != FA_OK) return st;
-  const std::shared_ptr<const Plan> plan = cached_plan(B, H, N, d, dv, dtype, mask_mode, di.cus);
+  const std::shared_ptr<const Plan> plan = cached_plan(B, H, Nq, Nk, d, dv, dtype, mask_mode, di.cus);
   const Plan& pl = *plan;
   void* ws = nullptr;
   if (pl.ws_bytes > 0) {
@@ -711,14 +728,33 @@ int fa_fwd(const void* q, const void* k, const void* v, const float* bias, int m
   return run(P, pl, ws, static_cast<hipStream_t>(stream));
 }
 
-size_t fa_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype,
-                             int mask_mode) {
-  if (check_shape(B, H, N, d, dv, dtype, mask_mode) != FA_OK) return 0;
-  if (B * H * N == 0) return 0;
+size_t fa_fwd_qk_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, int dtype,
+                                int mask_mode) {
+  if (check_shape_qk(B, H, Nq, Nk, d, dv, dtype, mask_mode) != FA_OK) return 0;
+  if (B * H * Nq == 0) return 0;
   int dev = 0;
   DevInfo di;
   if (device_info(&dev, &di) != FA_OK) return 0;
-  return cached_plan(B, H, N, d, dv, dtype, mask_mode, di.cus)->ws_bytes;
+  return cached_plan(B, H, Nq, Nk, d, dv, dtype, mask_mode, di.cus)->ws_bytes;
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
+              void* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
+              const fa_strides* strides, int dtype, void* stream, void* workspace,
+              size_t workspace_bytes) {
+  return fa_fwd_qk_ex(q, k, v, bias, mask_mode, out, lse, B, H, N, N, d, dv, strides, dtype, stream, workspace,
+                      workspace_bytes);
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
+           void* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
+           const fa_strides* strides, int dtype, void* stream) {
+  return fa_fwd_qk(q, k, v, bias, mask_mode, out, lse, B, H, N, N, d, dv, strides, dtype, stream);
+}
+
+size_t fa_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype,
+                             int mask_mode) {
+  return fa_fwd_qk_workspace_size(B, H, N, N, d, dv, dtype, mask_mode);
 }
 
 const char* fa_status_string(int status) {
@@ -746,7 +782,7 @@ int fa_plan_describe(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int
   if (!info || compute_units < 1) return FA_ERR_NULL;
   const int st = check_shape(B, H, N, d, dv, dtype, mask_mode);
   if (st != FA_OK) return st;
-  const std::shared_ptr<const Plan> plan = cached_plan(B, H, N, d, dv, dtype, mask_mode, compute_units);
+  const std::shared_ptr<const Plan> plan = cached_plan(B, H, N, N, d, dv, dtype, mask_mode, compute_units);
   const Plan& pl = *plan;
   info->split = pl.split ? 1 : 0;
   info->n_qtiles = pl.mfma ? pl.n_qt : 0;

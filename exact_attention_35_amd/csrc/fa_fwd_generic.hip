@@ -54,13 +54,13 @@ __global__ __launch_bounds__(256) void fwd_generic(Params p) {
   const int row = tid / LPR;
   const int sub = tid % LPR;
   // 1-D grid: block = (b*h) * n_qt + query tile
-  const int n_qt = (p.N + BM - 1) / BM;
+  const int n_qt = (p.Nq + BM - 1) / BM;
   const int bh = blockIdx.x / n_qt;
   const int b = bh / p.H;
   const int h = bh % p.H;
   const int q0 = (blockIdx.x % n_qt) * BM;
   const int qi = q0 + row;
-  const bool qvalid = qi < p.N;
+  const bool qvalid = qi < p.Nq;
 
   const T* qp = static_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
   const T* kp = static_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh;
@@ -78,7 +78,8 @@ __global__ __launch_bounds__(256) void fwd_generic(Params p) {
   float m = -INFINITY;  // running max, base-2 units
   float l = 0.f;        // running normaliser
 
-  const int kv_end = p.causal ? min(p.N, q0 + BM) : p.N;
+  // causal: key j is allowed for row i iff j <= i + coff
+  const int kv_end = p.causal ? min(p.N, max(q0 + BM + p.coff, 0)) : p.N;
   for (int kv0 = 0; kv0 < kv_end; kv0 += BK) {
     __syncthreads();  // previous block fully consumed
     for (int idx = tid; idx < BK * D; idx += 256) {
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256) void fwd_generic(Params p) {
       const int key = kv0 + j;
       float x = acc * p.scale_log2;
       if (bp && key < p.N && qvalid) x = fmaf(bp[key], kLog2e, x);
-      if (key >= p.N || (p.causal && key > qi)) x = -INFINITY;
+      if (key >= p.N || (p.causal && key > qi + p.coff)) x = -INFINITY;
       s[j] = x;
       bmax = fmaxf(bmax, x);
     }
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void fwd_generic(Params p) {
 
 template <typename T>
 hipError_t launch_t(const Params& p, hipStream_t stream) {
-  dim3 grid((unsigned)(((p.N + kGenericBM - 1) / kGenericBM) * (int64_t)p.B * p.H));
+  dim3 grid((unsigned)(((p.Nq + kGenericBM - 1) / kGenericBM) * (int64_t)p.B * p.H));
   dim3 block(256);
   if (p.d == 64 && p.dv == 64) hipLaunchKernelGGL((fwd_generic<T, 64, 64>), grid, block, 0, stream, p);
   else if (p.d == 64 && p.dv == 128) hipLaunchKernelGGL((fwd_generic<T, 64, 128>), grid, block, 0, stream, p);

@@ -137,8 +137,8 @@ struct Unit {
 };
 
 __device__ __forceinline__ int qtile_ntiles(const Params& p, int qt, int BM, int BN) {
-  const int kv_len = p.causal ? min(p.N, (qt + 1) * BM) : p.N;
-  return (kv_len + BN - 1) / BN;
+  const int kv_len = p.causal ? min(p.N, (qt + 1) * BM + p.coff) : p.N;
+  return (max(kv_len, 0) + BN - 1) / BN;
 }
 
 // Units of a plan without a split are (b*h, query tile) pairs, longest query tile
@@ -304,7 +304,7 @@ struct MergeItems {
       const float inv = !ok ? __builtin_nanf("") : any ? 1.f / l : 0.f;
 #pragma unroll
       for (int j = 0; j < kMaxRanges; ++j) w_s[j * RG + tid] = ok && !any ? 0.f : w[j] * lp[j] * inv;
-      if (p.lse && qr < p.N)
+      if (p.lse && qr < p.Nq)
         p.lse[b * p.l_sb + h * p.l_sh + qr] =
             !ok ? __builtin_nanf("") : any ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
     }
@@ -315,7 +315,7 @@ struct MergeItems {
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
       const int qr = qt * BM + rg * RG + k * RG1 + rr;
-      if (qr >= p.N) continue;
+      if (qr >= p.Nq) continue;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < kMaxRanges; ++j) {
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(256) void merge_split(Params p) {
   __shared__ float w_s[kMaxRanges * MI::RG];
   const int qt = blockIdx.z;
   // the argument cache lines used below and the tile's table entries in one round trip
-  asm volatile("" ::"s"(p.out), "s"(p.o_sn), "s"(p.N), "s"(p.part_ml), "s"(p.ubase[qt]), "s"((int)p.nchq[qt]));
+  asm volatile("" ::"s"(p.out), "s"(p.o_sn), "s"(p.Nq), "s"(p.part_ml), "s"(p.ubase[qt]), "s"((int)p.nchq[qt]));
   const int nch = p.nchq[qt];
   if (nch == 1) return;  // written directly by the forward kernel
   MI items;
@@ -433,7 +433,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   // ---- Q^T operand: lane holds query (wq0 + l32), dims kk*16 + g*8 .. +8 ----
   const int wq0 = q0 + wave * 32;
   const int qi = wq0 + l32;
-  const bool qvalid = qi < N;
+  const bool qvalid = qi < p.Nq;
+  const int qlim = qi + p.coff;  // causal: this row's last allowed key
   bf16x8 qreg[C::KK];
 #pragma unroll
   for (int kk = 0; kk < C::KK; ++kk)
@@ -441,11 +442,15 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
 
   // bias row of this lane's query (rows past N read row N-1; their results are dropped)
   const float* brow = nullptr;
-  if constexpr (BIAS) brow = p.bias + b * p.b_sb + h * p.b_sh + (int64_t)min(qi, N - 1) * p.b_si;
+  if constexpr (BIAS) brow = p.bias + b * p.b_sb + h * p.b_sh + (int64_t)min(qi, p.Nq - 1) * p.b_si;
 
-  // tiles this wave computes: causal tiles entirely above its rows are skipped
+  // tiles this wave computes: causal tiles entirely above its rows are skipped, and a
+  // wave whose rows all lie past the last query row computes nothing
   const int t_begin = U.t_begin, t_end = U.t_end;
-  const int tw_end = p.causal ? min(t_end, (wq0 + 31) / C::BN + 1) : t_end;
+  const int wlast = wq0 + 31 + p.coff;  // causal: last key the wave's last row may see
+  const int tw_end = wq0 >= p.Nq ? t_begin
+                     : p.causal  ? (wlast < 0 ? t_begin : min(t_end, wlast / C::BN + 1))
+                                 : t_end;
 
   // ---- per-lane operand addresses (bytes within a stage) ----
   // K operand: row kb*32 + l32, logical chunk 2*kk + g, physical chunk
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          if (key >= N || (p.causal && key > qi)) s[kb][r] = -INFINITY;
+          if (key >= N || (p.causal && key > qlim)) s[kb][r] = -INFINITY;
         }
     } else if constexpr (k < Pl::XCH) {
       constexpr int c = (k - Pl::MAX0) & 1, j = (k - Pl::MAX0) >> 1;
@@ -594,7 +599,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          if (key >= N || (p.causal && key > qi)) s[kb][r] = -INFINITY;
+          if (key >= N || (p.causal && key > qlim)) s[kb][r] = -INFINITY;
         }
     }
     static_for<Pl::MAX0, Pl::NOPS>([&](auto K) { sm_step(K, st, s, pk, alpha, seq_plan, kv0); });
@@ -714,7 +719,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     const bool do_qk = t + 1 < tw_end;
     const bool do_sm = t < tw_end;
     const bool do_pv = t > t_begin && t - 1 < tw_end;
-    const bool edge = (kv0 + C::BN > N) || (p.causal && kv0 + C::BN - 1 > wq0);
+    const bool edge = (kv0 + C::BN > N) || (p.causal && kv0 + C::BN - 1 > wq0 + p.coff);
     if (do_pv && __builtin_amdgcn_ballot_w64(alpha_prev != 1.f)) {
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha_prev;

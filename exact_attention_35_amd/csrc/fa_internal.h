@@ -27,7 +27,9 @@ struct Params {
   int64_t o_sb, o_sh, o_sn;
   int64_t b_sb, b_sh, b_si;
   int64_t l_sb, l_sh;
-  int B, H, N, d, dv;
+  int B, H, N, d, dv; // N: keys (rows of K and V)
+  int Nq;             // query rows (rows of Q, O, lse); N_q = N for square problems
+  int coff;           // causal mask: key j allowed for query i iff j <= i + coff (= N - N_q)
   int causal;
   int bias_vec4;      // bias base 16-byte aligned and row stride a multiple of 4
   float scale_log2;   // log2(e) / sqrt(d): scores in base-2 units

@@ -28,18 +28,28 @@ MI355X_PEAK_F32_FLOPS = 157.3e12     # fp32 matrix / vector
 MI355X_HBM_BYTES_PER_S = 8.0e12      # HBM3E
 
 
-def allowed_pairs(N: int, causal: bool) -> int:
-    """Query/key pairs per head that the mask allows (no bias mask counted)."""
-    return N * (N + 1) // 2 if causal else N * N
+def allowed_pairs(N: int, causal: bool, Nq: int = None) -> int:
+    """Query/key pairs per head that the mask allows (no bias mask counted). With Nq
+    query rows against N keys, the causal mask lets row i see keys j <= i + N - Nq."""
+    if Nq is None or Nq == N:
+        return N * (N + 1) // 2 if causal else N * N
+    if not causal:
+        return Nq * N
+    off = N - Nq
+    # row i sees min(N, max(0, i + off + 1)) keys
+    lo = max(0, -off)                 # first row that sees a key
+    hi = min(Nq, N - off)             # rows below hi see fewer than N keys
+    partial = sum(range(lo + off + 1, hi + off + 1)) if hi > lo else 0
+    return partial + max(0, Nq - max(hi, lo)) * N
 
 
-def alg_flops(B, H, N, d, dv, causal, pairs=None) -> int:
+def alg_flops(B, H, N, d, dv, causal, pairs=None, Nq=None) -> int:
     """Algorithmic FLOPs: 2*d per pair for QK^T plus 2*dv per pair for PV.
 
     Softmax arithmetic is not counted. `pairs` overrides the per-head count (e.g. the
-    allowed pairs of a sparse bias mask).
+    allowed pairs of a sparse bias mask); Nq: query rows when they differ from N.
     """
-    p = allowed_pairs(N, causal) if pairs is None else pairs
+    p = allowed_pairs(N, causal, Nq) if pairs is None else pairs
     return 2 * (d + dv) * p * B * H
 
 
@@ -58,12 +68,14 @@ def min_bytes_bwd(B, H, N, d, dv, elem_bytes, bias_bytes=0) -> int:
     return B * H * N * ((2 * d + 3 * dv) * elem_bytes + 4 + (2 * d + dv) * elem_bytes) + bias_bytes
 
 
-def min_bytes(B, H, N, d, dv, elem_bytes, bias_bytes=0, lse_bytes=4) -> int:
+def min_bytes(B, H, N, d, dv, elem_bytes, bias_bytes=0, lse_bytes=4, Nq=None) -> int:
     """Minimum HBM bytes: Q, K, V read once, O written once, lse written once,
-    and an optional bias read once (`bias_bytes` is its total size)."""
-    qkv = B * H * N * (d + d + dv) * elem_bytes
-    o = B * H * N * dv * elem_bytes
-    return qkv + o + B * H * N * lse_bytes + bias_bytes
+    and an optional bias read once (`bias_bytes` is its total size). Nq: query rows
+    (Q, O, lse) when they differ from the N keys (K, V)."""
+    nq = N if Nq is None else Nq
+    qkv = B * H * (nq * d + N * (d + dv)) * elem_bytes
+    o = B * H * nq * dv * elem_bytes
+    return qkv + o + B * H * nq * lse_bytes + bias_bytes
 
 
 def materialised_sp_bytes(B, H, N, sp_elem_bytes=4) -> int:

@@ -19,7 +19,8 @@ The five workloads are the single fp32 head (N=256, d=64), the single bf16 causa
 of length 8192 and width 128 that the traffic accounting on the page
 "AI Infra 第5章图解: 算子与运行时" (section "FlashAttention: Softmax 也能逐块算")
 uses, a batched multi-head causal case in [B, N, H, d] storage, an additive fp32 bias
-with a 10% sparse mask and d != dv, and a long causal sequence with peaked scores.
+with a 10% sparse mask and d != dv, and a long causal sequence with peaked scores; and
+one decoding step (a single query row per head against 8192 cached keys).
 """
 
 from __future__ import annotations
@@ -48,6 +49,11 @@ class Workload:
     v_sigma: float = 1.0
     mask_p: float = 0.0   # probability that an off-diagonal bias entry is -inf
     seed: int = 0
+    Nq: int = 0           # query rows when they differ from the N keys (0: N_q = N)
+
+    @property
+    def n_q(self) -> int:
+        return self.Nq if self.Nq else self.N
 
     def resized(self, **kw) -> "Workload":
         """Same distribution and structure at other sizes (for CPU-sized parity cases)."""
@@ -71,6 +77,10 @@ WORKLOADS = {
         "bf16_causal_long_h8_n32768_d128", B=1, H=8, N=32768, d=128, dv=128,
         dtype="bf16", layout="bhnd", causal=True, bias=False, q_sigma=2.0, k_sigma=2.0,
         seed=35005),
+    # one decoding step against a key/value cache: one query row per (b, h)
+    "bf16_decode_b8_h32_nk8192_d128": Workload(
+        "bf16_decode_b8_h32_nk8192_d128", B=8, H=32, N=8192, d=128, dv=128, dtype="bf16",
+        layout="bhnd", causal=True, bias=False, seed=35006, Nq=1),
 }
 
 # The order the workloads are listed in (small fp32 case first, headline case second).
@@ -93,34 +103,34 @@ def _draw(rng, shape, sigma):
 def make_inputs(w: Workload, device="cpu"):
     """Draw one workload's inputs. Returns a dict of torch tensors.
 
-    q, k: logical [B, H, N, d]; v: logical [B, H, N, dv] — views whose storage follows
-    `w.layout` ([B,N,H,*] storage gives non-contiguous [B,H,N,*] views).
-    bias: None or fp32 [1, H, N, N] (broadcast over B, i.e. batch stride 0).
+    q: logical [B, H, N_q, d]; k: logical [B, H, N, d]; v: logical [B, H, N, dv] — views
+    whose storage follows `w.layout` ([B,N,H,*] storage gives non-contiguous [B,H,N,*]
+    views). bias: None or fp32 [1, H, N_q, N] (broadcast over B, i.e. batch stride 0).
     """
     import torch
 
     rng = np.random.default_rng(w.seed)
     if w.layout == "bhnd":
-        shp = lambda dd: (w.B, w.H, w.N, dd)          # noqa: E731
+        shp = lambda n, dd: (w.B, w.H, n, dd)         # noqa: E731
         to_logical = lambda t: t                      # noqa: E731
     elif w.layout == "bnhd":
-        shp = lambda dd: (w.B, w.N, w.H, dd)          # noqa: E731
+        shp = lambda n, dd: (w.B, n, w.H, dd)         # noqa: E731
         to_logical = lambda t: t.permute(0, 2, 1, 3)  # noqa: E731
     else:
         raise ValueError(w.layout)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
     out = {}
-    for name, dd, sig in (("q", w.d, w.q_sigma), ("k", w.d, w.k_sigma),
-                          ("v", w.dv, w.v_sigma)):
-        t = torch.from_numpy(_draw(rng, shp(dd), sig)).to(tdt)
+    for name, n, dd, sig in (("q", w.n_q, w.d, w.q_sigma), ("k", w.N, w.d, w.k_sigma),
+                             ("v", w.N, w.dv, w.v_sigma)):
+        t = torch.from_numpy(_draw(rng, shp(n, dd), sig)).to(tdt)
         out[name] = to_logical(t.to(device))
     out["bias"] = None
     if w.bias:
-        vals = _draw(rng, (1, w.H, w.N, w.N), 1.0)
+        vals = _draw(rng, (1, w.H, w.n_q, w.N), 1.0)
         if w.mask_p > 0:
-            u = rng.random(size=(1, w.H, w.N, w.N), dtype=np.float32)
+            u = rng.random(size=(1, w.H, w.n_q, w.N), dtype=np.float32)
             kill = u < np.float32(w.mask_p)
-            idx = np.arange(w.N)
+            idx = np.arange(min(w.n_q, w.N))
             kill[:, :, idx, idx] = False
             vals[kill] = -np.inf
         out["bias"] = torch.from_numpy(vals).to(device)

@@ -16,9 +16,15 @@
  * log-sum-exp  lse_i = m_i + ln(l_i) = ln sum_j exp(S_ij)  (natural log).
  *
  * C is the sum of (a) the optional fp32 bias tensor and (b) the causal mask
- * (C_ij = -inf for key j > query i, square N x N, top-left aligned) when
+ * (C_ij = -inf for key j > query i + (N_k - N_q); for the square problems of fa_fwd,
+ * N_q = N_k = N and this is the mask above the diagonal) when
  * mask_mode == FA_MASK_CAUSAL. The scale is 1/sqrt(d) with d the Q/K width, also
  * when d != dv. The bias is added after scaling and is not scaled.
+ *
+ * fa_fwd_qk takes N_q query rows against N_k keys (the pages treat N_q = N_k = N and
+ * fix no causal convention for other lengths; this library aligns the query rows to
+ * the end of the key sequence: query i is position N_k - N_q + i, so a single query
+ * row sees every key, as in decoding against a key/value cache).
  *
  * The page assumes every query row has at least one allowed key. For a row that has
  * none, this library writes O = 0 and lse = -inf (a convention of this library).
@@ -132,6 +138,30 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias, in
               void* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
               const fa_strides* strides, int dtype, void* stream, void* workspace,
               size_t workspace_bytes);
+
+/*
+ * fa_fwd_qk — fa_fwd with N_q query rows against N_k keys (N_q, N_k >= 0).
+ * q: [B, H, N_q, d]; k: [B, H, N_k, d]; v: [B, H, N_k, dv]; out: [B, H, N_q, dv];
+ * lse: NULL or [B, H, N_q]; bias: NULL or fp32 [B, H, N_q, N_k] (strides as fa_strides,
+ * whose n axes are then N_q for q, out, bias rows and lse, and N_k for k and v; NULL
+ * strides mean contiguous tensors of these shapes). Causal mask: key j is allowed for
+ * query i iff j <= i + N_k - N_q; rows with no allowed key (N_q > N_k, or N_k = 0) get
+ * O = 0, lse = -inf. k and v may be NULL when N_k = 0. Otherwise as fa_fwd (which is
+ * fa_fwd_qk with N_q = N_k = N).
+ */
+int fa_fwd_qk(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
+              void* out, float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+              int64_t dv, const fa_strides* strides, int dtype, void* stream);
+
+/* Scratch bytes fa_fwd_qk_ex needs (0 when none, or for invalid arguments). */
+size_t fa_fwd_qk_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                int64_t dv, int dtype, int mask_mode);
+
+/* fa_fwd_qk with caller-provided scratch memory (as fa_fwd_ex); allocates nothing. */
+int fa_fwd_qk_ex(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
+                 void* out, float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                 int64_t dv, const fa_strides* strides, int dtype, void* stream, void* workspace,
+                 size_t workspace_bytes);
 
 /* Static description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -74,7 +74,7 @@ def _row_block(qbh, kbh, vbh, c_rows, rows, causal, scale, allow_empty_rows):
         keys = np.arange(kbh.shape[0])[None, :]
         s = np.where(keys > rows[:, None] + (kbh.shape[0] - n_q), -np.inf, s)
     # m_i = max_j S_ij
-    m = s.max(axis=1)
+    m = s.max(axis=1, initial=-np.inf)  # max over no key at all: -inf (an empty row)
     empty = ~np.isfinite(m) & (m < 0)
     if empty.any() and not allow_empty_rows:
         raise EmptyRowError(f"{int(empty.sum())} query row(s) have no allowed key")

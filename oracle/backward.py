@@ -51,7 +51,7 @@ def _probabilities(qbh, kbh, c_rows, rows, causal, scale, allow_empty_rows):
     if causal:
         keys = np.arange(kbh.shape[0])[None, :]
         s = np.where(keys > rows[:, None], -np.inf, s)
-    m = s.max(axis=1)
+    m = s.max(axis=1, initial=-np.inf)  # max over no key at all: -inf (an empty row)
     empty = ~np.isfinite(m) & (m < 0)
     if empty.any() and not allow_empty_rows:
         raise EmptyRowError(f"{int(empty.sum())} query row(s) have no allowed key")

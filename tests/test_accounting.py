@@ -49,3 +49,14 @@ def test_roofline_bound_two_regimes():
     assert which == "compute" and attain == p and t == pytest.approx(1e12 / p)
     attain, t, which = rf.roofline_bound(1e11, 1e9, p, b)      # I = 100 < ridge
     assert which == "memory" and attain == pytest.approx(b * 100) and t == pytest.approx(1e9 / b)
+
+
+def test_allowed_pairs_of_rectangular_problems_by_counting():
+    # N_q rows against N keys; causal: row i sees keys j <= i + N - N_q
+    from exact_attention_35_amd.roofline import allowed_pairs
+
+    for nq in range(0, 9):
+        for n in range(0, 9):
+            for causal in (False, True):
+                count = sum(1 for i in range(nq) for j in range(n) if not causal or j <= i + n - nq)
+                assert allowed_pairs(n, causal, nq) == count

@@ -170,3 +170,25 @@ def test_python_binding_rejects_bad_tensors():
         capi.fa_fwd(q.transpose(-1, -2).contiguous().transpose(-1, -2), q, q)
     with pytest.raises(capi.FaError):
         capi.fa_fwd(q.half(), q.half(), q.half())
+
+
+def _qk_call(c, Nq, Nk, k=None, v=None):
+    vp = ctypes.c_void_p
+    return capi.lib().fa_fwd_qk(vp(c.q), vp(c.k if k is None else k), vp(c.v if v is None else v), vp(c.bias),
+                                c.mask, vp(c.out), vp(c.lse), c.B, c.H, Nq, Nk, c.d, c.dv, None, c.dtype, vp(0))
+
+
+def test_rectangular_entry_validation():
+    c = Call()
+    assert _qk_call(c, -1, 100) == S["FA_ERR_SHAPE"]
+    assert _qk_call(c, 100, -1) == S["FA_ERR_SHAPE"]
+    assert _qk_call(c, 100, 1 << 31) == S["FA_ERR_SHAPE"]
+    assert _qk_call(c, 100, 50, k=0) == S["FA_ERR_NULL"]
+    # no query rows: nothing to do; no keys: k and v may be NULL (reaches the device check)
+    assert _qk_call(c, 0, 50) == S["FA_OK"]
+    assert _qk_call(c, 10, 0, k=0, v=0) in (S["FA_ERR_DEVICE"], S["FA_OK"])
+    # out over k is caught with the key extent (N_k rows), not the query extent
+    c2 = Call(N=10)
+    c2.out = c2.k + 29440  # inside the 20-row extent of k (30720 bytes), past a 10-row one (28160)
+    assert _qk_call(c2, 10, 20) == S["FA_ERR_ALIAS"]
+    assert capi.lib().fa_fwd_qk_workspace_size(1, 1, 1, 100, 96, 128, capi.FA_BF16, 1) == 0
