@@ -225,7 +225,7 @@ __device__ __forceinline__ BwdUnit bwd_unit(const BwdParams& p, int u, bool kv) 
   w.s_begin = (int)((info >> 8) & 0x1ff);
   w.s_end = w.s_begin + (int)((info >> 17) & 0x1ff);
   w.bh = (int)(info >> 26);
-  w.partial = (kv ? p.nch_kv[w.tile] : p.nch_q[w.tile]) > 1;
+  w.partial = kernarg_byte(kv ? p.nch_kv : p.nch_q, w.tile) > 1;
   return w;
 }
 
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdParams p) {
   const int bh = blockIdx.y;
   const bool kv = (int)blockIdx.z < p.n_tiles;
   const int tile = kv ? blockIdx.z : blockIdx.z - p.n_tiles;
-  const int nch = kv ? p.nch_kv[tile] : p.nch_q[tile];
+  const int nch = kernarg_byte(kv ? p.nch_kv : p.nch_q, tile);
   if (nch <= 1) return;
   const int b = bh / p.H, h = bh % p.H;
   const int W = kv ? D + DV : D;  // floats per row of a slot
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdParams p) {
   const uint8_t* nch_of = kv ? p.nch_kv : p.nch_q;
   const bool rev = !kv && p.causal;
   int before = 0;
-  for (int t = rev ? p.n_tiles - 1 : 0; t != tile; t += rev ? -1 : 1) before += nch_of[t];
+  for (int t = rev ? p.n_tiles - 1 : 0; t != tile; t += rev ? -1 : 1) before += kernarg_byte(nch_of, t);
   const int slot0 = before * p.B * p.H + bh * nch;
   const float* base = p.part + (kv ? 0 : p.part_q_off) + (int64_t)slot0 * 128 * W;
   const int n4 = kReduceRows * W / 4;  // float4 items of the block's rows

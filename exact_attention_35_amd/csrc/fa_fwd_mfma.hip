@@ -254,7 +254,7 @@ struct MergeItems {
 
   __device__ __forceinline__ void init(const Params& p, int qt, int bh, int rg_, int nch) {
     rg = rg_;
-    const int slot0 = p.ubase[qt] + bh * nch;
+    const int slot0 = (int)(p.qtile_info[qt] & 0xffffffu) + bh * nch;
     // slot j holds [BM/32][dv/4][32][4] bf16: row r, chunk c4 at ((r/32)*NC4 + c4)*32 + r%32
     ro = __builtin_amdgcn_make_buffer_rsrc(p.part_o + (int64_t)slot0 * (BM * DV), 0, nch * BM * DV * 2, kBufferWord3);
     rml = __builtin_amdgcn_make_buffer_rsrc(p.part_ml + (int64_t)slot0 * (2 * BM), 0, nch * 2 * BM * 4, kBufferWord3);
@@ -331,9 +331,9 @@ struct MergeItems {
   }
 };
 
-// Merge blocks of the forward kernel itself (blocks n_units on): split query tiles from
-// the last one, then b*h, then groups of rows. The units of the tile publish their
-// partial states by storing this call's number into their flags once the states are
+// Merge blocks of the forward kernel itself (blocks n_units on): the split query tiles
+// (p.split_qt, from the last one), then b*h, then groups of rows. The units of the tile
+// publish their partial states by storing this call's number into their flags once the states are
 // written through to memory; wave 0 polls the flags (one lane per range) with
 // agent-scope loads until all of them hold it. The merge blocks come after every unit
 // in the grid, so a waiting merge block never holds back a unit. The polls are bounded:
@@ -348,9 +348,10 @@ __device__ void merge_block(const Params& p, int m, float* w_s) {
   const int rg = m % groups;
   const int t = m / groups;
   const int bh = t % BH;
-  const int qt = p.n_qt - 1 - t / BH;
-  const int nch = p.nchq[qt];
-  const uint64_t* flag = p.part_flag + p.ubase[qt] + bh * nch;
+  const int qt = kernarg_byte(p.split_qt, (t / BH) % kMaxSplitQTiles);
+  const uint32_t qinfo = p.qtile_info[qt];
+  const int nch = (int)(qinfo >> 24);
+  const uint64_t* flag = p.part_flag + (qinfo & 0xffffffu) + bh * nch;
   int* ready_s = reinterpret_cast<int*>(w_s + kMaxRanges * MI::RG);
   MI items;
   items.init(p, qt, bh, rg, nch);
@@ -385,8 +386,8 @@ __global__ __launch_bounds__(256) void merge_split(Params p) {
   __shared__ float w_s[kMaxRanges * MI::RG];
   const int qt = blockIdx.z;
   // the argument cache lines used below and the tile's table entries in one round trip
-  asm volatile("" ::"s"(p.out), "s"(p.o_sn), "s"(p.Nq), "s"(p.part_ml), "s"(p.ubase[qt]), "s"((int)p.nchq[qt]));
-  const int nch = p.nchq[qt];
+  asm volatile("" ::"s"(p.out), "s"(p.o_sn), "s"(p.Nq), "s"(p.part_ml), "s"(p.qtile_info[qt]));
+  const int nch = (int)(p.qtile_info[qt] >> 24);
   if (nch == 1) return;  // written directly by the forward kernel
   MI items;
   items.init(p, qt, blockIdx.y, blockIdx.x, nch);

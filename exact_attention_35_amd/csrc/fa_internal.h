@@ -47,9 +47,13 @@ struct Params {
   uint64_t seq;
   int n_units;        // forward units (blocks 0 .. n_units-1)
   // Split plans: units enumerate query tiles from the last one; query tile qt owns
-  // units ubase[qt] .. ubase[qt] + B*H*nchq[qt] - 1, nchq[qt] ranges for each (b, h).
-  int32_t ubase[kMaxSplitQTiles + 1];
-  uint8_t nchq[kMaxSplitQTiles];
+  // units ubase .. ubase + B*H*nch - 1, nch ranges for each (b, h), where
+  // qtile_info[qt] = ubase | nch << 24 (one 32-bit word, see kernarg_byte).
+  uint32_t qtile_info[kMaxSplitQTiles];
+  // Split plans: the query tiles cut into more than one range, from the last one (the
+  // merge blocks of the forward kernel take them in this order; which tiles are cut
+  // depends on the cost model, so they need not be the last ones).
+  uint8_t split_qt[kMaxSplitQTiles];
   // Split plans: unit u is query tile (unit_info[u] & 0xff), key tiles from
   // ((>> 8) & 0x1ff), count ((>> 17) & 0x1ff), b*h (>> 26), so a workgroup decodes its
   // unit with one load.
@@ -123,6 +127,16 @@ struct BwdParams {
   uint32_t unit[kMaxBwdUnits];
   uint8_t nch_kv[kMaxBwdTiles], nch_q[kMaxBwdTiles];  // chunks per tile
 };
+
+// Byte i of a byte table in the kernel arguments, read through its aligned 32-bit word.
+// (Indexing such tables directly let this compiler form a scalar load whose base
+// address was the table base plus a byte index, shared with a 32-bit table indexed the
+// same way; scalar loads drop the low two address bits, so that load read the
+// neighbouring entry.)
+__device__ __forceinline__ int kernarg_byte(const uint8_t* table, int i) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(table)[i >> 2];
+  return (int)((w >> (8 * (i & 3))) & 0xffu);
+}
 
 // Kernel arguments are passed by value; keep them within the 4 KiB argument block.
 static_assert(sizeof(Params) <= 4096, "forward kernel arguments exceed 4 KiB");

@@ -62,6 +62,7 @@ SMALL = [
     (3, dict(B=2, H=3, N=555)),
     (4, dict(H=2, N=1500)),
     (4, dict(B=1, H=40, N=300)),
+    (1, dict(H=40, N=900)),   # between one and two query tiles per CU: split too
 ]
 
 

@@ -29,6 +29,7 @@ SHAPES = [  # (B, H, N, d, dv, causal)
     (1, 64, 200, 64, 64, True), (1, 65, 200, 64, 64, True), (1, 1, 1, 64, 64, True),
     (1, 1, 129, 128, 64, True), (3, 5, 1000, 128, 64, False), (1, 8, 3000, 128, 128, True),
     (4, 32, 4096, 128, 128, True), (1, 8, 32768, 128, 128, True), (2, 16, 2048, 64, 128, False),
+    (1, 4, 8192, 128, 128, True), (1, 3, 8192, 64, 64, False),
 ]
 
 
@@ -43,8 +44,9 @@ def test_plan_covers_every_key_tile_once(shape, cus):
     if not info.split:
         assert info.units == BH * n_qt and info.merge_blocks == 0 and info.workspace_bytes == 0
         return
-    # split only where the query tiles leave CUs idle, within the table's limits
-    assert BH * n_qt < cus and BH <= 64 and n_qt <= 256
+    # split only where the query tiles give the CUs fewer than two workgroups each,
+    # within the table's limits
+    assert BH * n_qt < 2 * cus and BH <= 64 and n_qt <= 256
     assert len(table) == info.units <= min(512, 2 * cus)
     ranges, order = {}, []
     for w in table:
