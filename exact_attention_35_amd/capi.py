@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = [
-    "FaError", "FA_OK", "FA_F32", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
+    "FaError", "FA_OK", "FA_F32", "FA_BF16", "FA_F16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
     "STATUS", "lib", "library_path", "fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size",
     "fa_status_string", "fa_version", "fa_shutdown", "fa_plan_describe", "make_strides", "FaStrides",
     "FaPlanInfo", "EXPORTED", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "FaBwdStrides",
@@ -23,6 +23,7 @@ __all__ = [
 FA_OK = 0
 FA_F32 = 0
 FA_BF16 = 1
+FA_F16 = 2
 FA_MASK_NONE = 0
 FA_MASK_CAUSAL = 1
 STATUS = {
@@ -154,6 +155,8 @@ def _dtype_code(t) -> int:
         return FA_BF16
     if t.dtype == torch.float32:
         return FA_F32
+    if t.dtype == torch.float16:
+        return FA_F16
     raise FaError(STATUS["FA_ERR_DTYPE"], f"unsupported dtype {t.dtype}")
 
 

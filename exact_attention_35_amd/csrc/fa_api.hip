@@ -95,12 +95,14 @@ fa_strides contiguous_strides(int64_t H, int64_t Nq, int64_t N, int64_t d, int64
   return s;
 }
 
-bool supported_width(int64_t x) { return x == 64 || x == 128; }
+bool supported_width(int64_t x) { return x >= 1 && x <= 256; }
+bool mfma_width(int64_t x) { return x == 64 || x == 128; }
+int elem_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 
 // Size/shape/dtype/mask checks shared by the size queries and the forward calls
 // (Nq query rows against N keys).
 int check_shape_qk(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t dv, int dtype, int mask) {
-  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
   if (B < 0 || H < 0 || N < 0 || Nq < 0) return FA_ERR_SHAPE;
   if (!supported_width(d) || !supported_width(dv)) return FA_ERR_SHAPE;
@@ -125,21 +127,15 @@ int validate(const Problem& P) {
     for (int i = 0; i < 3; ++i)
       if (all[t][i] < 0) return FA_ERR_STRIDE;
   if (s.lse[0] < 0 || s.lse[1] < 0) return FA_ERR_STRIDE;
-  // the bf16 kernel addresses a 64-row key tile with 32-bit byte offsets
-  if (P.dtype == FA_BF16 && (s.k[2] >= kMaxRowStride || s.v[2] >= kMaxRowStride)) return FA_ERR_STRIDE;
   const int64_t sz[3] = {P.B, P.H, P.Nq};   // q, out, lse, bias rows
   const int64_t szk[3] = {P.B, P.H, P.N};   // k, v
   if (!non_overlapping(sz, s.out, 3, P.dv)) return FA_ERR_STRIDE;
   if (P.lse && !non_overlapping(sz, s.lse, 2, P.Nq)) return FA_ERR_STRIDE;
 
-  const int es = P.dtype == FA_BF16 ? 2 : 4;
+  const int es = elem_size(P.dtype);
   const void* ptrs[4] = {P.q, P.k, P.v, P.out};
-  const int64_t* strd[4] = {s.q, s.k, s.v, s.out};
-  for (int t = 0; t < 4; ++t) {
-    if (!aligned(ptrs[t], 16)) return FA_ERR_ALIGN;
-    for (int i = 0; i < 3; ++i)
-      if ((strd[t][i] * es) % 16 != 0) return FA_ERR_ALIGN;
-  }
+  for (int t = 0; t < 4; ++t)
+    if (!aligned(ptrs[t], es)) return FA_ERR_ALIGN;
   if (P.bias && !aligned(P.bias, 4)) return FA_ERR_ALIGN;
   if (P.lse && !aligned(P.lse, 4)) return FA_ERR_ALIGN;
 
@@ -286,7 +282,7 @@ uint32_t pack_unit(int qt, int begin, int len, int64_t bh) {
 
 Plan make_plan(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t dv, int dtype, int mask, int cus) {
   Plan pl;
-  pl.mfma = dtype == FA_BF16;  // d, dv in {64, 128} already checked
+  pl.mfma = dtype == FA_BF16 && mfma_width(d) && mfma_width(dv);
   if (!pl.mfma) return pl;
   const bool causal = mask == FA_MASK_CAUSAL;
   const int64_t coff = N - Nq;
@@ -370,7 +366,27 @@ uint64_t next_call_number() {
   return next.fetch_add(2, std::memory_order_relaxed);
 }
 
-int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
+// The matrix-core kernel's layout conditions (checked per call; the plan depends on the
+// shape only): 16-byte aligned bases and row strides of q, k, v and out (128-bit loads
+// and stores), and k/v row strides below 2^24 elements (a 64-row tile is addressed
+// with 32-bit byte offsets). Other layouts take the general kernel.
+bool mfma_layout_ok(const Problem& P) {
+  const fa_strides& s = P.st;
+  const void* ptrs[4] = {P.q, P.k, P.v, P.out};
+  const int64_t* strd[4] = {s.q, s.k, s.v, s.out};
+  for (int t = 0; t < 4; ++t) {
+    if (!aligned(ptrs[t], 16)) return false;
+    for (int i = 0; i < 3; ++i)
+      if ((strd[t][i] * 2) % 16 != 0) return false;
+  }
+  return s.k[2] < kMaxRowStride && s.v[2] < kMaxRowStride;
+}
+
+int run(const Problem& P, const Plan& pl_in, void* ws, hipStream_t stream) {
+  // a shape planned for the matrix cores whose layout is not theirs runs on the
+  // general kernel (no split; the workspace is then unused)
+  static const Plan kGenericPlan{};
+  const Plan& pl = pl_in.mfma && !mfma_layout_ok(P) ? kGenericPlan : pl_in;
   Params p{};
   p.q = P.q; p.k = P.k; p.v = P.v; p.bias = P.bias; p.out = P.out; p.lse = P.lse;
   const fa_strides& s = P.st;
@@ -417,10 +433,10 @@ int run(const Problem& P, const Plan& pl, void* ws, hipStream_t stream) {
   }
   const int grid = pl.grid + (in_kernel_merge ? pl.merge_blocks : 0);
   hipError_t e = pl.mfma ? fa::launch_mfma_bf16(p, grid, split && !in_kernel_merge, stream)
-                         : fa::launch_generic(p, P.dtype == FA_BF16, stream);
+                         : fa::launch_generic(p, P.dtype, stream);
   if (std::getenv("FA_LOG"))
     std::fprintf(stderr, "[fa] %s B=%lld H=%lld Nq=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d n_qt=%d split=%d grid=%d merge=%d ws=%zu\n",
-                 pl.mfma ? "mfma_bf16" : (P.dtype == FA_BF16 ? "generic_bf16" : "generic_f32"),
+                 pl.mfma ? "mfma_bf16" : (P.dtype == FA_BF16 ? "generic_bf16" : P.dtype == FA_F16 ? "generic_f16" : "generic_f32"),
                  (long long)P.B, (long long)P.H, (long long)P.Nq, (long long)P.N, (long long)P.d, (long long)P.dv,
                  p.causal, P.bias != nullptr, pl.n_qt, (int)pl.split, grid, pl.merge_grid, pl.ws_bytes);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -495,6 +511,7 @@ int check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int 
   const int st = check_shape(B, H, N, d, dv, dtype, mask);
   if (st != FA_OK) return st;
   if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!mfma_width(d) || !mfma_width(dv)) return FA_ERR_SHAPE;
   // rows of the statistics workspace are indexed with 32-bit integers
   if ((B * H) * bwd_groups(N) * 64 >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
   return FA_OK;
@@ -763,11 +780,11 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "unsupported or invalid shape (d and dv must be 64 or 128)";
+    case FA_ERR_SHAPE: return "unsupported or invalid shape (d and dv: 1..256; gradients: 64 or 128)";
     case FA_ERR_DTYPE: return "unsupported dtype";
     case FA_ERR_MASK: return "unsupported mask mode";
     case FA_ERR_STRIDE: return "negative stride or overlapping output rows";
-    case FA_ERR_ALIGN: return "misaligned pointer or stride";
+    case FA_ERR_ALIGN: return "misaligned pointer";
     case FA_ERR_ALIAS: return "an output overlaps an input or the other output";
     case FA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case FA_ERR_LAUNCH: return "kernel launch failed";

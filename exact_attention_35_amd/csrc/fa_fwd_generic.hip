@@ -1,4 +1,4 @@
-// General attention-forward kernel on the vector ALUs (fp32 and bf16 inputs).
+// General attention-forward kernel on the vector ALUs (fp32, bf16 and fp16 inputs).
 //
 // It applies the online-softmax recurrence of the page "编译器与内核" (Compilers and
 // kernels), section "FlashAttention 围绕 IO 改写算法", one key block at a time: a
@@ -15,8 +15,9 @@
 // Four lanes share one query row: lane `sub` owns the dims sub, sub+4, sub+8, ... of
 // q and of o, so the four lanes of a row read consecutive LDS words (no bank
 // conflict) and every row of the workgroup reads the same key (an LDS broadcast).
-// This kernel serves the fp32 path, where the problem sizes are small; the bf16 fast
-// path runs on the matrix cores (fa_fwd_mfma.hip).
+// This kernel is the general path: fp32, fp16, any width up to 256, and any element-
+// aligned layout; the bf16 fast path (widths 64 and 128, 16-byte aligned rows) runs on
+// the matrix cores (fa_fwd_mfma.hip).
 
 #include "fa_internal.h"
 
@@ -27,19 +28,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <typename T>
-__device__ __forceinline__ float to_f32(T x);
-template <>
-__device__ __forceinline__ float to_f32<float>(float x) { return x; }
-template <>
-__device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return (float)x; }
-
+__device__ __forceinline__ float to_f32(T x) { return (float)x; }  // exact for every T here
 template <typename T>
-__device__ __forceinline__ T from_f32(float x);
-template <>
-__device__ __forceinline__ float from_f32<float>(float x) { return x; }
-template <>
-__device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }  // RNE
+__device__ __forceinline__ T from_f32(float x) { return (T)x; }    // round to nearest even
 
+// D, DV: the widths rounded up to 32, 64, 128 or 256; the actual widths p.d, p.dv mask
+// the loads (dims past them read as 0, which adds nothing to a dot product) and the
+// stores.
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(256) void fwd_generic(Params p) {
   constexpr int BM = kGenericBM;  // query rows per workgroup
@@ -49,6 +44,7 @@ __global__ __launch_bounds__(256) void fwd_generic(Params p) {
   constexpr int DO = DV / LPR;
   __shared__ float Ks[BK][D];
   __shared__ float Vs[BK][DV];
+  const int d = p.d, dv = p.dv;
 
   const int tid = threadIdx.x;
   const int row = tid / LPR;
@@ -70,7 +66,8 @@ __global__ __launch_bounds__(256) void fwd_generic(Params p) {
 
   float qr[DQ];
 #pragma unroll
-  for (int i = 0; i < DQ; ++i) qr[i] = qvalid ? to_f32<T>(qp[(int64_t)qi * p.q_sn + sub + LPR * i]) : 0.f;
+  for (int i = 0; i < DQ; ++i)
+    qr[i] = qvalid && sub + LPR * i < d ? to_f32<T>(qp[(int64_t)qi * p.q_sn + sub + LPR * i]) : 0.f;
 
   float o[DO];
 #pragma unroll
@@ -85,12 +82,12 @@ __global__ __launch_bounds__(256) void fwd_generic(Params p) {
     for (int idx = tid; idx < BK * D; idx += 256) {
       const int r = idx / D, c = idx % D;
       const int key = kv0 + r;
-      Ks[r][c] = key < p.N ? to_f32<T>(kp[(int64_t)key * p.k_sn + c]) : 0.f;
+      Ks[r][c] = key < p.N && c < d ? to_f32<T>(kp[(int64_t)key * p.k_sn + c]) : 0.f;
     }
     for (int idx = tid; idx < BK * DV; idx += 256) {
       const int r = idx / DV, c = idx % DV;
       const int key = kv0 + r;
-      Vs[r][c] = key < p.N ? to_f32<T>(vp[(int64_t)key * p.v_sn + c]) : 0.f;
+      Vs[r][c] = key < p.N && c < dv ? to_f32<T>(vp[(int64_t)key * p.v_sn + c]) : 0.f;
     }
     __syncthreads();
 
@@ -137,29 +134,48 @@ __global__ __launch_bounds__(256) void fwd_generic(Params p) {
   T* op = static_cast<T*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qi * p.o_sn;
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int i = 0; i < DO; ++i) op[sub + LPR * i] = from_f32<T>(o[i] * inv);
+  for (int i = 0; i < DO; ++i)
+    if (sub + LPR * i < dv) op[sub + LPR * i] = from_f32<T>(o[i] * inv);
   if (p.lse && sub == 0) {
     p.lse[b * p.l_sb + h * p.l_sh + qi] =
         l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
   }
 }
 
+// the width bin of x (1 .. 256): 32, 64, 128 or 256
+inline int width_bin(int x) { return x <= 32 ? 32 : x <= 64 ? 64 : x <= 128 ? 128 : 256; }
+
+template <typename T, int D>
+hipError_t launch_dv(const Params& p, dim3 grid, hipStream_t stream) {
+  switch (width_bin(p.dv)) {
+    case 32: hipLaunchKernelGGL((fwd_generic<T, D, 32>), grid, dim3(256), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((fwd_generic<T, D, 64>), grid, dim3(256), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((fwd_generic<T, D, 128>), grid, dim3(256), 0, stream, p); break;
+    default: hipLaunchKernelGGL((fwd_generic<T, D, 256>), grid, dim3(256), 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_t(const Params& p, hipStream_t stream) {
-  dim3 grid((unsigned)(((p.Nq + kGenericBM - 1) / kGenericBM) * (int64_t)p.B * p.H));
-  dim3 block(256);
-  if (p.d == 64 && p.dv == 64) hipLaunchKernelGGL((fwd_generic<T, 64, 64>), grid, block, 0, stream, p);
-  else if (p.d == 64 && p.dv == 128) hipLaunchKernelGGL((fwd_generic<T, 64, 128>), grid, block, 0, stream, p);
-  else if (p.d == 128 && p.dv == 64) hipLaunchKernelGGL((fwd_generic<T, 128, 64>), grid, block, 0, stream, p);
-  else if (p.d == 128 && p.dv == 128) hipLaunchKernelGGL((fwd_generic<T, 128, 128>), grid, block, 0, stream, p);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (p.d < 1 || p.d > 256 || p.dv < 1 || p.dv > 256) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(((p.Nq + kGenericBM - 1) / kGenericBM) * (int64_t)p.B * p.H));
+  switch (width_bin(p.d)) {
+    case 32: return launch_dv<T, 32>(p, grid, stream);
+    case 64: return launch_dv<T, 64>(p, grid, stream);
+    case 128: return launch_dv<T, 128>(p, grid, stream);
+    default: return launch_dv<T, 256>(p, grid, stream);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_generic(const Params& p, bool is_bf16, hipStream_t stream) {
-  return is_bf16 ? launch_t<__bf16>(p, stream) : launch_t<float>(p, stream);
+hipError_t launch_generic(const Params& p, int dtype, hipStream_t stream) {
+  switch (dtype) {
+    case 1: return launch_t<__bf16>(p, stream);
+    case 2: return launch_t<_Float16>(p, stream);
+    default: return launch_t<float>(p, stream);
+  }
 }
 
 }  // namespace fa

@@ -149,7 +149,8 @@ constexpr int kBwdQT = 128;
 // Launchers (each returns the hipError_t of the launch).
 // grid: forward units; merge: whether split query tiles need the merge kernel.
 hipError_t launch_mfma_bf16(const Params& p, int grid, bool merge, hipStream_t stream);
-hipError_t launch_generic(const Params& p, bool is_bf16, hipStream_t stream);
+// dtype: an fa_dtype value (FA_F32, FA_BF16, FA_F16).
+hipError_t launch_generic(const Params& p, int dtype, hipStream_t stream);
 // Gradients dQ, dK, dV (bf16): row statistics, one grid of `grid` dK/dV and dQ units,
 // then (split plans) the reduction of the chunk partials.
 hipError_t launch_bwd_bf16(const BwdParams& p, int grid, hipStream_t stream);

@@ -40,7 +40,7 @@ class Workload:
     N: int
     d: int
     dv: int
-    dtype: str            # "f32" or "bf16": dtype of Q, K, V and O
+    dtype: str            # "f32", "bf16" or "f16": dtype of Q, K, V and O
     layout: str           # "bhnd" (contiguous [B,H,N,*]) or "bnhd" ([B,N,H,*] storage)
     causal: bool
     bias: bool            # fp32 additive bias of shape [1, H, N, N] (broadcast over B)
@@ -118,7 +118,7 @@ def make_inputs(w: Workload, device="cpu"):
         to_logical = lambda t: t.permute(0, 2, 1, 3)  # noqa: E731
     else:
         raise ValueError(w.layout)
-    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
     out = {}
     for name, n, dd, sig in (("q", w.n_q, w.d, w.q_sigma), ("k", w.N, w.d, w.k_sigma),
                              ("v", w.N, w.dv, w.v_sigma)):
@@ -143,6 +143,6 @@ def make_grad_out(w: Workload, device="cpu"):
 
     rng = np.random.default_rng(w.seed + 500000)
     shape = (w.B, w.H, w.N, w.dv) if w.layout == "bhnd" else (w.B, w.N, w.H, w.dv)
-    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
     t = torch.from_numpy(_draw(rng, shape, 1.0)).to(tdt).to(device)
     return t if w.layout == "bhnd" else t.permute(0, 2, 1, 3)

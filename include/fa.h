@@ -29,11 +29,11 @@
  * The page assumes every query row has at least one allowed key. For a row that has
  * none, this library writes O = 0 and lse = -inf (a convention of this library).
  *
- * Numerics: bf16 inputs are multiplied on the matrix cores with fp32 accumulation;
+ * Numerics: bf16 inputs on the matrix cores are multiplied with fp32 accumulation;
  * probabilities are rounded to bf16 for the P V product while the normaliser (and so
  * the log-sum-exp) sums them unrounded in fp32; O is rounded to the output dtype once
- * (round to nearest even).
- * fp32 inputs are computed in fp32 throughout. Results equal the definition up to
+ * (round to nearest even). On the general path (fp32, fp16, other widths or layouts)
+ * every step is fp32 after the exact conversion of the inputs. Results equal the definition up to
  * rounding ("exact" means the same function, not the same bits). For a fixed build,
  * device, shape and input, results are bitwise reproducible from run to run: there are
  * no floating-point atomics and partial results are merged in a fixed order.
@@ -56,12 +56,12 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* q, k, v or out is NULL (with B*H*N > 0), or strides NULL where needed */
-  FA_ERR_SHAPE = -2,     /* negative size, size too large, or (d, dv) not supported */
+  FA_ERR_SHAPE = -2,     /* negative size, size too large, or d, dv outside 1..256 */
   FA_ERR_DTYPE = -3,     /* dtype is not FA_F32 or FA_BF16 */
   FA_ERR_MASK = -4,      /* mask_mode is not FA_MASK_NONE or FA_MASK_CAUSAL */
   FA_ERR_STRIDE = -5,    /* a negative stride, rows of out / lse that overlap, or a bf16
                             k / v row stride of 2^24 elements or more */
-  FA_ERR_ALIGN = -6,     /* a base pointer or row stride not 16-byte aligned (bias: 4-byte) */
+  FA_ERR_ALIGN = -6,     /* a base pointer not aligned to its element size (bias, lse: 4 bytes) */
   FA_ERR_ALIAS = -7,     /* out or lse overlaps an input, or out overlaps lse */
   FA_ERR_WORKSPACE = -8, /* workspace NULL or smaller than fa_fwd_workspace_size() */
   FA_ERR_LAUNCH = -9,    /* the HIP runtime refused the launch */
@@ -69,7 +69,7 @@ typedef enum {
   FA_ERR_ALLOC = -11     /* the library-owned workspace could not be allocated */
 } fa_status;
 
-typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_F16 = 2 } fa_dtype;
 
 typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1 } fa_mask_mode;
 
@@ -96,14 +96,18 @@ typedef struct {
  * out:    device pointer, dtype `dtype`, logical shape [B, H, N, dv]; fully written.
  * lse:    NULL (not written) or a device pointer to fp32 [B, H, N]; fully written.
  * B, H, N: batch, heads, sequence length (>= 0; B*H*N == 0 returns FA_OK at once).
- * d, dv:  Q/K width and V/O width; each must be 64 or 128.
+ * d, dv:  Q/K width and V/O width, each 1..256.
  * strides: element strides of every tensor (see fa_strides); NULL means contiguous
  *         [B, H, N, *] tensors, a contiguous [B, H, N, N] bias and a contiguous lse.
- * dtype:  FA_BF16 (bf16 q, k, v, out; fp32 accumulation) or FA_F32 (all fp32).
+ * dtype:  FA_BF16 (bf16 q, k, v, out; fp32 accumulation), FA_F16 (the same in fp16) or
+ *         FA_F32 (all fp32).
  * stream: a hipStream_t (NULL = the default stream).
  *
- * Alignment: q, k, v, out and every non-zero q/k/v/out stride must be 16-byte
- * aligned in bytes; bias and lse 4-byte aligned.
+ * Alignment: q, k, v and out aligned to their element size; bias and lse 4-byte
+ * aligned. Paths: bf16 with d, dv in {64, 128}, 16-byte aligned q/k/v/out bases and row
+ * strides, and k/v row strides below 2^24 elements runs on the matrix cores; every
+ * other valid call runs on the general (vector ALU) kernel, which computes the same
+ * recurrence in fp32 from the converted inputs.
  * Ownership: all pointers are caller-owned device memory; the library keeps none of
  * them after the call's device work finishes, and never mutates q, k, v or bias.
  * Split problems (few, long query tiles) need a scratch workspace: fa_fwd uses a

@@ -3,6 +3,7 @@
 Tolerances (applied element by element, GPU vs the fp64 oracle on the same inputs):
   * fp32 path: max |dO| <= 1e-5;
   * bf16 inputs with fp32 accumulation: |dO| <= 2e-2 + 1e-2 * |O_ref|;
+  * fp16 inputs (general path): |dO| <= 1e-4 + 2^-10 * |O_ref|;
   * log-sum-exp: |dlse| <= 1e-3; rows whose oracle lse is -inf must be -inf.
 """
 
@@ -12,6 +13,10 @@ F32_ATOL = 1e-5
 BF16_ATOL = 2e-2
 BF16_RTOL = 1e-2
 LSE_ATOL = 1e-3
+# fp16 (general path: fp32 arithmetic, one rounding of O to fp16, whose half-ulp is at
+# most 2^-11 |O|): |dO| <= 1e-4 + 2^-10 |O_ref|, twice the rounding plus an fp32 floor.
+F16_ATOL = 1e-4
+F16_RTOL = 2.0 ** -10
 
 
 def to_np(t):
@@ -25,6 +30,10 @@ def check_out(o_gpu, o_ref, dtype, where=""):
     if dtype == "f32":
         worst = float(err.max()) if err.size else 0.0
         assert worst <= F32_ATOL, f"max |dO| = {worst:.3g} > {F32_ATOL} {where}"
+    elif dtype == "f16":
+        bad = err > F16_ATOL + F16_RTOL * np.abs(o_ref)
+        assert not bad.any(), (f"{int(bad.sum())} elements out of tolerance {where}; "
+                               f"max |dO| = {float(err.max()):.3g}")
     else:
         bound = BF16_ATOL + BF16_RTOL * np.abs(o_ref)
         bad = err > bound

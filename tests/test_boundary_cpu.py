@@ -89,10 +89,10 @@ S = capi.STATUS
 
 
 @pytest.mark.parametrize("mutate,expected", [
-    (lambda c: setattr(c, "dtype", 2), "FA_ERR_DTYPE"),
+    (lambda c: setattr(c, "dtype", 3), "FA_ERR_DTYPE"),
     (lambda c: setattr(c, "mask", 2), "FA_ERR_MASK"),
-    (lambda c: setattr(c, "d", 96), "FA_ERR_SHAPE"),
-    (lambda c: setattr(c, "dv", 32), "FA_ERR_SHAPE"),
+    (lambda c: setattr(c, "d", 257), "FA_ERR_SHAPE"),
+    (lambda c: setattr(c, "dv", 0), "FA_ERR_SHAPE"),
     (lambda c: setattr(c, "B", -1), "FA_ERR_SHAPE"),
     (lambda c: setattr(c, "N", 1 << 31), "FA_ERR_SHAPE"),
     (lambda c: setattr(c, "q", 0), "FA_ERR_NULL"),
@@ -102,10 +102,8 @@ S = capi.STATUS
     (lambda c: c.s.q.__setitem__(2, -128), "FA_ERR_STRIDE"),
     (lambda c: c.s.out.__setitem__(2, 64), "FA_ERR_STRIDE"),       # rows overlap (dv=128)
     (lambda c: c.s.lse.__setitem__(1, 50), "FA_ERR_STRIDE"),       # heads overlap (N=100)
-    (lambda c: c.s.k.__setitem__(2, 1 << 24), "FA_ERR_STRIDE"),    # key tile offsets overflow
-    (lambda c: setattr(c, "q", BASE + 2), "FA_ERR_ALIGN"),
-    (lambda c: setattr(c, "out", c.out + 8), "FA_ERR_ALIGN"),
-    (lambda c: c.s.k.__setitem__(2, 132), "FA_ERR_ALIGN"),         # 264-byte rows
+    (lambda c: setattr(c, "q", BASE + 1), "FA_ERR_ALIGN"),         # not 2-byte aligned (bf16)
+    (lambda c: setattr(c, "out", c.out + 3), "FA_ERR_ALIGN"),
     (lambda c: setattr(c, "lse", c.lse + 2), "FA_ERR_ALIGN"),
     (lambda c: setattr(c, "out", c.q), "FA_ERR_ALIAS"),
     (lambda c: setattr(c, "out", c.v + 256), "FA_ERR_ALIAS"),
@@ -139,17 +137,33 @@ def test_zero_size_is_ok_without_pointers(B, H, N):
     assert c.fwd_ex() == S["FA_OK"]
 
 
-def test_fp32_validation_uses_4_byte_elements():
+def test_alignment_is_per_element_size_and_other_layouts_are_valid():
+    # fp32 needs 4-byte aligned bases; 16-byte alignment, odd widths and fp16 only select
+    # the general kernel (valid arguments reach the device check, which fails without a
+    # gfx950 GPU)
+    ok = (S["FA_ERR_DEVICE"], S["FA_OK"])
     c = Call(dtype=capi.FA_F32, d=64, dv=64)
-    c.s.q[2] = 68          # 272-byte rows: 16-byte aligned for fp32
-    c.s.q[1] = 68 * c.N
-    c.s.q[0] = 68 * c.N * c.H
     c.out = c.q + (1 << 30)
-    # valid arguments reach the device check, which fails without a gfx950 GPU
-    st = c.fwd()
-    assert st in (S["FA_ERR_DEVICE"], S["FA_OK"])
-    c.s.q[2] = 66          # 264-byte rows: not 16-byte aligned
+    c.s.q[2] = 66          # 264-byte rows: not 16-byte aligned, still valid
+    c.s.q[1] = 66 * c.N
+    c.s.q[0] = 66 * c.N * c.H
+    assert c.fwd() in ok
+    c.q += 2               # 2-byte aligned fp32 base: invalid
     assert c.fwd() == S["FA_ERR_ALIGN"]
+    for kw in (dict(d=96), dict(dv=40), dict(d=1, dv=256), dict(dtype=capi.FA_F16)):
+        c = Call(**kw)
+        assert c.fwd() in ok, kw
+    c = Call()
+    c.q += 2               # bf16 base 2-byte aligned: the general kernel takes it
+    assert c.fwd() in ok
+    c = Call()
+    c.s.k[2] = 1 << 24     # a key row stride the matrix-core kernel cannot address
+    c.s.k[1] = c.s.k[2] * c.N
+    c.s.k[0] = c.s.k[1] * c.H
+    c.v = c.k + c.s.k[0] * c.B * 2  # keep v past the strided k
+    c.out = c.v + (1 << 32)
+    c.lse = c.out + (1 << 32)
+    assert c.fwd() in ok
 
 
 def test_workspace_size_invalid_is_zero():
@@ -169,7 +183,7 @@ def test_python_binding_rejects_bad_tensors():
     with pytest.raises(capi.FaError):
         capi.fa_fwd(q.transpose(-1, -2).contiguous().transpose(-1, -2), q, q)
     with pytest.raises(capi.FaError):
-        capi.fa_fwd(q.half(), q.half(), q.half())
+        capi.fa_fwd(q.double(), q.double(), q.double())
 
 
 def _qk_call(c, Nq, Nk, k=None, v=None):

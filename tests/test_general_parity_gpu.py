@@ -1,0 +1,84 @@
+"""GPU parity of the general path: fp16 inputs, widths other than 64 and 128, and layouts
+the matrix-core kernel does not take (bases or row strides not 16-byte aligned), through
+the C ABI against the fp64 oracle on the same seeded inputs."""
+
+import numpy as np
+import pytest
+
+from exact_attention_35_amd import capi, workloads
+from oracle import sdpa_reference
+from parity_util import check_lse, check_out
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, dev, place=None, rect=False):
+    import torch
+
+    inp = workloads.make_inputs(w, device="cpu")
+    g = {n: (None if t is None else t.to(dev)) for n, t in inp.items()}
+    if place:
+        g.update({n: place(g[n]) for n in ("q", "k", "v")})
+    fwd = capi.fa_fwd_qk if rect else capi.fa_fwd
+    out, lse = fwd(g["q"], g["k"], g["v"], bias=g["bias"], causal=w.causal)
+    torch.cuda.synchronize()
+    o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
+    return out, lse, o_ref, l_ref
+
+
+CASES = [  # (dtype, d, dv, N, causal, bias)
+    ("f16", 128, 128, 333, True, False),
+    ("f16", 64, 128, 200, False, True),
+    ("bf16", 96, 96, 300, True, False),
+    ("bf16", 40, 72, 150, False, True),
+    ("bf16", 256, 256, 130, True, False),
+    ("f32", 1, 256, 64, True, False),
+    ("f32", 256, 24, 100, False, True),
+    ("f16", 17, 33, 97, True, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-dv{c[2]}-n{c[3]}" for c in CASES])
+def test_other_dtypes_and_widths(gpu_device, case):
+    dt, d, dv, N, causal, bias = case
+    w = workloads.workload(3).resized(B=1, H=2, N=N, d=d, dv=dv, causal=causal, bias=bias, dtype=dt,
+                                      mask_p=0.1 if bias else 0.0, seed=8000 + d + dv + N)
+    print(f"\n[general] {case}", flush=True)
+    out, lse, o_ref, l_ref = _run(w, gpu_device)
+    check_out(out, o_ref, dt, str(case))
+    check_lse(lse, l_ref, str(case))
+
+
+def _misaligned(t):
+    # the same values in storage that starts one element past a 16-byte boundary
+    import torch
+
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def _padded_rows(t):
+    # rows of d + 4 elements (not a multiple of 16 bytes for bf16 at d = 64)
+    import torch
+
+    B, H, N, d = t.shape
+    buf = torch.zeros(B, H, N, d + 4, dtype=t.dtype, device=t.device)
+    buf[..., :d] = t
+    return buf[..., :d]
+
+
+@pytest.mark.parametrize("place", [_misaligned, _padded_rows], ids=["base+2B", "rows+8B"])
+def test_layouts_outside_the_matrix_core_kernel(gpu_device, place):
+    w = workloads.workload(1).resized(H=2, N=500, d=64, dv=64)
+    out, lse, o_ref, l_ref = _run(w, gpu_device, place=place)
+    check_out(out, o_ref, "bf16", place.__name__)
+    check_lse(lse, l_ref, place.__name__)
+
+
+def test_fp16_rectangular_decode(gpu_device):
+    w = workloads.workload(1).resized(H=3, N=500, Nq=3, dtype="f16")
+    out, lse, o_ref, l_ref = _run(w, gpu_device, rect=True)
+    check_out(out, o_ref, "f16", "decode fp16")
+    check_lse(lse, l_ref, "decode fp16")
