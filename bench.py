@@ -13,6 +13,7 @@ it is launched on), and the CPU oracle timed on this host as a reported baseline
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
   python bench.py --pass bwd [...]  # the gradients (fa_bwd) of the same workload instead
+  python bench.py --tile-sweep      # tile shapes of the general kernel (fp32 experiment)
   python bench.py --copy-probe      # plain copy kernel of known size (counter calibration)
 """
 
@@ -133,6 +134,8 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the gradients of the workload")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="time the general kernel's tile shapes on the fp32 sweep workload")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -146,6 +149,8 @@ def main() -> int:
     if args.copy_probe:
         copy_probe(args.steps)
         return 0
+    if args.tile_sweep:
+        return tile_sweep(args)
 
     from exact_attention_35_amd import capi, roofline as rf, workloads
 
@@ -260,6 +265,44 @@ def main() -> int:
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(res), flush=True)
+    return 0
+
+
+# (FA_GENERIC_TILE value, query rows per workgroup BM, keys per block BK)
+TILES = [(1, 32, 32), (0, 64, 32), (2, 64, 16), (3, 64, 64), (4, 128, 32)]
+
+
+def tile_sweep(args) -> int:
+    """The tile-shape experiment: the general fp32 kernel at each (BM, BK) on one
+    workload; one JSON line per tile with the time per call and the modelled bytes that
+    the workgroups load (every query tile streams all N keys and values once:
+    B*H * ceil(N/BM) * N * (d + dv) * 4 bytes, the pages' N^2 d^2 / M with BM ~ M / d)."""
+    import torch
+
+    from exact_attention_35_amd import capi, roofline as rf, workloads
+
+    w = workloads.WORKLOADS["fp32_tile_sweep_h8_n4096_d64"]
+    dev = torch.device("cuda:0")
+    g = {n: (None if t is None else t.to(dev)) for n, t in workloads.make_inputs(w).items()}
+    for code, bm, bk in TILES:
+        os.environ["FA_GENERIC_TILE"] = str(code)
+        f = lambda: capi.fa_fwd(g["q"], g["k"], g["v"], causal=w.causal)  # noqa: E731
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        kv_bytes = w.B * w.H * (-(-w.N // bm)) * w.N * (w.d + w.dv) * 4
+        flops = rf.alg_flops(w.B, w.H, w.N, w.d, w.dv, w.causal)
+        print(json.dumps({"tile_sweep": w.name, "BM": bm, "BK": bk, "FA_GENERIC_TILE": code,
+                          "us_per_call": us, "TFLOP/s": flops / us / 1e6,
+                          "model_kv_load_bytes": kv_bytes}), flush=True)
+    os.environ.pop("FA_GENERIC_TILE", None)
     return 0
 
 

@@ -401,6 +401,9 @@ int run(const Problem& P, const Plan& pl_in, void* ws, hipStream_t stream) {
   p.coff = (int)(P.N - P.Nq);
   p.causal = P.mask == FA_MASK_CAUSAL;
   p.bias_vec4 = P.bias && aligned(P.bias, 16) && s.bias[0] % 4 == 0 && s.bias[1] % 4 == 0 && s.bias[2] % 4 == 0;
+  // tile shape of the general fp32 kernel for the tile-shape experiment (FA_GENERIC_TILE
+  // 1..4; 0, the default, is 64 rows x 32 keys)
+  p.gtile = env_int("FA_GENERIC_TILE");
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.d));
   p.scale = (float)(1.0 / std::sqrt((double)P.d));
   p.n_qt = pl.n_qt;

@@ -19,6 +19,8 @@
 // aligned layout; the bf16 fast path (widths 64 and 128, 16-byte aligned rows) runs on
 // the matrix cores (fa_fwd_mfma.hip).
 
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -35,10 +37,10 @@ __device__ __forceinline__ T from_f32(float x) { return (T)x; }    // round to n
 // D, DV: the widths rounded up to 32, 64, 128 or 256; the actual widths p.d, p.dv mask
 // the loads (dims past them read as 0, which adds nothing to a dot product) and the
 // stores.
-template <typename T, int D, int DV>
-__global__ __launch_bounds__(256) void fwd_generic(Params p) {
-  constexpr int BM = kGenericBM;  // query rows per workgroup
-  constexpr int BK = 32;          // keys per block
+// BM: query rows per workgroup (4 lanes each, so BM * 4 threads); BK: keys per block.
+template <typename T, int D, int DV, int BM = kGenericBM, int BK = 32>
+__global__ __launch_bounds__(BM * 4) void fwd_generic(Params p) {
+  constexpr int NT = BM * 4;      // threads
   constexpr int LPR = 4;          // lanes per query row
   constexpr int DQ = D / LPR;
   constexpr int DO = DV / LPR;
@@ -79,12 +81,12 @@ __global__ __launch_bounds__(256) void fwd_generic(Params p) {
   const int kv_end = p.causal ? min(p.N, max(q0 + BM + p.coff, 0)) : p.N;
   for (int kv0 = 0; kv0 < kv_end; kv0 += BK) {
     __syncthreads();  // previous block fully consumed
-    for (int idx = tid; idx < BK * D; idx += 256) {
+    for (int idx = tid; idx < BK * D; idx += NT) {
       const int r = idx / D, c = idx % D;
       const int key = kv0 + r;
       Ks[r][c] = key < p.N && c < d ? to_f32<T>(kp[(int64_t)key * p.k_sn + c]) : 0.f;
     }
-    for (int idx = tid; idx < BK * DV; idx += 256) {
+    for (int idx = tid; idx < BK * DV; idx += NT) {
       const int r = idx / DV, c = idx % DV;
       const int key = kv0 + r;
       Vs[r][c] = key < p.N && c < dv ? to_f32<T>(vp[(int64_t)key * p.v_sn + c]) : 0.f;
@@ -156,9 +158,32 @@ hipError_t launch_dv(const Params& p, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Other tile shapes (BM, BK) of the fp32 kernel at widths up to 64 and 128, for the
+// tile-shape experiment: p.gtile 1: (32, 32), 2: (64, 16), 3: (64, 64), 4: (128, 32).
+template <int D, int DV>
+hipError_t launch_tile(const Params& p, hipStream_t stream) {
+  auto grid = [&](int bm) { return dim3((unsigned)(((p.Nq + bm - 1) / bm) * (int64_t)p.B * p.H)); };
+  switch (p.gtile) {
+    case 1: hipLaunchKernelGGL((fwd_generic<float, D, DV, 32, 32>), grid(32), dim3(128), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((fwd_generic<float, D, DV, 64, 16>), grid(64), dim3(256), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((fwd_generic<float, D, DV, 64, 64>), grid(64), dim3(256), 0, stream, p); break;
+    default: hipLaunchKernelGGL((fwd_generic<float, D, DV, 128, 32>), grid(128), dim3(512), 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_t(const Params& p, hipStream_t stream) {
   if (p.d < 1 || p.d > 256 || p.dv < 1 || p.dv > 256) return hipErrorInvalidValue;
+  if constexpr (std::is_same<T, float>::value) {
+    if (p.gtile >= 1 && p.gtile <= 4 && p.d <= 128 && p.dv <= 128) {
+      const int bd = width_bin(p.d) <= 64 ? 64 : 128, bdv = width_bin(p.dv) <= 64 ? 64 : 128;
+      if (bd == 64 && bdv == 64) return launch_tile<64, 64>(p, stream);
+      if (bd == 64) return launch_tile<64, 128>(p, stream);
+      if (bdv == 64) return launch_tile<128, 64>(p, stream);
+      return launch_tile<128, 128>(p, stream);
+    }
+  }
   const dim3 grid((unsigned)(((p.Nq + kGenericBM - 1) / kGenericBM) * (int64_t)p.B * p.H));
   switch (width_bin(p.d)) {
     case 32: return launch_dv<T, 32>(p, grid, stream);

@@ -32,6 +32,7 @@ struct Params {
   int coff;           // causal mask: key j allowed for query i iff j <= i + coff (= N - N_q)
   int causal;
   int bias_vec4;      // bias base 16-byte aligned and row stride a multiple of 4
+  int gtile;          // general fp32 kernel: tile shape of the tile experiment (0: default)
   float scale_log2;   // log2(e) / sqrt(d): scores in base-2 units
   float scale;        // 1 / sqrt(d)
   // Work decomposition. A unit is (batch*head, query tile, range of key tiles).

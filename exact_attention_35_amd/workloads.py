@@ -77,6 +77,11 @@ WORKLOADS = {
         "bf16_causal_long_h8_n32768_d128", B=1, H=8, N=32768, d=128, dv=128,
         dtype="bf16", layout="bhnd", causal=True, bias=False, q_sigma=2.0, k_sigma=2.0,
         seed=35005),
+    # the tile-shape experiment of the general kernel (fp32, no mask: every query tile
+    # streams every key and value once)
+    "fp32_tile_sweep_h8_n4096_d64": Workload(
+        "fp32_tile_sweep_h8_n4096_d64", B=1, H=8, N=4096, d=64, dv=64, dtype="f32",
+        layout="bhnd", causal=False, bias=False, seed=35007),
     # one decoding step against a key/value cache: one query row per (b, h)
     "bf16_decode_b8_h32_nk8192_d128": Workload(
         "bf16_decode_b8_h32_nk8192_d128", B=8, H=32, N=8192, d=128, dv=128, dtype="bf16",

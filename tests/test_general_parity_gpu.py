@@ -82,3 +82,13 @@ def test_fp16_rectangular_decode(gpu_device):
     out, lse, o_ref, l_ref = _run(w, gpu_device, rect=True)
     check_out(out, o_ref, "f16", "decode fp16")
     check_lse(lse, l_ref, "decode fp16")
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+def test_tile_shapes_of_the_experiment(gpu_device, tile, monkeypatch):
+    # every (BM, BK) of the tile-shape experiment computes the same function
+    w = workloads.workload(0).resized(H=2, N=300, causal=True)
+    monkeypatch.setenv("FA_GENERIC_TILE", str(tile))
+    out, lse, o_ref, l_ref = _run(w, gpu_device)
+    check_out(out, o_ref, "f32", f"tile {tile}")
+    check_lse(lse, l_ref, f"tile {tile}")
