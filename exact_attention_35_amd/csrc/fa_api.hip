@@ -39,6 +39,7 @@ namespace {
 using fa::Params;
 
 constexpr int kMaxSplitBH = 64;  // split plans: b*h fits the unit table's 6-bit field
+constexpr int kMaxSplitBH1 = 1 << 14;  // ... and its 14 bits when there is one query tile
 constexpr int64_t kMaxRowStride = 1 << 24;     // bf16 k/v row stride limit (elements)
 
 struct Range {
@@ -275,9 +276,19 @@ int64_t cut_ranges(const Plan& pl, int64_t N, int64_t coff, int64_t BH, bool cau
 }
 
 // One unit table entry: query tile (bits 0-7), first key tile (8-16), key-tile count
-// (17-25), b*h (26-31).
-uint32_t pack_unit(int qt, int begin, int len, int64_t bh) {
-  return (uint32_t)qt | (uint32_t)begin << 8 | (uint32_t)len << 17 | (uint32_t)bh << 26;
+// (17-25), b*h (26-31). Plans with a single query tile put b*h's low 8 bits in bits 0-7.
+uint32_t pack_unit(int qt, int begin, int len, int64_t bh, bool one_qtile) {
+  const uint32_t lo = one_qtile ? (uint32_t)(bh & 0xff) : (uint32_t)qt;
+  const uint32_t hi = one_qtile ? (uint32_t)(bh >> 8) : (uint32_t)bh;
+  return lo | (uint32_t)begin << 8 | (uint32_t)len << 17 | hi << 26;
+}
+
+// Merge blocks per split tile and b*h: the row groups of a query tile that hold query
+// rows (all of them unless the only tile is short, as in decoding).
+int merge_groups_used(int64_t Nq, int n_qt, int64_t dv) {
+  const int groups = fa::merge_groups((int)dv, fa::kFusedMergeItems);
+  const int rows = fa::kMfmaBM / groups;
+  return n_qt == 1 ? (int)std::min<int64_t>(groups, (Nq + rows - 1) / rows) : groups;
 }
 
 Plan make_plan(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t dv, int dtype, int mask, int cus) {
@@ -295,7 +306,9 @@ Plan make_plan(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t d
   // CUs idle; below two, a causal problem's longest tiles set the time: measured
   // 147 -> 84 us for four causal heads of 8192) and the unit table's fields fit
   // (b*h < 64, query tile < 256, key tiles < 512).
-  if (tiles <= 0 || tiles >= 2 * (int64_t)cus || BH > kMaxSplitBH || pl.n_qt > fa::kMaxSplitQTiles) return pl;
+  if (tiles <= 0 || tiles >= 2 * (int64_t)cus || BH > (pl.n_qt == 1 ? kMaxSplitBH1 : kMaxSplitBH) ||
+      pl.n_qt > fa::kMaxSplitQTiles)
+    return pl;
   // Cut the query tiles' key ranges into units of about equal cost, as many as the CUs
   // hold at once (two workgroups per CU): the smallest cost cap whose cut fits.
   const int64_t target = std::min<int64_t>(fa::kMaxSplitUnits,
@@ -315,7 +328,7 @@ Plan make_plan(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t d
   pl.split = true;
   pl.grid = (int)units;
   pl.merge_grid = (int)(tiles * fa::merge_groups((int)dv, 1));
-  pl.merge_blocks = (int)(n_split * BH * fa::merge_groups((int)dv, fa::kFusedMergeItems));
+  pl.merge_blocks = (int)(n_split * BH * merge_groups_used(Nq, pl.n_qt, dv));
   pl.off_flag = 0;
   pl.off_ml = round_up(units * sizeof(uint64_t), 256);
   pl.off_o = round_up(pl.off_ml + units * 2 * bm * sizeof(float), 256);
@@ -417,7 +430,7 @@ int run(const Problem& P, const Plan& pl_in, void* ws, hipStream_t stream) {
       if (r.nch > 1) p.split_qt[n_split++] = (uint8_t)qt;
       for (int64_t bh = 0; bh < P.B * P.H; ++bh)
         for (int c = 0; c < r.nch; ++c)
-          p.unit_info[acc + bh * r.nch + c] = pack_unit(qt, r.begin[c], r.len[c], bh);
+          p.unit_info[acc + bh * r.nch + c] = pack_unit(qt, r.begin[c], r.len[c], bh, pl.n_qt == 1);
       acc += (int32_t)(P.B * P.H * r.nch);
     }
   }
@@ -427,6 +440,7 @@ int run(const Problem& P, const Plan& pl_in, void* ws, hipStream_t stream) {
   const bool split = pl.split;
   const bool in_kernel_merge = split && !stream_capturing(stream) && env_int("FA_MERGE_KERNEL") == 0;
   p.n_units = pl.grid;
+  p.merge_groups = merge_groups_used(P.Nq, pl.n_qt, P.dv);
   p.seq = next_call_number();
   if (pl.ws_bytes > 0) {
     unsigned char* w = static_cast<unsigned char*>(ws);
@@ -819,7 +833,7 @@ int fa_plan_describe(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int
       const Plan::Ranges& r = pl.ranges[qt];
       for (int64_t bh = 0; bh < B * H; ++bh)
         for (int c = 0; c < r.nch; ++c, ++u)
-          if (u < max_units) unit_info[u] = pack_unit(qt, r.begin[c], r.len[c], bh);
+          if (u < max_units) unit_info[u] = pack_unit(qt, r.begin[c], r.len[c], bh, pl.n_qt == 1);
     }
   }
   return FA_OK;

@@ -144,6 +144,7 @@ __device__ __forceinline__ int qtile_ntiles(const Params& p, int qt, int BM, int
 // Units of a plan without a split are (b*h, query tile) pairs, longest query tile
 // first; a split plan reads its unit from the table. The decode is branch-free, so the
 // table entry and the plan type are read from the kernel arguments in one round trip.
+// With a single query tile (decoding) the query-tile bits hold the low 8 bits of b*h.
 __device__ __forceinline__ Unit decode_unit(const Params& p, int u, int BM, int BN) {
   static_assert((kMaxSplitUnits & (kMaxSplitUnits - 1)) == 0, "unit table size must be a power of two");
   const unsigned info = p.unit_info[u & (kMaxSplitUnits - 1)];  // inside the table for any plan
@@ -151,8 +152,9 @@ __device__ __forceinline__ Unit decode_unit(const Params& p, int u, int BM, int 
   const unsigned BH = (unsigned)(p.B * p.H);
   const unsigned r = (unsigned)u / BH;
   Unit w;
-  w.qt = split ? (int)(info & 0xff) : (p.causal ? p.n_qt - 1 - (int)r : (int)r);
-  w.bh = split ? (int)(info >> 26) : (int)((unsigned)u - r * BH);
+  const bool one = p.n_qt == 1;
+  w.qt = split ? (one ? 0 : (int)(info & 0xff)) : (p.causal ? p.n_qt - 1 - (int)r : (int)r);
+  w.bh = split ? (int)(one ? (info & 0xff) | (info >> 26) << 8 : info >> 26) : (int)((unsigned)u - r * BH);
   const int nt = qtile_ntiles(p, w.qt, BM, BN);
   w.t_begin = split ? (int)((info >> 8) & 0x1ff) : 0;
   const int len = split ? (int)((info >> 17) & 0x1ff) : nt;
@@ -343,7 +345,7 @@ constexpr int kMaxMergePolls = 1 << 20;
 template <int DV>
 __device__ void merge_block(const Params& p, int m, float* w_s) {
   using MI = MergeItems<DV, kFusedMergeItems>;
-  constexpr int groups = merge_groups(DV, kFusedMergeItems);
+  const int groups = p.merge_groups;  // groups of rows that hold query rows (<= the tile's)
   const int BH = p.B * p.H;
   const int rg = m % groups;
   const int t = m / groups;
@@ -785,6 +787,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   const __amdgpu_buffer_rsrc_t pml = __builtin_amdgcn_make_buffer_rsrc(
       p.part_ml + (int64_t)U.slot * (2 * C::BM), 0, 2 * C::BM * 4, kBufferWord3);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // a wave whose rows all lie past the last query row stores nothing (no merge reads it)
+  if (wq0 < p.Nq) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -799,6 +803,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   if (g == 0) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref), pml, row * 4, 0, kStoreWriteThrough);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_tot), pml, (C::BM + row) * 4, 0, kStoreWriteThrough);
+  }
   }
   if (p.part_flag) {  // merged by merge blocks of this kernel: publish the state
     __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are complete (written through)

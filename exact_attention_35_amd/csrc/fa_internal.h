@@ -47,6 +47,7 @@ struct Params {
   uint64_t* part_flag;
   uint64_t seq;
   int n_units;        // forward units (blocks 0 .. n_units-1)
+  int merge_groups;   // merge blocks per split tile and b*h (row groups that hold query rows)
   // Split plans: units enumerate query tiles from the last one; query tile qt owns
   // units ubase .. ubase + B*H*nch - 1, nch ranges for each (b, h), where
   // qtile_info[qt] = ubase | nch << 24 (one 32-bit word, see kernarg_byte).
@@ -57,7 +58,8 @@ struct Params {
   uint8_t split_qt[kMaxSplitQTiles];
   // Split plans: unit u is query tile (unit_info[u] & 0xff), key tiles from
   // ((>> 8) & 0x1ff), count ((>> 17) & 0x1ff), b*h (>> 26), so a workgroup decodes its
-  // unit with one load.
+  // unit with one load. With a single query tile, bits 0-7 hold b*h's low 8 bits and
+  // bits 26-31 its next 6 (b*h < 2^14).
   uint32_t unit_info[kMaxSplitUnits];
 };
 

@@ -30,6 +30,7 @@ SHAPES = [  # (B, H, N, d, dv, causal)
     (1, 1, 129, 128, 64, True), (3, 5, 1000, 128, 64, False), (1, 8, 3000, 128, 128, True),
     (4, 32, 4096, 128, 128, True), (1, 8, 32768, 128, 128, True), (2, 16, 2048, 64, 128, False),
     (1, 4, 8192, 128, 128, True), (1, 3, 8192, 64, 64, False),
+    (8, 32, 100, 128, 128, True), (2, 100, 40, 64, 64, False), (1, 300, 128, 128, 64, True),
 ]
 
 
@@ -45,12 +46,14 @@ def test_plan_covers_every_key_tile_once(shape, cus):
         assert info.units == BH * n_qt and info.merge_blocks == 0 and info.workspace_bytes == 0
         return
     # split only where the query tiles give the CUs fewer than two workgroups each,
-    # within the table's limits
-    assert BH * n_qt < 2 * cus and BH <= 64 and n_qt <= 256
+    # within the table's limits (b*h < 64, or < 2^14 with a single query tile)
+    assert BH * n_qt < 2 * cus and (BH <= 64 or n_qt == 1) and n_qt <= 256
     assert len(table) == info.units <= min(512, 2 * cus)
     ranges, order = {}, []
     for w in table:
         qt, t0, n, bh = w & 0xFF, (w >> 8) & 0x1FF, (w >> 17) & 0x1FF, w >> 26
+        if n_qt == 1:  # the query-tile bits hold b*h's low 8 bits
+            qt, bh = 0, (w & 0xFF) | (w >> 26) << 8
         assert n >= 1 and qt < n_qt and bh < BH
         ranges.setdefault((qt, bh), []).append((t0, n))
         order.append(qt)
@@ -67,7 +70,9 @@ def test_plan_covers_every_key_tile_once(shape, cus):
         assert t == ntiles(N, qt, causal)
         n_split += len(cuts[0]) > 1
     assert n_split > 0
-    assert info.merge_blocks == n_split * BH * (128 * dv // (1024 * 2))
+    groups = 128 * dv // (1024 * 2)  # row groups of a query tile
+    used = groups if n_qt > 1 else min(groups, -(-N // (128 // groups)))  # groups holding rows
+    assert info.merge_blocks == n_split * BH * used
     assert info.workspace_bytes >= info.units * (8 + 2 * 128 * 4 + 128 * dv * 2)
 
 

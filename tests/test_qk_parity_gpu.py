@@ -31,6 +31,8 @@ CASES = [  # (N_q, N_k, causal, bias, d, dv, B, H)
     (130, 130, True, False, 128, 128, 1, 1),
     (5, 64, True, True, 128, 128, 1, 3),
     (300, 0, False, False, 128, 128, 1, 1),    # no keys at all
+    (3, 2000, True, False, 128, 128, 4, 40),   # 160 heads of one query tile: wide b*h split
+    (40, 900, True, True, 64, 64, 2, 50),      # a short single tile: merge only its row groups
 ]
 
 
