@@ -293,7 +293,7 @@ int merge_groups_used(int64_t Nq, int n_qt, int64_t dv) {
 
 Plan make_plan(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t dv, int dtype, int mask, int cus) {
   Plan pl;
-  pl.mfma = dtype == FA_BF16 && mfma_width(d) && mfma_width(dv);
+  pl.mfma = (dtype == FA_BF16 || dtype == FA_F16) && mfma_width(d) && mfma_width(dv);
   if (!pl.mfma) return pl;
   const bool causal = mask == FA_MASK_CAUSAL;
   const int64_t coff = N - Nq;
@@ -446,14 +446,15 @@ int run(const Problem& P, const Plan& pl_in, void* ws, hipStream_t stream) {
     unsigned char* w = static_cast<unsigned char*>(ws);
     p.part_flag = in_kernel_merge ? reinterpret_cast<uint64_t*>(w + pl.off_flag) : nullptr;
     p.part_ml = reinterpret_cast<float*>(w + pl.off_ml);
-    p.part_o = reinterpret_cast<__bf16*>(w + pl.off_o);
+    p.part_o = w + pl.off_o;
   }
   const int grid = pl.grid + (in_kernel_merge ? pl.merge_blocks : 0);
-  hipError_t e = pl.mfma ? fa::launch_mfma_bf16(p, grid, split && !in_kernel_merge, stream)
+  hipError_t e = pl.mfma ? fa::launch_mfma(p, grid, split && !in_kernel_merge, P.dtype == FA_F16, stream)
                          : fa::launch_generic(p, P.dtype, stream);
   if (std::getenv("FA_LOG"))
     std::fprintf(stderr, "[fa] %s B=%lld H=%lld Nq=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d n_qt=%d split=%d grid=%d merge=%d ws=%zu\n",
-                 pl.mfma ? "mfma_bf16" : (P.dtype == FA_BF16 ? "generic_bf16" : P.dtype == FA_F16 ? "generic_f16" : "generic_f32"),
+                 pl.mfma ? (P.dtype == FA_F16 ? "mfma_f16" : "mfma_bf16")
+                         : (P.dtype == FA_BF16 ? "generic_bf16" : P.dtype == FA_F16 ? "generic_f16" : "generic_f32"),
                  (long long)P.B, (long long)P.H, (long long)P.Nq, (long long)P.N, (long long)P.d, (long long)P.dv,
                  p.causal, P.bias != nullptr, pl.n_qt, (int)pl.split, grid, pl.merge_grid, pl.ws_bytes);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

@@ -1,4 +1,6 @@
-// bf16 attention forward on the gfx950 matrix cores (MFMA), fp32 accumulation.
+// bf16 and fp16 attention forward on the gfx950 matrix cores (MFMA), fp32 accumulation.
+// (Written for bf16 below; the fp16 kernels are the same template with fp16 operands,
+// v_mfma_f32_32x32x16_f16, fp16 probabilities and fp16 partial outputs.)
 //
 // Method: the online-softmax recurrence of the page "编译器与内核" (Compilers and
 // kernels), section "FlashAttention 围绕 IO 改写算法": a workgroup keeps a tile of
@@ -92,9 +94,10 @@ struct Cfg {
 // tile's first row and whose size covers only the rows that exist, so the per-lane
 // byte offsets do not depend on the tile, and the rows past the sequence end (tail
 // tile only) read as zeros instead of touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const __bf16* base, int64_t sn, int kv0, int N) {
+template <typename E>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const E* base, int64_t sn, int kv0, int N) {
   const int rows = min(kMfmaBN, N - kv0);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(base + (int64_t)kv0 * sn), 0,
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(base + (int64_t)kv0 * sn), 0,
                                            rows * (int)sn * 2, kBufferWord3);
 }
 
@@ -241,8 +244,9 @@ constexpr int kLoadAgentScope = 16;  // buffer load cache policy: sc1
 // The merge items of one thread (IT chunks of 4 dv values, rows RG1 apart) in every
 // range of a split query tile, and the (m_p, l_p) of row rg*RG + tid for tid < RG.
 // Ranges j >= nch keep o = 0, m = -inf, l = 0, so they weigh nothing.
-template <int DV, int IT>
+template <typename E, int DV, int IT>
 struct MergeItems {
+  typedef typename Vec<E>::v4 e4;
   static constexpr int BM = kMfmaBM;
   static constexpr int NC4 = DV / 4;     // chunks of 4 values in a row of o
   static constexpr int RG1 = 256 / NC4;  // rows of one item per thread: 8 (dv = 128) or 16 (dv = 64)
@@ -258,7 +262,7 @@ struct MergeItems {
     rg = rg_;
     const int slot0 = (int)(p.qtile_info[qt] & 0xffffffu) + bh * nch;
     // slot j holds [BM/32][dv/4][32][4] bf16: row r, chunk c4 at ((r/32)*NC4 + c4)*32 + r%32
-    ro = __builtin_amdgcn_make_buffer_rsrc(p.part_o + (int64_t)slot0 * (BM * DV), 0, nch * BM * DV * 2, kBufferWord3);
+    ro = __builtin_amdgcn_make_buffer_rsrc(static_cast<E*>(p.part_o) + (int64_t)slot0 * (BM * DV), 0, nch * BM * DV * 2, kBufferWord3);
     rml = __builtin_amdgcn_make_buffer_rsrc(p.part_ml + (int64_t)slot0 * (2 * BM), 0, nch * 2 * BM * 4, kBufferWord3);
     const int rr = threadIdx.x % RG1, c4 = threadIdx.x / RG1;
 #pragma unroll
@@ -321,14 +325,14 @@ struct MergeItems {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < kMaxRanges; ++j) {
-        const bf16x4 hv = __builtin_bit_cast(bf16x4, raw[k][j]);
+        const e4 hv = __builtin_bit_cast(e4, raw[k][j]);
         acc += w_s[j * RG + k * RG1 + rr] * floatx4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
       }
-      bf16x4 o4;
+      e4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
-      __bf16* orow = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_sn;
-      *reinterpret_cast<bf16x4*>(orow + dv0) = o4;
+      for (int e = 0; e < 4; ++e) o4[e] = (E)acc[e];
+      E* orow = static_cast<E*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_sn;
+      *reinterpret_cast<e4*>(orow + dv0) = o4;
     }
   }
 };
@@ -342,9 +346,9 @@ struct MergeItems {
 // a tile whose ranges never publish gets NaN rows instead of a hang.
 constexpr int kMaxMergePolls = 1 << 20;
 
-template <int DV>
+template <typename E, int DV>
 __device__ void merge_block(const Params& p, int m, float* w_s) {
-  using MI = MergeItems<DV, kFusedMergeItems>;
+  using MI = MergeItems<E, DV, kFusedMergeItems>;
   const int groups = p.merge_groups;  // groups of rows that hold query rows (<= the tile's)
   const int BH = p.B * p.H;
   const int rg = m % groups;
@@ -382,9 +386,9 @@ __device__ void merge_block(const Params& p, int m, float* w_s) {
 
 // Separate merge kernel (used where the forward kernel runs without merge blocks):
 // block = (group of rows, b*h, query tile) = (blockIdx.x, .y, .z).
-template <int DV>
+template <typename E, int DV>
 __global__ __launch_bounds__(256) void merge_split(Params p) {
-  using MI = MergeItems<DV, 1>;
+  using MI = MergeItems<E, DV, 1>;
   __shared__ float w_s[kMaxRanges * MI::RG];
   const int qt = blockIdx.z;
   // the argument cache lines used below and the tile's table entries in one round trip
@@ -399,16 +403,18 @@ __global__ __launch_bounds__(256) void merge_split(Params p) {
   items.combine(p, qt, blockIdx.y, w_s, true);
 }
 
-template <int D, int DV, bool BIAS>
+template <typename E, int D, int DV, bool BIAS>
 __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   using C = Cfg<D, DV>;
+  typedef typename Vec<E>::v8 e8;
+  typedef typename Vec<E>::v4 e4;
   // LDS stages, one array each: the compiler can then tell that a copy into one stage
   // never overlaps operand reads from the other, and does not wait for the copy.
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[C::KTILE], k_lds1[C::KTILE];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[C::VTILE], v_lds1[C::VTILE];
 
   if ((int)blockIdx.x >= p.n_units) {  // merge block (the LDS stages are free for it)
-    merge_block<DV>(p, blockIdx.x - p.n_units, reinterpret_cast<float*>(k_lds0));
+    merge_block<E, DV>(p, blockIdx.x - p.n_units, reinterpret_cast<float*>(k_lds0));
     return;
   }
   const int tid = threadIdx.x;
@@ -429,19 +435,19 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   const int q0 = U.qt * C::BM;
   const int N = p.N;
 
-  const __bf16* qp = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
-  const __bf16* kp = static_cast<const __bf16*>(p.k) + b * p.k_sb + h * p.k_sh;
-  const __bf16* vp = static_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh;
+  const E* qp = static_cast<const E*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const E* kp = static_cast<const E*>(p.k) + b * p.k_sb + h * p.k_sh;
+  const E* vp = static_cast<const E*>(p.v) + b * p.v_sb + h * p.v_sh;
 
   // ---- Q^T operand: lane holds query (wq0 + l32), dims kk*16 + g*8 .. +8 ----
   const int wq0 = q0 + wave * 32;
   const int qi = wq0 + l32;
   const bool qvalid = qi < p.Nq;
   const int qlim = qi + p.coff;  // causal: this row's last allowed key
-  bf16x8 qreg[C::KK];
+  e8 qreg[C::KK];
 #pragma unroll
   for (int kk = 0; kk < C::KK; ++kk)
-    qreg[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_sn + kk * 16 + g * 8) : bf16x8{};
+    qreg[kk] = qvalid ? *reinterpret_cast<const e8*>(qp + (int64_t)qi * p.q_sn + kk * 16 + g * 8) : e8{};
 
   // bias row of this lane's query (rows past N read row N-1; their results are dropped)
   const float* brow = nullptr;
@@ -478,14 +484,14 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   }
   auto vaddr = [&](int sg, int hh, int db) { return (16 * sg + 8 * hh) * (DV * 2) + voff[db]; };
   auto k_operand = [&](const unsigned char* ks, int kk, int kb) {
-    return *reinterpret_cast<const bf16x8*>(ks + kb * 32 * (D * 2) + koff[kk]);
+    return *reinterpret_cast<const e8*>(ks + kb * 32 * (D * 2) + koff[kk]);
   };
   auto v_operand = [&](const unsigned char* vs, int sg, int db) {
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + vaddr(sg, 0, db)));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + vaddr(sg, 1, db)));
-    bf16x8 a;
-    a.lo = __builtin_bit_cast(bf16x4, lo);
-    a.hi = __builtin_bit_cast(bf16x4, hi);
+    e8 a;
+    a.lo = __builtin_bit_cast(e4, lo);
+    a.hi = __builtin_bit_cast(e4, hi);
     return a;
   };
 
@@ -505,7 +511,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(k_operand(ks, kk, kb), qreg[kk], s[kb]);
   };
   // O^T += V^T P^T over the tile's 4 groups of 16 keys; dv blocks innermost.
-  auto pv = [&](const unsigned char* vs, const bf16x8 (&pk)[4]) {
+  auto pv = [&](const unsigned char* vs, const e8 (&pk)[4]) {
 #pragma unroll
     for (int sg = 0; sg < 4; ++sg)
 #pragma unroll
@@ -540,7 +546,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   const float cs = BIAS ? kLog2e : p.scale_log2;
 
   // micro-step k of the softmax of scores s (see SmPlan); writes pk and alpha
-  auto sm_step = [&](auto K, SmState& st, floatx16 (&s)[2], bf16x8 (&pk)[4], float& alpha, auto PlanTag,
+  auto sm_step = [&](auto K, SmState& st, floatx16 (&s)[2], e8 (&pk)[4], float& alpha, auto PlanTag,
                      int kv0) {
     using Pl = typename decltype(PlanTag)::type;
     constexpr int k = decltype(K)::value;
@@ -579,8 +585,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
         st.ps[f & 3] += st.pf[f];
         if constexpr (f & 1) {
           constexpr int r = f % 16;
-          pk[(f / 16) * 2 + r / 8][r % 8 - 1] = (__bf16)st.pf[f - 1];
-          pk[(f / 16) * 2 + r / 8][r % 8] = (__bf16)st.pf[f];
+          pk[(f / 16) * 2 + r / 8][r % 8 - 1] = (E)st.pf[f - 1];
+          pk[(f / 16) * 2 + r / 8][r % 8] = (E)st.pf[f];
         }
       }
     } else {
@@ -592,7 +598,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   // The general softmax runs its steps back to back, so an exponential's result is
   // used 8 steps later (its latency is not hidden behind matrix instructions here).
   const std::common_type<SmPlan<BIAS, false, 8>> seq_plan;
-  auto softmax = [&](floatx16 (&s)[2], bf16x8 (&pk)[4], int kv0, bool edge, float& alpha) {
+  auto softmax = [&](floatx16 (&s)[2], e8 (&pk)[4], int kv0, bool edge, float& alpha) {
     using Pl = SmPlan<BIAS, false, 8>;
     SmState st;
     static_for<0, Pl::MAX0>([&](auto K) { sm_step(K, st, s, pk, alpha, seq_plan, kv0); });
@@ -616,8 +622,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   // Slot i issues one matrix instruction, the LDS operand read of the instruction
   // LA slots ahead, and its share of the softmax micro-steps; sched_barrier keeps
   // the compiler from regrouping them.
-  auto fused = [&](const unsigned char* ks, const unsigned char* vs, floatx16 (&s)[2], bf16x8 (&pc)[4],
-                   const bf16x8 (&pp)[4], float& alpha, int next_kv0) {
+  auto fused = [&](const unsigned char* ks, const unsigned char* vs, floatx16 (&s)[2], e8 (&pc)[4],
+                   const e8 (&pp)[4], float& alpha, int next_kv0) {
     using Pl = SmPlan<BIAS>;
     constexpr int NP = 4 * C::NDB, P2 = NP + C::KK, NS = P2 + C::KK;
     constexpr int LA = 3;  // operand reads run this many slots ahead
@@ -629,12 +635,12 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
       else if constexpr (j < P2) return k_operand(ks, j - NP, 0);
       else return k_operand(ks, j - P2, 1);
     };
-    bf16x8 ring[LA];
+    e8 ring[LA];
     static_for<0, LA>([&](auto J) { ring[J] = operand(J); });
     SmState st;
     static_for<0, NS>([&](auto I) {
       constexpr int i = decltype(I)::value;
-      const bf16x8 a = ring[i % LA];
+      const e8 a = ring[i % LA];
       if constexpr (i + LA < NS) ring[i % LA] = operand(std::integral_constant<int, i + LA>{});
       // The wave's issue priority is raised for the Q K^T half of the body (the two
       // waves of a SIMD belong to different workgroups and drift in phase; measured
@@ -660,7 +666,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   // A wave's last tile (no next scores to form; the causal diagonal tile, or the
   // last tile of its key range): P(t-1) V(t-1) on the matrix cores while the vector
   // ALUs run the softmax of tile t, element masks included when EDGE.
-  auto fused_last = [&](const unsigned char* vs, floatx16 (&s)[2], bf16x8 (&pc)[4], const bf16x8 (&pp)[4],
+  auto fused_last = [&](const unsigned char* vs, floatx16 (&s)[2], e8 (&pc)[4], const e8 (&pp)[4],
                         float& alpha, int kv0, auto EDGEc) {
     constexpr bool EDGE = decltype(EDGEc)::value;
     using Pl = SmPlan<BIAS, EDGE>;
@@ -671,12 +677,12 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
       constexpr int j = decltype(J)::value;
       return v_operand(vs, j / C::NDB, j % C::NDB);
     };
-    bf16x8 ring[LA];
+    e8 ring[LA];
     static_for<0, LA>([&](auto J) { ring[J] = operand(J); });
     SmState st;
     static_for<0, NP>([&](auto I) {
       constexpr int i = decltype(I)::value;
-      const bf16x8 a = ring[i % LA];
+      const e8 a = ring[i % LA];
       if constexpr (i + LA < NP) ring[i % LA] = operand(std::integral_constant<int, i + LA>{});
       oacc[i % C::NDB] = mfma32(a, pp[i / C::NDB], oacc[i % C::NDB]);
       static_for<Pl::first(i, NP, NP, NP), Pl::first(i + 1, NP, NP, NP)>(
@@ -706,7 +712,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   // caller swaps their roles every iteration, so no register copies are needed. o is
   // rescaled by alpha(t-1) before P(t-1) V(t-1) is added.
   float alpha_prev = 1.f;
-  auto step = [&](auto PARc, int t, floatx16 (&s)[2], bf16x8 (&pc)[4], const bf16x8 (&pp)[4]) {
+  auto step = [&](auto PARc, int t, floatx16 (&s)[2], e8 (&pc)[4], const e8 (&pp)[4]) {
     constexpr int PAR = decltype(PARc)::value;
     unsigned char* k_same = PAR ? k_lds1 : k_lds0;   // K(t), refilled with K(t+2)
     unsigned char* k_next = PAR ? k_lds0 : k_lds1;   // K(t+1)
@@ -744,7 +750,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
     alpha_prev = alpha;
   };
   floatx16 s[2];
-  bf16x8 pA[4], pB[4];
+  e8 pA[4], pB[4];
   if (t_begin < tw_end) qk(k_lds0, s);
   if constexpr (BIAS) {
     if (t_begin < tw_end) load_bias(t_begin * C::BN);
@@ -761,16 +767,16 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
 
   if (!U.partial) {
     if (!qvalid) return;
-    __bf16* op = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qi * p.o_sn;
+    E* op = static_cast<E*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qi * p.o_sn;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 o4;
+        e4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][r4 * 4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + db * 32 + r4 * 8 + g * 4) = o4;
+        for (int e = 0; e < 4; ++e) o4[e] = (E)(oacc[db][r4 * 4 + e] * inv);
+        *reinterpret_cast<e4*>(op + db * 32 + r4 * 8 + g * 4) = o4;
       }
     if (p.lse && g == 0)
       p.lse[b * p.l_sb + h * p.l_sh + qi] = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
@@ -783,7 +789,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   // [BM/32][dv/4][32][4]: one wave's 32 rows of 4 dv values are 256 consecutive bytes;
   // m and l stay fp32. ----
   const __amdgpu_buffer_rsrc_t po = __builtin_amdgcn_make_buffer_rsrc(
-      p.part_o + (int64_t)U.slot * (C::BM * DV), 0, C::BM * DV * 2, kBufferWord3);
+      static_cast<E*>(p.part_o) + (int64_t)U.slot * (C::BM * DV), 0, C::BM * DV * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t pml = __builtin_amdgcn_make_buffer_rsrc(
       p.part_ml + (int64_t)U.slot * (2 * C::BM), 0, 2 * C::BM * 4, kBufferWord3);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -794,9 +800,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int c4 = db * 8 + r4 * 2 + g;
-      bf16x4 h4;
+      e4 h4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h4[e] = (__bf16)(oacc[db][r4 * 4 + e] * inv);
+      for (int e = 0; e < 4; ++e) h4[e] = (E)(oacc[db][r4 * 4 + e] * inv);
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), po,
                                             ((wave * (DV / 4) + c4) * 32 + l32) * 8, 0, kStoreWriteThrough);
     }
@@ -815,36 +821,46 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
 // Every variant is instantiated explicitly: the host pass then emits a launch stub
 // for each of them (implicit instantiation through the launch macro alone left all
 // but one of them undefined with this compiler).
-template __global__ void fwd_mfma<64, 64, false>(Params);
-template __global__ void fwd_mfma<64, 64, true>(Params);
-template __global__ void fwd_mfma<64, 128, false>(Params);
-template __global__ void fwd_mfma<64, 128, true>(Params);
-template __global__ void fwd_mfma<128, 64, false>(Params);
-template __global__ void fwd_mfma<128, 64, true>(Params);
-template __global__ void fwd_mfma<128, 128, false>(Params);
-template __global__ void fwd_mfma<128, 128, true>(Params);
+#define FA_FWD_VARIANTS(E)                                   \
+  template __global__ void fwd_mfma<E, 64, 64, false>(Params);  \
+  template __global__ void fwd_mfma<E, 64, 64, true>(Params);   \
+  template __global__ void fwd_mfma<E, 64, 128, false>(Params); \
+  template __global__ void fwd_mfma<E, 64, 128, true>(Params);  \
+  template __global__ void fwd_mfma<E, 128, 64, false>(Params); \
+  template __global__ void fwd_mfma<E, 128, 64, true>(Params);  \
+  template __global__ void fwd_mfma<E, 128, 128, false>(Params);\
+  template __global__ void fwd_mfma<E, 128, 128, true>(Params); \
+  template __global__ void merge_split<E, 64>(Params);          \
+  template __global__ void merge_split<E, 128>(Params);
+FA_FWD_VARIANTS(__bf16)
+FA_FWD_VARIANTS(_Float16)
+#undef FA_FWD_VARIANTS
 
-
-template <int D, int DV>
+template <typename E, int D, int DV>
 hipError_t launch_dd(const Params& p, int grid, bool merge, hipStream_t stream) {
   if (p.bias)
-    hipLaunchKernelGGL((fwd_mfma<D, DV, true>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fwd_mfma<E, D, DV, true>), dim3(grid), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_mfma<D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fwd_mfma<E, D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !merge) return e;
-  hipLaunchKernelGGL((merge_split<DV>), dim3(merge_groups(DV, 1), p.B * p.H, p.n_qt), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((merge_split<E, DV>), dim3(merge_groups(DV, 1), p.B * p.H, p.n_qt), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_e(const Params& p, int grid, bool merge, hipStream_t stream) {
+  if (p.d == 128 && p.dv == 128) return launch_dd<E, 128, 128>(p, grid, merge, stream);
+  if (p.d == 64 && p.dv == 128) return launch_dd<E, 64, 128>(p, grid, merge, stream);
+  if (p.d == 128 && p.dv == 64) return launch_dd<E, 128, 64>(p, grid, merge, stream);
+  if (p.d == 64 && p.dv == 64) return launch_dd<E, 64, 64>(p, grid, merge, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_mfma_bf16(const Params& p, int grid, bool merge, hipStream_t stream) {
-  if (p.d == 128 && p.dv == 128) return launch_dd<128, 128>(p, grid, merge, stream);
-  if (p.d == 64 && p.dv == 128) return launch_dd<64, 128>(p, grid, merge, stream);
-  if (p.d == 128 && p.dv == 64) return launch_dd<128, 64>(p, grid, merge, stream);
-  if (p.d == 64 && p.dv == 64) return launch_dd<64, 64>(p, grid, merge, stream);
-  return hipErrorInvalidValue;
+hipError_t launch_mfma(const Params& p, int grid, bool merge, bool fp16, hipStream_t stream) {
+  return fp16 ? launch_e<_Float16>(p, grid, merge, stream) : launch_e<__bf16>(p, grid, merge, stream);
 }
 
 }  // namespace fa

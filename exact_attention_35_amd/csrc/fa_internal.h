@@ -39,7 +39,7 @@ struct Params {
   int n_qt;           // query tiles per (b, h)
   int split;          // 1: query tiles cut into key ranges (see unit_info), merged afterwards
   // Scratch for split problems: one slot per unit.
-  __bf16* part_o;     // [slot][BM/32][dv/4][32][4] unnormalised numerators (bf16)
+  void* part_o;      // [slot][BM/32][dv/4][32][4] normalised partial outputs (input dtype)
   float* part_ml;     // [slot][2][BM]       reference (base 2) and normaliser
   // Merge inside the forward kernel: blocks n_units .. gridDim.x-1 merge the split query
   // tiles; unit u publishes its partial state by storing `seq` (a number unique to this
@@ -151,7 +151,8 @@ constexpr int kBwdQT = 128;
 
 // Launchers (each returns the hipError_t of the launch).
 // grid: forward units; merge: whether split query tiles need the merge kernel.
-hipError_t launch_mfma_bf16(const Params& p, int grid, bool merge, hipStream_t stream);
+// fp16: fp16 inputs and outputs (else bf16).
+hipError_t launch_mfma(const Params& p, int grid, bool merge, bool fp16, hipStream_t stream);
 // dtype: an fa_dtype value (FA_F32, FA_BF16, FA_F16).
 hipError_t launch_generic(const Params& p, int dtype, hipStream_t stream);
 // Gradients dQ, dK, dV (bf16): row statistics, one grid of `grid` dK/dV and dQ units,

@@ -14,6 +14,13 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+
+// 8- and 4-element vectors of a 16-bit element type (bf16 or fp16).
+template <typename E> struct Vec;
+template <> struct Vec<__bf16> { typedef bf16x8 v8; typedef bf16x4 v4; };
+template <> struct Vec<_Float16> { typedef halfx8 v8; typedef halfx4 v4; };
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format, no swizzle).
@@ -27,6 +34,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 // of lane l is C[8*(r/4) + 4*(l/32) + r%4][l mod 32].
 __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_32x32x16_f16: the same shapes and register layout with fp16 operands.
+__device__ __forceinline__ floatx16 mfma32(halfx8 a, halfx8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Compile-time loop: f(integral_constant<int, I>) for I = I0 .. N-1.

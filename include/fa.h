@@ -29,8 +29,8 @@
  * The page assumes every query row has at least one allowed key. For a row that has
  * none, this library writes O = 0 and lse = -inf (a convention of this library).
  *
- * Numerics: bf16 inputs on the matrix cores are multiplied with fp32 accumulation;
- * probabilities are rounded to bf16 for the P V product while the normaliser (and so
+ * Numerics: bf16 (fp16) inputs on the matrix cores are multiplied with fp32 accumulation;
+ * probabilities are rounded to bf16 (fp16) for the P V product while the normaliser (and so
  * the log-sum-exp) sums them unrounded in fp32; O is rounded to the output dtype once
  * (round to nearest even). On the general path (fp32, fp16, other widths or layouts)
  * every step is fp32 after the exact conversion of the inputs. Results equal the definition up to
@@ -104,8 +104,8 @@ typedef struct {
  * stream: a hipStream_t (NULL = the default stream).
  *
  * Alignment: q, k, v and out aligned to their element size; bias and lse 4-byte
- * aligned. Paths: bf16 with d, dv in {64, 128}, 16-byte aligned q/k/v/out bases and row
- * strides, and k/v row strides below 2^24 elements runs on the matrix cores; every
+ * aligned. Paths: bf16 or fp16 with d, dv in {64, 128}, 16-byte aligned q/k/v/out bases
+ * and row strides, and k/v row strides below 2^24 elements runs on the matrix cores; every
  * other valid call runs on the general (vector ALU) kernel, which computes the same
  * recurrence in fp32 from the converted inputs.
  * Ownership: all pointers are caller-owned device memory; the library keeps none of

@@ -89,10 +89,11 @@ def test_headline_plan_fills_the_chip():
 def test_fp32_and_invalid_plans():
     info, table = capi.fa_plan_describe(1, 1, 256, 64, 64, capi.FA_F32, False, 256)
     assert (info.split, info.n_qtiles, info.units, info.qtile_rows) == (0, 0, 0, 64) and table == []
-    # other widths and fp16 take the general kernel: no matrix-core plan
-    for d, dv, dt in ((96, 64, capi.FA_BF16), (64, 64, capi.FA_F16)):
-        info, table = capi.fa_plan_describe(1, 1, 256, d, dv, dt, False, 256)
-        assert (info.split, info.units, info.qtile_rows) == (0, 0, 64) and table == []
+    # other widths take the general kernel: no matrix-core plan; fp16 at 64/128 has one
+    info, table = capi.fa_plan_describe(1, 1, 256, 96, 64, capi.FA_BF16, False, 256)
+    assert (info.split, info.units, info.qtile_rows) == (0, 0, 64) and table == []
+    info, _ = capi.fa_plan_describe(1, 1, 256, 64, 64, capi.FA_F16, False, 256)
+    assert info.qtile_rows == 128 and info.units >= 2
     with pytest.raises(capi.FaError):
         capi.fa_plan_describe(1, 1, 256, 257, 64, capi.FA_BF16, False, 256)
     with pytest.raises(capi.FaError):
