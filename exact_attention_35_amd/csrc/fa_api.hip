@@ -528,7 +528,7 @@ int64_t bwd_groups(int64_t N) { return (N + fa::kBwdQT - 1) / fa::kBwdQT * 2; }
 int check_bwd_shape(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask) {
   const int st = check_shape(B, H, N, d, dv, dtype, mask);
   if (st != FA_OK) return st;
-  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
   if (!mfma_width(d) || !mfma_width(dv)) return FA_ERR_SHAPE;
   // rows of the statistics workspace are indexed with 32-bit integers
   if ((B * H) * bwd_groups(N) * 64 >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
@@ -715,7 +715,7 @@ int run_bwd(const BwdProblem& P, const BwdPlan& pl, void* ws, hipStream_t stream
     std::copy(pl.nch_kv, pl.nch_kv + fa::kMaxBwdTiles, p.nch_kv);
     std::copy(pl.nch_q, pl.nch_q + fa::kMaxBwdTiles, p.nch_q);
   }
-  const hipError_t e = fa::launch_bwd_bf16(p, pl.units_kv + pl.units_q, stream);
+  const hipError_t e = fa::launch_bwd(p, pl.units_kv + pl.units_q, P.dtype == FA_F16, stream);
   if (env_int("FA_LOG"))
     std::fprintf(stderr, "[fa] bwd B=%lld H=%lld N=%lld d=%lld dv=%lld causal=%d bias=%d split=%d units=%d+%d ws=%zu\n",
                  (long long)P.B, (long long)P.H, (long long)P.N, (long long)P.d, (long long)P.dvw, p.causal,

@@ -1,5 +1,6 @@
-// Gradients of the bf16 attention forward on the gfx950 matrix cores (MFMA), fp32
-// accumulation.
+// Gradients of the bf16 (and fp16) attention forward on the gfx950 matrix cores (MFMA),
+// fp32 accumulation. (Written for bf16 below; the fp16 kernels are the same templates with
+// fp16 operands, v_mfma_f32_32x32x16_f16, and fp16 P, dS and gradients.)
 //
 // The page "编译器与内核" (Compilers and kernels), section "FlashAttention 围绕 IO 改写算法",
 // notes that the backward pass recomputes the score and probability blocks rather
@@ -96,23 +97,31 @@ struct TileCopy2 {
       off[i] = (int)(row * sn * 2) + ((slot % CH) ^ (dual_key(row) & (CH - 1))) * 16;
     }
   }
-  __device__ __forceinline__ void copy(unsigned char* dst, const __bf16* base, int64_t sn, int r0, int N,
-                                       int wave) const {
-    const int rows = min(ROWS, N - r0);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(base + (int64_t)r0 * sn), 0, rows * (int)sn * 2, kBufferWord3);
+  // r: the buffer resource of the tile's rows (rows_rsrc)
+  __device__ __forceinline__ void copy(unsigned char* dst, __amdgpu_buffer_rsrc_t r, int wave) const {
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, dst + (wave * NLD + i) * 1024), 16, off[i], 0, 0, 0);
   }
 };
 
+// Buffer resource over rows r0 .. r0 + ROWS - 1 of a matrix (row stride sn elements) that
+// covers only the rows below N.
+template <int ROWS, typename E>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const E* base, int64_t sn, int r0, int N) {
+  const int rows = min(ROWS, N - r0);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(base + (int64_t)r0 * sn), 0, rows * (int)sn * 2,
+                                           kBufferWord3);
+}
+
 // Operand reads from a dual-swizzled LDS tile of W bf16 per row. A read's byte offset
 // within the tile is a per-lane base XOR a compile-time constant (the swizzled chunk
 // index is an XOR, and the fields it touches are disjoint from the row's), so one
 // register per kind of read serves every k-step and column block.
-template <int W>
+template <typename E, int W>
 struct TileReads {
+  typedef typename Vec<E>::v8 e8;
+  typedef typename Vec<E>::v4 e4;
   static constexpr int CH = W / 8;
   int rbase;     // row-wise read: row l32 (+32*blk), logical chunk 2*kk + g -> rbase ^ 32*kk
   int tbase[2];  // transposing read, half hh: column block db -> tbase[hh] ^ 64*db
@@ -134,25 +143,25 @@ struct TileReads {
     }
   }
   // A or B operand: row 32*blk + (lane mod 32), k = 16*kk + 8*g .. +7
-  __device__ __forceinline__ bf16x8 row(const unsigned char* t, int blk, int kk) const {
-    return *reinterpret_cast<const bf16x8*>(t + blk * 32 * (W * 2) + (rbase ^ (32 * kk)));
+  __device__ __forceinline__ e8 row(const unsigned char* t, int blk, int kk) const {
+    return *reinterpret_cast<const e8*>(t + blk * 32 * (W * 2) + (rbase ^ (32 * kk)));
   }
   // A operand of a product over the tile's rows: column 32*db + (lane mod 32), with k
   // running over the 16 rows of group sg in the order the accumulator layout holds them.
-  __device__ __forceinline__ bf16x8 tr(const unsigned char* t, int sg, int db) const {
+  __device__ __forceinline__ e8 tr(const unsigned char* t, int sg, int db) const {
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         LDS_PTR(i16x4, t + 16 * sg * (W * 2) + (tbase[0] ^ (64 * db))));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         LDS_PTR(i16x4, t + 16 * sg * (W * 2) + (tbase[1] ^ (64 * db))));
-    bf16x8 a;
-    a.lo = __builtin_bit_cast(bf16x4, lo);
-    a.hi = __builtin_bit_cast(bf16x4, hi);
+    e8 a;
+    a.lo = __builtin_bit_cast(e4, lo);
+    a.hi = __builtin_bit_cast(e4, hi);
     return a;
   }
 };
 
 // Row statistics: 16 threads per row. rowstat group layout: see BwdParams.
-template <int DV>
+template <typename E, int DV>
 __global__ __launch_bounds__(256) void bwd_rowstat(BwdParams p) {
   constexpr int EL = DV / 16;  // elements per thread
   const int row = blockIdx.x * 16 + threadIdx.x / 16;
@@ -162,9 +171,9 @@ __global__ __launch_bounds__(256) void bwd_rowstat(BwdParams p) {
   const int b = bh / p.H, h = bh % p.H;
   float acc = 0.f;
   if (i < p.N) {
-    const __bf16* o = static_cast<const __bf16*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_sn + part * EL;
-    const __bf16* g = static_cast<const __bf16*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)i * p.do_sn + part * EL;
-    typedef __bf16 vec_t __attribute__((ext_vector_type(EL)));
+    const E* o = static_cast<const E*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_sn + part * EL;
+    const E* g = static_cast<const E*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)i * p.do_sn + part * EL;
+    typedef E vec_t __attribute__((ext_vector_type(EL)));
     const vec_t ov = *reinterpret_cast<const vec_t*>(o);
     const vec_t gv = *reinterpret_cast<const vec_t*>(g);
 #pragma unroll
@@ -230,9 +239,11 @@ __device__ __forceinline__ BwdUnit bwd_unit(const BwdParams& p, int u, bool kv) 
 }
 
 // ---- dK, dV of 128 keys of one (b, h) ----
-template <int D, int DV, bool BIAS>
+template <typename E, int D, int DV, bool BIAS>
 __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsigned char* st1) {
   using C = BwdCfg<D, DV>;
+  typedef typename Vec<E>::v8 e8;
+  typedef typename Vec<E>::v4 e4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const BwdUnit U = bwd_unit(p, blk, true);
@@ -244,20 +255,20 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
   const int key = wk0 + l32;  // this lane's key
   const bool kvalid = key < N;
 
-  const __bf16* qp = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
-  const __bf16* gp = static_cast<const __bf16*>(p.dout) + b * p.do_sb + h * p.do_sh;
-  const __bf16* kp = static_cast<const __bf16*>(p.k) + b * p.k_sb + h * p.k_sh;
-  const __bf16* vp = static_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh;
+  const E* qp = static_cast<const E*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const E* gp = static_cast<const E*>(p.dout) + b * p.do_sb + h * p.do_sh;
+  const E* kp = static_cast<const E*>(p.k) + b * p.k_sb + h * p.k_sh;
+  const E* vp = static_cast<const E*>(p.v) + b * p.v_sb + h * p.v_sh;
   const float* stat = p.rowstat + (int64_t)bh * p.n_grp * 128;
 
   // K^T and V^T as B operands: lane holds its key, dims 16*kk + 8*g .. +7
-  bf16x8 kreg[D / 16], vreg[DV / 16];
+  e8 kreg[D / 16], vreg[DV / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    kreg[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(kp + (int64_t)key * p.k_sn + kk * 16 + g * 8) : bf16x8{};
+    kreg[kk] = kvalid ? *reinterpret_cast<const e8*>(kp + (int64_t)key * p.k_sn + kk * 16 + g * 8) : e8{};
 #pragma unroll
   for (int kk = 0; kk < DV / 16; ++kk)
-    vreg[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(vp + (int64_t)key * p.v_sn + kk * 16 + g * 8) : bf16x8{};
+    vreg[kk] = kvalid ? *reinterpret_cast<const e8*>(vp + (int64_t)key * p.v_sn + kk * 16 + g * 8) : e8{};
 
   const float* bcol = nullptr;  // bias column of this lane's key (rows added per element)
   if constexpr (BIAS) bcol = p.bias + b * p.b_sb + h * p.b_sh + min(key, N - 1);
@@ -266,8 +277,8 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
   TileCopy2<DV, C::QS> gcp;
   qcp.init(p.q_sn, wave, lane);
   gcp.init(p.do_sn, wave, lane);
-  TileReads<D> qr;
-  TileReads<DV> gr;
+  TileReads<E, D> qr;
+  TileReads<E, DV> gr;
   qr.init(lane);
   gr.init(lane);
 
@@ -276,8 +287,8 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
   const int qs0 = (p.causal ? (k0 / C::QS) * C::QS : 0) + U.s_begin * C::QS;
   const int nsteps = U.s_end - U.s_begin;
   auto copy_step = [&](unsigned char* st, int qs) {
-    qcp.copy(st, qp, p.q_sn, qs, N, wave);
-    gcp.copy(st + C::QTILE, gp, p.do_sn, qs, N, wave);
+    qcp.copy(st, rows_rsrc<C::QS>(qp, p.q_sn, qs, N), wave);
+    gcp.copy(st + C::QTILE, rows_rsrc<C::QS>(gp, p.do_sn, qs, N), wave);
     if (wave == 0 && lane < 32) {  // the step's 64 lse and 64 D values: one 512-byte group
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(stat + (qs / 64) * 128), 0, 512, kBufferWord3);
@@ -331,7 +342,7 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
       for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(qr.row(qt_, qb, kk), kreg[kk], sacc);
 #pragma unroll
       for (int kk = 0; kk < DV / 16; ++kk) dpacc = mfma32(gr.row(gt_, qb, kk), vreg[kk], dpacc);
-      bf16x8 pk[2], dsk[2];
+      e8 pk[2], dsk[2];
       // P and dS of the block. Causal mask: key > row, i.e. kd > 8*(r/4) + r%4 with
       // kd = key - qb0 - 4g; it never fires on blocks below the diagonal, and kd is made
       // the smallest int without a causal mask.
@@ -341,8 +352,8 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
         // base-2 exponent of P: sqrt(d) (S - lse) * log2(e) / sqrt(d)
         float pr = __builtin_amdgcn_exp2f(sacc[r] * p.scale_log2);
         pr = kd > 8 * (r >> 2) + (r & 3) ? 0.f : pr;
-        pk[r >> 3][r & 7] = (__bf16)pr;
-        dsk[r >> 3][r & 7] = (__bf16)(pr * dpacc[r]);
+        pk[r >> 3][r & 7] = (E)pr;
+        dsk[r >> 3][r & 7] = (E)(pr * dpacc[r]);
       }
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
@@ -372,32 +383,34 @@ __device__ void dkdv_block(const BwdParams& p, int blk, unsigned char* st0, unsi
             floatx4{dvacc[db][r4 * 4], dvacc[db][r4 * 4 + 1], dvacc[db][r4 * 4 + 2], dvacc[db][r4 * 4 + 3]};
     return;
   }
-  __bf16* dkp = static_cast<__bf16*>(p.grad_k) + b * p.dk_sb + h * p.dk_sh + (int64_t)key * p.dk_sn;
-  __bf16* dvp = static_cast<__bf16*>(p.grad_v) + b * p.dv_sb + h * p.dv_sh + (int64_t)key * p.dv_sn;
+  E* dkp = static_cast<E*>(p.grad_k) + b * p.dk_sb + h * p.dk_sh + (int64_t)key * p.dk_sn;
+  E* dvp = static_cast<E*>(p.grad_v) + b * p.dv_sb + h * p.dv_sh + (int64_t)key * p.dv_sn;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      bf16x4 o4;
+      e4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(dkacc[db][r4 * 4 + e] * p.scale);
-      *reinterpret_cast<bf16x4*>(dkp + db * 32 + r4 * 8 + g * 4) = o4;
+      for (int e = 0; e < 4; ++e) o4[e] = (E)(dkacc[db][r4 * 4 + e] * p.scale);
+      *reinterpret_cast<e4*>(dkp + db * 32 + r4 * 8 + g * 4) = o4;
     }
 #pragma unroll
   for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      bf16x4 o4;
+      e4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)dvacc[db][r4 * 4 + e];
-      *reinterpret_cast<bf16x4*>(dvp + db * 32 + r4 * 8 + g * 4) = o4;
+      for (int e = 0; e < 4; ++e) o4[e] = (E)dvacc[db][r4 * 4 + e];
+      *reinterpret_cast<e4*>(dvp + db * 32 + r4 * 8 + g * 4) = o4;
     }
 }
 
 // ---- dQ of 128 query rows of one (b, h) ----
-template <int D, int DV, bool BIAS>
+template <typename E, int D, int DV, bool BIAS>
 __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsigned char* st1) {
   using C = BwdCfg<D, DV>;
+  typedef typename Vec<E>::v8 e8;
+  typedef typename Vec<E>::v4 e4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const BwdUnit U = bwd_unit(p, blk, false);
@@ -408,19 +421,19 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
   const int qi = wq0 + l32;  // this lane's query row
   const bool qvalid = qi < N;
 
-  const __bf16* qp = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
-  const __bf16* gp = static_cast<const __bf16*>(p.dout) + b * p.do_sb + h * p.do_sh;
-  const __bf16* kp = static_cast<const __bf16*>(p.k) + b * p.k_sb + h * p.k_sh;
-  const __bf16* vp = static_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh;
+  const E* qp = static_cast<const E*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const E* gp = static_cast<const E*>(p.dout) + b * p.do_sb + h * p.do_sh;
+  const E* kp = static_cast<const E*>(p.k) + b * p.k_sb + h * p.k_sh;
+  const E* vp = static_cast<const E*>(p.v) + b * p.v_sb + h * p.v_sh;
 
   // Q^T and dO^T as B operands: lane holds its row, dims 16*kk + 8*g .. +7
-  bf16x8 qreg[D / 16], greg[DV / 16];
+  e8 qreg[D / 16], greg[DV / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    qreg[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_sn + kk * 16 + g * 8) : bf16x8{};
+    qreg[kk] = qvalid ? *reinterpret_cast<const e8*>(qp + (int64_t)qi * p.q_sn + kk * 16 + g * 8) : e8{};
 #pragma unroll
   for (int kk = 0; kk < DV / 16; ++kk)
-    greg[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(gp + (int64_t)qi * p.do_sn + kk * 16 + g * 8) : bf16x8{};
+    greg[kk] = qvalid ? *reinterpret_cast<const e8*>(gp + (int64_t)qi * p.do_sn + kk * 16 + g * 8) : e8{};
   const int qc = min(qi, N - 1);
   const float* grp = p.rowstat + ((int64_t)bh * p.n_grp + qc / 64) * 128;
   // base-2 exponent of P: (sqrt(d) (Q K^T/sqrt(d) + C) - lse sqrt(d)) log2(e)/sqrt(d)
@@ -433,8 +446,8 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
   TileCopy2<DV, C::KS> vcp;
   kcp.init(p.k_sn, wave, lane);
   vcp.init(p.v_sn, wave, lane);
-  TileReads<D> kr;
-  TileReads<DV> vr;
+  TileReads<E, D> kr;
+  TileReads<E, DV> vr;
   kr.init(lane);
   vr.init(lane);
 
@@ -442,8 +455,8 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
   const int t_begin = U.s_begin, t_end = U.s_end;
   const int tw_end = p.causal ? min(t_end, (wq0 + 31) / C::KS + 1) : t_end;
   auto copy_step = [&](unsigned char* st, int t) {
-    kcp.copy(st, kp, p.k_sn, t * C::KS, N, wave);
-    vcp.copy(st + C::KTILE, vp, p.v_sn, t * C::KS, N, wave);
+    kcp.copy(st, rows_rsrc<C::KS>(kp, p.k_sn, t * C::KS, N), wave);
+    vcp.copy(st + C::KTILE, rows_rsrc<C::KS>(vp, p.v_sn, t * C::KS, N), wave);
   };
 
   floatx16 dqacc[D / 32];
@@ -493,7 +506,7 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
 #pragma unroll
       for (int kk = 0; kk < DV / 16; ++kk) dpacc[kb] = mfma32(vr.row(vt_, kb, kk), greg[kk], dpacc[kb]);
     }
-    bf16x8 dsk[4];
+    e8 dsk[4];
     // dS of the tile; tiles that cross the diagonal or the sequence end mask keys
     auto dscores = [&](auto MASKc) {
 #pragma unroll
@@ -505,7 +518,7 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
             const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
             if (key >= N || (p.causal && key > qi)) pr = 0.f;
           }
-          dsk[kb * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (dpacc[kb][r] + ndrow));
+          dsk[kb * 2 + (r >> 3)][r & 7] = (E)(pr * (dpacc[kb][r] + ndrow));
         }
     };
     if (kv0 + C::KS > N || (p.causal && kv0 + C::KS - 1 > wq0))
@@ -529,26 +542,26 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
             floatx4{dqacc[db][r4 * 4], dqacc[db][r4 * 4 + 1], dqacc[db][r4 * 4 + 2], dqacc[db][r4 * 4 + 3]};
     return;
   }
-  __bf16* dqp = static_cast<__bf16*>(p.grad_q) + b * p.dq_sb + h * p.dq_sh + (int64_t)qi * p.dq_sn;
+  E* dqp = static_cast<E*>(p.grad_q) + b * p.dq_sb + h * p.dq_sh + (int64_t)qi * p.dq_sn;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      bf16x4 o4;
+      e4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(dqacc[db][r4 * 4 + e] * p.scale);
-      *reinterpret_cast<bf16x4*>(dqp + db * 32 + r4 * 8 + g * 4) = o4;
+      for (int e = 0; e < 4; ++e) o4[e] = (E)(dqacc[db][r4 * 4 + e] * p.scale);
+      *reinterpret_cast<e4*>(dqp + db * 32 + r4 * 8 + g * 4) = o4;
     }
 }
 
-template <int D, int DV, bool BIAS>
+template <typename E, int D, int DV, bool BIAS>
 __global__ __launch_bounds__(256, 2) void bwd_mfma(BwdParams p) {
   using C = BwdCfg<D, DV>;
   __shared__ __attribute__((aligned(16))) unsigned char st0[C::STAGE], st1[C::STAGE];
   if ((int)blockIdx.x < p.n_kv_blocks)
-    dkdv_block<D, DV, BIAS>(p, blockIdx.x, st0, st1);
+    dkdv_block<E, D, DV, BIAS>(p, blockIdx.x, st0, st1);
   else
-    dq_block<D, DV, BIAS>(p, blockIdx.x - p.n_kv_blocks, st0, st1);
+    dq_block<E, D, DV, BIAS>(p, blockIdx.x - p.n_kv_blocks, st0, st1);
 }
 
 // Sum of the chunk partials of split tiles, in chunk order, into the bf16 gradients.
@@ -557,8 +570,9 @@ __global__ __launch_bounds__(256, 2) void bwd_mfma(BwdParams p) {
 // row groups give each thread one or two items, whose chunk loads are all in flight
 // together.
 constexpr int kReduceRows = 8;
-template <int D, int DV>
+template <typename E, int D, int DV>
 __global__ __launch_bounds__(256) void bwd_reduce(BwdParams p) {
+  typedef typename Vec<E>::v4 e4;
   const int bh = blockIdx.y;
   const bool kv = (int)blockIdx.z < p.n_tiles;
   const int tile = kv ? blockIdx.z : blockIdx.z - p.n_tiles;
@@ -588,62 +602,71 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdParams p) {
       if (j < nch) acc += v[j];
     const int n = tile * 128 + r;
     if (n >= p.N) continue;
-    bf16x4 o4;
-    __bf16* dst;
+    e4 o4;
+    E* dst;
     if (kv && c >= D) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
-      dst = static_cast<__bf16*>(p.grad_v) + b * p.dv_sb + h * p.dv_sh + (int64_t)n * p.dv_sn + (c - D);
+      for (int e = 0; e < 4; ++e) o4[e] = (E)acc[e];
+      dst = static_cast<E*>(p.grad_v) + b * p.dv_sb + h * p.dv_sh + (int64_t)n * p.dv_sn + (c - D);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * p.scale);
-      dst = kv ? static_cast<__bf16*>(p.grad_k) + b * p.dk_sb + h * p.dk_sh + (int64_t)n * p.dk_sn + c
-               : static_cast<__bf16*>(p.grad_q) + b * p.dq_sb + h * p.dq_sh + (int64_t)n * p.dq_sn + c;
+      for (int e = 0; e < 4; ++e) o4[e] = (E)(acc[e] * p.scale);
+      dst = kv ? static_cast<E*>(p.grad_k) + b * p.dk_sb + h * p.dk_sh + (int64_t)n * p.dk_sn + c
+               : static_cast<E*>(p.grad_q) + b * p.dq_sb + h * p.dq_sh + (int64_t)n * p.dq_sn + c;
     }
-    *reinterpret_cast<bf16x4*>(dst) = o4;
+    *reinterpret_cast<e4*>(dst) = o4;
   }
 }
 
-template __global__ void bwd_mfma<64, 64, false>(BwdParams);
-template __global__ void bwd_mfma<64, 64, true>(BwdParams);
-template __global__ void bwd_mfma<64, 128, false>(BwdParams);
-template __global__ void bwd_mfma<64, 128, true>(BwdParams);
-template __global__ void bwd_mfma<128, 64, false>(BwdParams);
-template __global__ void bwd_mfma<128, 64, true>(BwdParams);
-template __global__ void bwd_mfma<128, 128, false>(BwdParams);
-template __global__ void bwd_mfma<128, 128, true>(BwdParams);
-template __global__ void bwd_rowstat<64>(BwdParams);
-template __global__ void bwd_rowstat<128>(BwdParams);
-template __global__ void bwd_reduce<64, 64>(BwdParams);
-template __global__ void bwd_reduce<64, 128>(BwdParams);
-template __global__ void bwd_reduce<128, 64>(BwdParams);
-template __global__ void bwd_reduce<128, 128>(BwdParams);
+#define FA_BWD_VARIANTS(E)                                      \
+  template __global__ void bwd_mfma<E, 64, 64, false>(BwdParams);   \
+  template __global__ void bwd_mfma<E, 64, 64, true>(BwdParams);    \
+  template __global__ void bwd_mfma<E, 64, 128, false>(BwdParams);  \
+  template __global__ void bwd_mfma<E, 64, 128, true>(BwdParams);   \
+  template __global__ void bwd_mfma<E, 128, 64, false>(BwdParams);  \
+  template __global__ void bwd_mfma<E, 128, 64, true>(BwdParams);   \
+  template __global__ void bwd_mfma<E, 128, 128, false>(BwdParams); \
+  template __global__ void bwd_mfma<E, 128, 128, true>(BwdParams);  \
+  template __global__ void bwd_rowstat<E, 64>(BwdParams);           \
+  template __global__ void bwd_rowstat<E, 128>(BwdParams);          \
+  template __global__ void bwd_reduce<E, 64, 64>(BwdParams);        \
+  template __global__ void bwd_reduce<E, 64, 128>(BwdParams);       \
+  template __global__ void bwd_reduce<E, 128, 64>(BwdParams);       \
+  template __global__ void bwd_reduce<E, 128, 128>(BwdParams);
+FA_BWD_VARIANTS(__bf16)
+FA_BWD_VARIANTS(_Float16)
+#undef FA_BWD_VARIANTS
 
-template <int D, int DV>
+template <typename E, int D, int DV>
 hipError_t launch_bwd_dd(const BwdParams& p, int grid, hipStream_t stream) {
   const int rows = p.B * p.H * p.n_grp * 64;
-  hipLaunchKernelGGL((bwd_rowstat<DV>), dim3(rows / 16), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_rowstat<E, DV>), dim3(rows / 16), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.bias)
-    hipLaunchKernelGGL((bwd_mfma<D, DV, true>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_mfma<E, D, DV, true>), dim3(grid), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((bwd_mfma<D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_mfma<E, D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || !p.split) return e;
-  hipLaunchKernelGGL((bwd_reduce<D, DV>), dim3(kBwdKT / kReduceRows, p.B * p.H, 2 * p.n_tiles), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_reduce<E, D, DV>), dim3(kBwdKT / kReduceRows, p.B * p.H, 2 * p.n_tiles), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
 }
 
+template <typename E>
+hipError_t launch_bwd_e(const BwdParams& p, int grid, hipStream_t stream) {
+  if (p.d == 128 && p.dv == 128) return launch_bwd_dd<E, 128, 128>(p, grid, stream);
+  if (p.d == 64 && p.dv == 128) return launch_bwd_dd<E, 64, 128>(p, grid, stream);
+  if (p.d == 128 && p.dv == 64) return launch_bwd_dd<E, 128, 64>(p, grid, stream);
+  if (p.d == 64 && p.dv == 64) return launch_bwd_dd<E, 64, 64>(p, grid, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int grid, hipStream_t stream) {
-  if (p.d == 128 && p.dv == 128) return launch_bwd_dd<128, 128>(p, grid, stream);
-  if (p.d == 64 && p.dv == 128) return launch_bwd_dd<64, 128>(p, grid, stream);
-  if (p.d == 128 && p.dv == 64) return launch_bwd_dd<128, 64>(p, grid, stream);
-  if (p.d == 64 && p.dv == 64) return launch_bwd_dd<64, 64>(p, grid, stream);
-  return hipErrorInvalidValue;
+hipError_t launch_bwd(const BwdParams& p, int grid, bool fp16, hipStream_t stream) {
+  return fp16 ? launch_bwd_e<_Float16>(p, grid, stream) : launch_bwd_e<__bf16>(p, grid, stream);
 }
 
 }  // namespace fa

@@ -155,8 +155,8 @@ constexpr int kBwdQT = 128;
 hipError_t launch_mfma(const Params& p, int grid, bool merge, bool fp16, hipStream_t stream);
 // dtype: an fa_dtype value (FA_F32, FA_BF16, FA_F16).
 hipError_t launch_generic(const Params& p, int dtype, hipStream_t stream);
-// Gradients dQ, dK, dV (bf16): row statistics, one grid of `grid` dK/dV and dQ units,
-// then (split plans) the reduction of the chunk partials.
-hipError_t launch_bwd_bf16(const BwdParams& p, int grid, hipStream_t stream);
+// Gradients dQ, dK, dV (bf16, or fp16 when fp16): row statistics, one grid of `grid`
+// dK/dV and dQ units, then (split plans) the reduction of the chunk partials.
+hipError_t launch_bwd(const BwdParams& p, int grid, bool fp16, hipStream_t stream);
 
 }  // namespace fa

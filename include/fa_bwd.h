@@ -17,9 +17,9 @@
  * constant: no gradient is formed for it. A query row with no allowed key (lse = -inf)
  * gets dQ = 0 and adds nothing to dK, dV.
  *
- * Numerics: bf16 only. Products run on the matrix cores with fp32 accumulation; P and
- * dS are rounded to bf16 as operands; D uses the bf16 O it is given; dQ, dK, dV are
- * rounded to bf16 once. Every sum is formed in a fixed order inside one workgroup: for
+ * Numerics: bf16 or fp16 (all of q, k, v, out, grad_out and the gradients in the same
+ * dtype). Products run on the matrix cores with fp32 accumulation; P and dS are rounded
+ * to that dtype as operands; D uses the O it is given; dQ, dK, dV are rounded once. Every sum is formed in a fixed order inside one workgroup: for
  * a fixed build, device, shape and input, results are bitwise reproducible.
  */
 #ifndef FA_BWD_H_
@@ -49,12 +49,12 @@ typedef struct {
  * fa_bwd — gradients of fa_fwd, enqueued on `stream`.
  *
  * q, k, v, bias, mask_mode, B, H, N, d, dv: exactly as given to fa_fwd.
- * out, lse: the forward's O ([B, H, N, dv], bf16) and log-sum-exp ([B, H, N], fp32).
- * grad_out: dO, bf16 [B, H, N, dv].
- * grad_q, grad_k: bf16 [B, H, N, d]; grad_v: bf16 [B, H, N, dv]; fully written.
+ * out, lse: the forward's O ([B, H, N, dv], dtype) and log-sum-exp ([B, H, N], fp32).
+ * grad_out: dO, [B, H, N, dv] in dtype.
+ * grad_q, grad_k: [B, H, N, d]; grad_v: [B, H, N, dv]; dtype; fully written.
  * strides: NULL means contiguous [B, H, N, *] tensors, [B, H, N, N] bias, [B, H, N] lse.
- * dtype: FA_BF16 (FA_F32 returns FA_ERR_DTYPE).
- * Alignment: every bf16 tensor base and non-zero stride 16-byte aligned; bias and lse
+ * dtype: FA_BF16 or FA_F16 (FA_F32 returns FA_ERR_DTYPE); d, dv: 64 or 128.
+ * Alignment: every 16-bit tensor base and non-zero stride 16-byte aligned; bias and lse
  * 4-byte aligned. grad_q, grad_k, grad_v must not overlap any input or each other.
  * Workspace: 8 bytes per row (rounded up to 128 rows per (b, h)); fa_bwd uses a
  * library-owned buffer per (device, stream), kept until fa_shutdown().

@@ -70,16 +70,20 @@ def check_lse(l_gpu, l_ref, where=""):
 # relative term covers the final bf16 rounding of the gradient itself.
 GRAD_SCALE_TOL = 2.0 ** -6
 GRAD_RTOL = 1e-2
+# fp16 gradients: the same form with fp16's half-ulp (2^-11): 2^-8 S + 2.5e-3 |G_ref|.
+GRAD_SCALE_TOL_F16 = 2.0 ** -8
+GRAD_RTOL_F16 = 2.5e-3
 
 
-def check_grad(g_gpu, g_ref, scale, where=""):
+def check_grad(g_gpu, g_ref, scale, where="", dtype="bf16"):
     g = to_np(g_gpu) if not isinstance(g_gpu, np.ndarray) else g_gpu
     assert np.isfinite(g).all(), f"non-finite gradient {where}"
     if g_ref.size == 0:
         return 0.0
     err = np.abs(g - g_ref)
     floor = 1e-6 * float(scale.max())
-    bound = GRAD_SCALE_TOL * scale + GRAD_RTOL * np.abs(g_ref) + floor
+    tol, rtol = (GRAD_SCALE_TOL_F16, GRAD_RTOL_F16) if dtype == "f16" else (GRAD_SCALE_TOL, GRAD_RTOL)
+    bound = tol * scale + rtol * np.abs(g_ref) + floor
     bad = err > bound
     assert not bad.any(), (f"{int(bad.sum())} elements out of tolerance {where}; "
                            f"worst |dG| / bound = {float((err / bound).max()):.3g}")

@@ -52,6 +52,7 @@ def _set(name, value):
 
 @pytest.mark.parametrize("mutate,expected", [
     (lambda c: setattr(c, "dtype", capi.FA_F32), "FA_ERR_DTYPE"),
+    (lambda c: setattr(c, "dtype", 3), "FA_ERR_DTYPE"),
     (lambda c: setattr(c, "dtype", 5), "FA_ERR_DTYPE"),
     (lambda c: setattr(c, "mask", 3), "FA_ERR_MASK"),
     (lambda c: setattr(c, "d", 80), "FA_ERR_SHAPE"),

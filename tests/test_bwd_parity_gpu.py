@@ -130,3 +130,22 @@ def test_key_gradients_sum_to_zero(gpu_device):
     tot = np.abs(g.sum(axis=2))
     scale = np.abs(g).sum(axis=2)
     assert (tot <= 2e-2 * scale + 1e-3).all()
+
+
+F16 = [  # (workload index, overrides): the fp16 gradient kernels
+    (1, dict(N=1000)),
+    (3, dict(B=2, H=3, N=555)),
+    (2, dict(B=2, H=4, N=777)),
+]
+
+
+@pytest.mark.parametrize("idx,over", F16, ids=[f"w{i}-{o}" for i, o in F16])
+def test_fp16_gradients(gpu_device, idx, over):
+    w = workloads.workload(idx).resized(dtype="f16", **over)
+    inp, gpu = _device_inputs(w, gpu_device)
+    dq, dk, dv = _fwd_bwd(gpu, w)
+    rq, rk, rv, (sq, sk, sv) = sdpa_backward_reference(inp["q"], inp["k"], inp["v"], inp["do"], inp["bias"],
+                                                       w.causal, with_scales=True)
+    e = [check_grad(dq, rq, sq, "dQ", "f16"), check_grad(dk, rk, sk, "dK", "f16"),
+         check_grad(dv, rv, sv, "dV", "f16")]
+    print(f"[bwd f16] worst |err| / bound: dQ {e[0]:.3g} dK {e[1]:.3g} dV {e[2]:.3g}", flush=True)
