@@ -149,3 +149,37 @@ def test_fp16_gradients(gpu_device, idx, over):
     e = [check_grad(dq, rq, sq, "dQ", "f16"), check_grad(dk, rk, sk, "dK", "f16"),
          check_grad(dv, rv, sv, "dV", "f16")]
     print(f"[bwd f16] worst |err| / bound: dQ {e[0]:.3g} dK {e[1]:.3g} dV {e[2]:.3g}", flush=True)
+
+
+def test_gradient_graph_capture_replays_match_eager(gpu_device):
+    """fa_bwd_ex of a split problem (row statistics, gradient grid, chunk reduction)
+    captured into a HIP graph gives, on every replay, bitwise the eager gradients for the
+    inputs of that replay; eager work runs between the replays."""
+    import torch
+
+    w = workloads.workload(1).resized(N=1500)
+    _, gpu = _device_inputs(w, gpu_device)
+    q, k, v, g = (gpu[n].clone() for n in ("q", "k", "v", "do"))
+    out, lse = capi.fa_fwd(q, k, v, causal=True)
+    nbytes = capi.fa_bwd_workspace_size(w.B, w.H, w.N, w.d, w.dv, capi.FA_BF16, True)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        capi.fa_bwd_ex(q, k, v, out, lse, g, ws, causal=True, grad_q=dq, grad_k=dk, grad_v=dv)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        capi.fa_bwd_ex(q, k, v, out, lse, g, ws, causal=True, grad_q=dq, grad_k=dk, grad_v=dv)
+    gen = torch.Generator().manual_seed(12)
+    for _ in range(3):
+        g.copy_(torch.randn(g.shape, generator=gen).to(g.dtype).to(gpu_device))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = capi.fa_bwd(q, k, v, out, lse, g, causal=True)
+        torch.cuda.synchronize()
+        for x, y in zip((dq, dk, dv), ref):
+            assert torch.equal(x, y)

@@ -92,3 +92,35 @@ def test_decode_workspace_entry_matches(gpu_device):
     b = capi.fa_fwd_qk_ex(gpu["q"], gpu["k"], gpu["v"], ws, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_graph_capture_replays_match_eager(gpu_device):
+    """A decoding step (one query row per head, split over keys) captured into a HIP graph
+    gives bitwise the eager output on every replay."""
+    import torch
+
+    w = workloads.workload(1).resized(B=2, H=8, N=3000, Nq=1)
+    _, gpu = _inputs(w, gpu_device)
+    q, k, v = (gpu[n].clone() for n in ("q", "k", "v"))
+    nbytes = capi.fa_fwd_qk_workspace_size(w.B, w.H, 1, w.N, w.d, w.dv, capi.FA_BF16, True)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=gpu_device)
+    out = torch.empty(w.B, w.H, 1, w.dv, dtype=q.dtype, device=gpu_device)
+    lse = torch.empty(w.B, w.H, 1, dtype=torch.float32, device=gpu_device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        capi.fa_fwd_qk_ex(q, k, v, ws, causal=True, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        capi.fa_fwd_qk_ex(q, k, v, ws, causal=True, out=out, lse=lse)
+    gen = torch.Generator().manual_seed(13)
+    for _ in range(3):
+        q.copy_(torch.randn(q.shape, generator=gen).to(q.dtype).to(gpu_device))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_ref, l_ref = capi.fa_fwd_qk(q, k, v, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(lse, l_ref)
