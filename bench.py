@@ -36,14 +36,15 @@ KERNEL_SRC = os.path.join(ROOT, "exact_attention_35_amd", "csrc", "fa_fwd_mfma.h
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_sha(src: str = KERNEL_SRC) -> str:
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per launch from a committed counter summary, if it was taken on the
-    current kernel source; otherwise None."""
-    path = os.path.join(PROFILES, f"traffic_fwd_mfma_{workload}.txt")
+def read_traffic(workload: str, kind: str = "fwd_mfma", src: str = KERNEL_SRC):
+    """HBM bytes per launch (forward) or per call (gradients, all their kernels) from a
+    committed counter summary, if it was taken on the current kernel source; otherwise
+    None."""
+    path = os.path.join(PROFILES, f"traffic_{kind}_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -51,7 +52,7 @@ def read_traffic(workload: str):
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_sha():
+    if kv.get("kernel_source_sha256_16") != kernel_sha(src):
         return None
     try:
         return float(kv["hbm_bytes_per_dispatch"])
@@ -405,8 +406,8 @@ def bench_bwd(args, w, inp, gpu, out, lse) -> int:
         "config": {"workload": w.name, "pass": "bwd", "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv,
                    "causal": w.causal, "bias": w.bias, "layout": w.layout, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
-                     "kernel": "bwd_rowstat + bwd_mfma (one fa_bwd call)",
+                     "frac": achieved / peak, "traffic": read_traffic(w.name, "bwd", BWD_SRC),
+                     "kernel": "bwd_rowstat + bwd_mfma [+ bwd_reduce] (one fa_bwd call)",
                      "avg_launch_us": avg_call_s * 1e6, "alg_flops_per_launch": flops,
                      "min_bytes_per_launch": rf.min_bytes_bwd(w.B, w.H, w.N, w.d, w.dv, 2, bias_bytes),
                      "kernel_source_sha256_16": hashlib.sha256(open(BWD_SRC, "rb").read()).hexdigest()[:16]},
