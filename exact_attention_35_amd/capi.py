@@ -312,7 +312,7 @@ def _prepare_bwd(q, k, v, out, lse, grad_out, bias, causal, grad_q, grad_k, grad
 def fa_bwd(q, k, v, out, lse, grad_out, bias=None, causal=False, grad_q=None, grad_k=None,
            grad_v=None, stream=None):
     """Gradients through fa_bwd: (grad_q, grad_k, grad_v) of fa_fwd's output for the
-    upstream gradient grad_out, from the forward's out and lse. bf16 tensors; outputs are
+    upstream gradient grad_out, from the forward's out and lse. bf16 or fp16 tensors; outputs are
     allocated when not given. Enqueued on `stream` (default: torch's current stream)."""
     (B, H, N, d, dv, dt, mask, bias, out, lse, grad_q, grad_k, grad_v,
      s) = _prepare_bwd(q, k, v, out, lse, grad_out, bias, causal, grad_q, grad_k, grad_v)
