@@ -57,7 +57,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* q, k, v or out is NULL (with B*H*N > 0), or strides NULL where needed */
   FA_ERR_SHAPE = -2,     /* negative size, size too large, or d, dv outside 1..256 */
-  FA_ERR_DTYPE = -3,     /* dtype is not FA_F32 or FA_BF16 */
+  FA_ERR_DTYPE = -3,     /* dtype is not FA_F32, FA_BF16 or FA_F16 (gradients: not a 16-bit type) */
   FA_ERR_MASK = -4,      /* mask_mode is not FA_MASK_NONE or FA_MASK_CAUSAL */
   FA_ERR_STRIDE = -5,    /* a negative stride, rows of out / lse that overlap, or a bf16
                             k / v row stride of 2^24 elements or more */
