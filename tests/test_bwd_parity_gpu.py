@@ -65,6 +65,26 @@ def test_gradients_small_elementwise(gpu_device, idx, over):
     print(f"[bwd] worst |err| / bound: dQ {e[0]:.3g} dK {e[1]:.3g} dV {e[2]:.3g}", flush=True)
 
 
+# Split plans under other unit targets (FA_BWD_UNITS) cut the tiles into other chunk
+# counts and lengths. Plans are cached per shape, so each case uses a shape that no other
+# test plans, and the target is read when that shape is planned first.
+UNIT_TARGETS = [(96, dict(N=2600)), (320, dict(N=2700)), (200, dict(H=2, N=2300, causal=False))]
+
+
+@pytest.mark.parametrize("units,over", UNIT_TARGETS, ids=[f"u{u}-{o}" for u, o in UNIT_TARGETS])
+def test_gradients_under_other_unit_targets(gpu_device, monkeypatch, units, over):
+    monkeypatch.setenv("FA_BWD_UNITS", str(units))
+    w = workloads.workload(1).resized(**over)
+    print(f"\n[bwd] {w.name} {over} units={units}", flush=True)
+    inp, gpu = _device_inputs(w, gpu_device)
+    dq, dk, dv = _fwd_bwd(gpu, w)
+    rq, rk, rv, (sq, sk, sv) = sdpa_backward_reference(inp["q"], inp["k"], inp["v"], inp["do"], inp["bias"],
+                                                       w.causal, with_scales=True)
+    check_grad(dq, rq, sq, "dQ")
+    check_grad(dk, rk, sk, "dK")
+    check_grad(dv, rv, sv, "dV")
+
+
 @pytest.mark.parametrize("N", [1, 17, 65, 129, 255])
 @pytest.mark.parametrize("d,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
 @pytest.mark.parametrize("causal,bias", [(True, False), (False, True)])
