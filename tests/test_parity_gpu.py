@@ -202,6 +202,25 @@ def test_split_merge_paths_agree(gpu_device, monkeypatch, idx, over):
         assert bool(o1.float().isfinite().all()) and bool(l1.isfinite().all())
 
 
+# Split plans under other unit targets (FA_SPLIT_UNITS): other range counts and cuts per
+# query tile. Plans are cached per shape, so each case uses a shape that no other test
+# plans, and the target is read when that shape is planned first.
+SPLIT_TARGETS = [(48, 1, dict(N=1900)), (160, 1, dict(N=2050, causal=False)),
+                 (384, 3, dict(B=1, H=2, N=1300))]
+
+
+@pytest.mark.parametrize("units,idx,over", SPLIT_TARGETS, ids=[f"u{u}-w{i}-{o}" for u, i, o in SPLIT_TARGETS])
+def test_split_plans_under_other_unit_targets(gpu_device, monkeypatch, units, idx, over):
+    monkeypatch.setenv("FA_SPLIT_UNITS", str(units))
+    w = workloads.workload(idx).resized(**over)
+    print(f"\n[fwd] {w.name} {over} units={units}", flush=True)
+    inp, gpu = _inputs(w, gpu_device)
+    o, l = _run(gpu, w, gpu_device)
+    o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
+    check_out(o, o_ref, "bf16", w.name + str(over))
+    check_lse(l, l_ref, w.name + str(over))
+
+
 def test_graph_capture_replays_match_eager(gpu_device):
     """A split problem captured into a HIP graph (there the merge is a second kernel)
     gives, on every replay, bitwise the eager result (merge blocks in the forward
