@@ -17,7 +17,7 @@ __all__ = [
     "STATUS", "lib", "library_path", "fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size",
     "fa_status_string", "fa_version", "fa_shutdown", "fa_plan_describe", "make_strides", "FaStrides",
     "FaPlanInfo", "EXPORTED", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "FaBwdStrides",
-    "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size",
+    "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size", "fa_plan_describe_qk",
 ]
 
 FA_OK = 0
@@ -35,7 +35,8 @@ STATUS = {
 # every symbol include/*.h declares
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
             "fa_version", "fa_shutdown", "fa_plan_describe", "fa_bwd", "fa_bwd_ex",
-            "fa_bwd_workspace_size", "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size")
+            "fa_bwd_workspace_size", "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size",
+            "fa_plan_describe_qk")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -65,7 +66,7 @@ class FaBwdStrides(ctypes.Structure):
 class FaPlanInfo(ctypes.Structure):
     _fields_ = [("split", ctypes.c_int32), ("n_qtiles", ctypes.c_int32), ("qtile_rows", ctypes.c_int32),
                 ("key_tile", ctypes.c_int32), ("units", ctypes.c_int32), ("merge_blocks", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("unit_tile_shift", ctypes.c_int32)]
 
 
 _lib = None
@@ -107,6 +108,9 @@ def lib():
     L.fa_plan_describe.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.POINTER(FaPlanInfo), ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
     L.fa_plan_describe.restype = ctypes.c_int
+    L.fa_plan_describe_qk.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(FaPlanInfo), ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+    L.fa_plan_describe_qk.restype = ctypes.c_int
     bwd_args = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, i64,
                 ctypes.POINTER(FaBwdStrides), ctypes.c_int, vp]
     L.fa_bwd.argtypes = bwd_args
@@ -134,10 +138,15 @@ def fa_shutdown() -> None:
 def fa_plan_describe(B, H, N, d, dv, dtype, causal, compute_units, max_units=4096):
     """The work plan of a problem on a device with `compute_units` CUs (no GPU needed):
     (FaPlanInfo, list of packed unit-table words; empty unless the plan splits)."""
+    return fa_plan_describe_qk(B, H, N, N, d, dv, dtype, causal, compute_units, max_units)
+
+
+def fa_plan_describe_qk(B, H, Nq, Nk, d, dv, dtype, causal, compute_units, max_units=4096):
+    """fa_plan_describe for N_q query rows against N_k keys (the plan of fa_fwd_qk)."""
     info = FaPlanInfo()
     table = (ctypes.c_uint32 * max_units)()
-    st = lib().fa_plan_describe(B, H, N, d, dv, dtype, FA_MASK_CAUSAL if causal else FA_MASK_NONE,
-                                compute_units, ctypes.byref(info), table, max_units)
+    st = lib().fa_plan_describe_qk(B, H, Nq, Nk, d, dv, dtype, FA_MASK_CAUSAL if causal else FA_MASK_NONE,
+                                   compute_units, ctypes.byref(info), table, max_units)
     _check(st)
     units = list(table[: min(info.units, max_units)]) if info.split else []
     return info, units
@@ -174,7 +183,31 @@ def make_strides(q, k, v, out, bias=None, lse=None) -> FaStrides:
     return s
 
 
-def _prepare(q, k, v, bias, causal, out, lse, rect=False):
+def _expect(t, name, shape, dtype):
+    """A caller-supplied tensor must have exactly the shape and dtype the C ABI sizes it
+    by (the library derives every extent from q's shape)."""
+    if tuple(t.shape) != tuple(shape):
+        raise FaError(STATUS["FA_ERR_SHAPE"], f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise FaError(STATUS["FA_ERR_DTYPE"], f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _same_device(named):
+    """Every tensor is device memory of one HIP device (the library dereferences the
+    pointers on the GPU)."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise FaError(STATUS["FA_ERR_NULL"], f"{name} is not a device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise FaError(STATUS["FA_ERR_NULL"], f"{name} is on {t.device}, expected {dev}")
+
+
+def _prepare(q, k, v, bias, causal, out, lse, rect=False, check_device=True):
     import torch
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -195,9 +228,19 @@ def _prepare(q, k, v, bias, causal, out, lse, rect=False):
             raise FaError(STATUS["FA_ERR_DTYPE"], "bias must be float32")
         if bias.dim() == 3:
             bias = bias.unsqueeze(0)
+        if bias.dim() != 4 or any(bs not in (1, full) for bs, full in zip(bias.shape, (B, H, N, Nk))) \
+                or tuple(bias.shape[2:]) != (N, Nk):
+            raise FaError(STATUS["FA_ERR_SHAPE"], f"bias of shape {tuple(bias.shape)} does not "
+                          f"broadcast to {(B, H, N, Nk)} as [B|1, H|1, N_q, N_k]")
         bias = bias.expand(B, H, N, Nk)
         if N and Nk and bias.stride(-1) != 1:
             raise FaError(STATUS["FA_ERR_STRIDE"], "bias key axis must be contiguous")
+    if out is not None:
+        _expect(out, "out", (B, H, N, dv), q.dtype)
+    if lse is not None:
+        _expect(lse, "lse", (B, H, N), torch.float32)
+    if check_device:
+        _same_device((("q", q), ("k", k), ("v", v), ("bias", bias), ("out", out), ("lse", lse)))
     if out is None:
         out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
     if lse is None:
@@ -207,6 +250,18 @@ def _prepare(q, k, v, bias, causal, out, lse, rect=False):
     if rect:
         return (B, H, N, Nk, d, dv, dt, mask, bias, out, lse, strides)
     return (B, H, N, d, dv, dt, mask, bias, out, lse, strides)
+
+
+def _workspace_bytes(workspace, like):
+    """Size of a caller workspace: a uint8 tensor on the inputs' device, or None."""
+    import torch
+
+    if workspace is None:
+        return 0
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise FaError(STATUS["FA_ERR_WORKSPACE"], "workspace must be a 1-D uint8 tensor")
+    _same_device((("q", like), ("workspace", workspace)))
+    return workspace.numel()
 
 
 def _stream_handle(stream, device):
@@ -258,7 +313,7 @@ def fa_fwd_qk_workspace_size(B, H, Nq, Nk, d, dv, dtype_code, causal) -> int:
 def fa_fwd_qk_ex(q, k, v, workspace, bias=None, causal=False, out=None, lse=None, stream=None):
     """fa_fwd_qk with a caller-provided workspace (a uint8 device tensor, or None)."""
     B, H, Nq, Nk, d, dv, dt, mask, bias, out, lse, strides = _prepare(q, k, v, bias, causal, out, lse, rect=True)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _workspace_bytes(workspace, q)
     st = lib().fa_fwd_qk_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), mask, _ptr(out), _ptr(lse),
                             B, H, Nq, Nk, d, dv, ctypes.byref(strides), dt,
                             _stream_handle(stream, q.device), _ptr(workspace), nbytes)
@@ -274,7 +329,7 @@ def fa_fwd_workspace_size(B, H, N, d, dv, dtype_code, causal) -> int:
 def fa_fwd_ex(q, k, v, workspace, bias=None, causal=False, out=None, lse=None, stream=None):
     """fa_fwd with a caller-provided workspace (a uint8 device tensor, or None)."""
     B, H, N, d, dv, dt, mask, bias, out, lse, strides = _prepare(q, k, v, bias, causal, out, lse)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _workspace_bytes(workspace, q)
     st = lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), mask, _ptr(out), _ptr(lse),
                          B, H, N, d, dv, ctypes.byref(strides), dt,
                          _stream_handle(stream, q.device), _ptr(workspace), nbytes)
@@ -285,9 +340,17 @@ def fa_fwd_ex(q, k, v, workspace, bias=None, causal=False, out=None, lse=None, s
 def _prepare_bwd(q, k, v, out, lse, grad_out, bias, causal, grad_q, grad_k, grad_v):
     import torch
 
-    B, H, N, d, dv, dt, mask, bias, out, lse, _ = _prepare(q, k, v, bias, causal, out, lse)
-    if tuple(grad_out.shape) != (B, H, N, dv) or grad_out.dtype != q.dtype:
-        raise FaError(STATUS["FA_ERR_SHAPE"], "grad_out must match out")
+    if out is None or lse is None or grad_out is None:
+        raise FaError(STATUS["FA_ERR_NULL"], "out, lse and grad_out (the forward's O, its "
+                      "log-sum-exp and dO) are required")
+    B, H, N, d, dv, dt, mask, bias, out, lse, _ = _prepare(q, k, v, bias, causal, out, lse,
+                                                           check_device=False)
+    _expect(grad_out, "grad_out", (B, H, N, dv), q.dtype)
+    for name, t, width in (("grad_q", grad_q, d), ("grad_k", grad_k, d), ("grad_v", grad_v, dv)):
+        if t is not None:
+            _expect(t, name, (B, H, N, width), q.dtype)
+    _same_device((("q", q), ("k", k), ("v", v), ("bias", bias), ("out", out), ("lse", lse),
+                  ("grad_out", grad_out), ("grad_q", grad_q), ("grad_k", grad_k), ("grad_v", grad_v)))
     if grad_q is None:
         grad_q = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
     if grad_k is None:
@@ -333,7 +396,7 @@ def fa_bwd_ex(q, k, v, out, lse, grad_out, workspace, bias=None, causal=False, g
     """fa_bwd with a caller-provided workspace (a uint8 device tensor)."""
     (B, H, N, d, dv, dt, mask, bias, out, lse, grad_q, grad_k, grad_v,
      s) = _prepare_bwd(q, k, v, out, lse, grad_out, bias, causal, grad_q, grad_k, grad_v)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _workspace_bytes(workspace, q)
     st = lib().fa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(grad_out), _ptr(bias),
                          mask, _ptr(grad_q), _ptr(grad_k), _ptr(grad_v), B, H, N, d, dv, ctypes.byref(s),
                          dt, _stream_handle(stream, q.device), _ptr(workspace), nbytes)

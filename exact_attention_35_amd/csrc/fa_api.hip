@@ -190,6 +190,7 @@ struct Plan {
   bool mfma = false;
   int n_qt = 0;
   bool split = false;   // query tiles cut into key ranges (units) merged afterwards
+  int shift = 0;        // range boundaries in granules of 2^shift key tiles
   struct Ranges {       // the key ranges of one query tile
     int nch;
     int begin[fa::kMaxRanges], len[fa::kMaxRanges];
@@ -227,8 +228,9 @@ constexpr double kDiagonalCost = 1.5;
 
 // Cuts nt key tiles into nch consecutive ranges of about equal cost for units u0 ..
 // u0+nch-1 (range k costs len_k * c_k, plus the diagonal cost for the last range);
-// returns the largest range cost.
-double cut_even(int nt, int nch, int64_t u0, int cus, double diag, Plan::Ranges* r) {
+// returns the largest range cost. Range boundaries fall on multiples of G key tiles (the
+// granule of the unit table's fields); nch is at most ceil(nt / G).
+double cut_even(int nt, int nch, int64_t u0, int cus, double diag, int G, Plan::Ranges* r) {
   double c[fa::kMaxRanges], inv_sum = 0.0, extra = 0.0;
   for (int k = 0; k < nch; ++k) {
     c[k] = u0 + k < cus ? 1.0 : kSecondSlotCost;
@@ -236,16 +238,17 @@ double cut_even(int nt, int nch, int64_t u0, int cus, double diag, Plan::Ranges*
   }
   extra = diag / c[nch - 1];
   const double T = (nt + extra) / inv_sum;  // the common cost if tiles were divisible
-  int t = 0;
+  const int ng = (nt + G - 1) / G;          // granules
+  int tg = 0;
   double acc = 0.0, worst = 0.0;
   for (int k = 0; k < nch; ++k) {
     acc += T / c[k] - (k == nch - 1 ? extra : 0.0);
-    int end = k == nch - 1 ? nt : (int)std::lround(acc);
-    end = std::min(std::max(end, t + 1), nt - (nch - 1 - k));  // every range keeps >= 1 tile
-    r->begin[k] = t;
-    r->len[k] = end - t;
+    int endg = k == nch - 1 ? ng : (int)std::lround(acc / G);
+    endg = std::min(std::max(endg, tg + 1), ng - (nch - 1 - k));  // every range keeps >= 1 granule
+    r->begin[k] = tg * G;
+    r->len[k] = std::min(endg * G, nt) - tg * G;
     worst = std::max(worst, r->len[k] * c[k] + (k == nch - 1 ? diag : 0.0));
-    t = end;
+    tg = endg;
   }
   r->nch = nch;
   return worst;
@@ -256,6 +259,7 @@ double cut_even(int nt, int nch, int64_t u0, int cus, double diag, Plan::Ranges*
 // than kMaxRanges ranges.
 int64_t cut_ranges(const Plan& pl, int64_t N, int64_t coff, int64_t BH, bool causal, int cus, double cap,
                    Plan::Ranges* out) {
+  const int G = 1 << pl.shift;
   int64_t u = 0;
   for (int qt = pl.n_qt - 1; qt >= 0; --qt) {
     const int nt = (int)qtile_ntiles(N, coff, qt, causal);
@@ -266,21 +270,28 @@ int64_t cut_ranges(const Plan& pl, int64_t N, int64_t coff, int64_t BH, bool cau
       u += BH;
       continue;
     }
+    const int ng = (nt + G - 1) / G;
     const double diag = causal ? kDiagonalCost : 0.0;
     int nch = 1;
-    while (cut_even(nt, nch, u, cus, diag, &out[qt]) > cap && nch < std::min(nt, fa::kMaxRanges)) ++nch;
-    if (cut_even(nt, nch, u, cus, diag, &out[qt]) > cap && nch < nt) return -1;
+    while (cut_even(nt, nch, u, cus, diag, G, &out[qt]) > cap && nch < std::min(ng, fa::kMaxRanges)) ++nch;
+    if (cut_even(nt, nch, u, cus, diag, G, &out[qt]) > cap && nch < ng) return -1;
     u += BH * nch;
   }
   return u;
 }
 
-// One unit table entry: query tile (bits 0-7), first key tile (8-16), key-tile count
-// (17-25), b*h (26-31). Plans with a single query tile put b*h's low 8 bits in bits 0-7.
-uint32_t pack_unit(int qt, int begin, int len, int64_t bh, bool one_qtile) {
+// Widest field of the unit table: first key tile and key-tile count are 9 bits each.
+constexpr int kUnitFieldMax = 511;
+
+// One unit table entry: query tile (bits 0-7), first key tile (8-16) and key-tile count
+// (17-25), both in granules of 2^shift tiles (the count rounded up: the kernel clips the
+// last range of a tile to the tile's key tiles), b*h (26-31). Plans with a single query
+// tile put b*h's low 8 bits in bits 0-7.
+uint32_t pack_unit(int qt, int begin, int len, int64_t bh, bool one_qtile, int shift) {
   const uint32_t lo = one_qtile ? (uint32_t)(bh & 0xff) : (uint32_t)qt;
   const uint32_t hi = one_qtile ? (uint32_t)(bh >> 8) : (uint32_t)bh;
-  return lo | (uint32_t)begin << 8 | (uint32_t)len << 17 | hi << 26;
+  const uint32_t b = (uint32_t)(begin >> shift), n = (uint32_t)((len + (1 << shift) - 1) >> shift);
+  return lo | b << 8 | n << 17 | hi << 26;
 }
 
 // Merge blocks per split tile and b*h: the row groups of a query tile that hold query
@@ -305,15 +316,25 @@ Plan make_plan(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t d
   // Split where the query tiles do not give every CU two workgroups (below one per CU
   // CUs idle; below two, a causal problem's longest tiles set the time: measured
   // 147 -> 84 us for four causal heads of 8192) and the unit table's fields fit
-  // (b*h < 64, query tile < 256, key tiles < 512).
+  // (b*h < 64, or < 2^14 with one query tile; query tile < 256).
   if (tiles <= 0 || tiles >= 2 * (int64_t)cus || BH > (pl.n_qt == 1 ? kMaxSplitBH1 : kMaxSplitBH) ||
       pl.n_qt > fa::kMaxSplitQTiles)
     return pl;
+  // The first key tile and the tile count of a unit are stored in granules of 2^shift
+  // key tiles, the smallest granule for which the longest query tile's key tiles fit the
+  // 9-bit fields (shift 0 up to 32704 keys per query tile).
+  int64_t nt_max = 0;
+  for (int qt = 0; qt < pl.n_qt; ++qt) nt_max = std::max(nt_max, qtile_ntiles(N, coff, qt, causal));
+  while (((nt_max + (1 << pl.shift) - 1) >> pl.shift) > kUnitFieldMax) ++pl.shift;
+  if (pl.shift > 15) {
+    pl.shift = 0;
+    return pl;
+  }
   // Cut the query tiles' key ranges into units of about equal cost, as many as the CUs
   // hold at once (two workgroups per CU): the smallest cost cap whose cut fits.
   const int64_t target = std::min<int64_t>(fa::kMaxSplitUnits,
                                            env_int("FA_SPLIT_UNITS") > 0 ? env_int("FA_SPLIT_UNITS") : 2 * (int64_t)cus);
-  double lo = 0.5, hi = (double)qtile_ntiles(N, coff, pl.n_qt - 1, causal) * kSecondSlotCost + kDiagonalCost + 1.0;
+  double lo = 0.5, hi = (double)nt_max * kSecondSlotCost + kDiagonalCost + 1.0;
   if (cut_ranges(pl, N, coff, BH, causal, cus, hi, pl.ranges) < 0) return pl;
   for (int it = 0; it < 24; ++it) {
     const double mid = 0.5 * (lo + hi);
@@ -430,7 +451,7 @@ int run(const Problem& P, const Plan& pl_in, void* ws, hipStream_t stream) {
       if (r.nch > 1) p.split_qt[n_split++] = (uint8_t)qt;
       for (int64_t bh = 0; bh < P.B * P.H; ++bh)
         for (int c = 0; c < r.nch; ++c)
-          p.unit_info[acc + bh * r.nch + c] = pack_unit(qt, r.begin[c], r.len[c], bh, pl.n_qt == 1);
+          p.unit_info[acc + bh * r.nch + c] = pack_unit(qt, r.begin[c], r.len[c], bh, pl.n_qt == 1, pl.shift);
       acc += (int32_t)(P.B * P.H * r.nch);
     }
   }
@@ -440,6 +461,7 @@ int run(const Problem& P, const Plan& pl_in, void* ws, hipStream_t stream) {
   const bool split = pl.split;
   const bool in_kernel_merge = split && !stream_capturing(stream) && env_int("FA_MERGE_KERNEL") == 0;
   p.n_units = pl.grid;
+  p.unit_shift = pl.shift;
   p.merge_groups = merge_groups_used(P.Nq, pl.n_qt, P.dv);
   p.seq = next_call_number();
   if (pl.ws_bytes > 0) {
@@ -471,27 +493,36 @@ Problem make_problem(const void* q, const void* k, const void* v, const float* b
 }
 
 // ---------------------------------------------------------------- owned workspaces
+// One library-owned scratch buffer per (device, stream), shared by fa_fwd and fa_bwd
+// (calls on one stream run in order, so they never use it at the same time). It only
+// grows: a larger need allocates a new buffer and retires the old one, which stays
+// allocated until fa_shutdown(), so a pointer handed to a call (maybe on another host
+// thread, not yet enqueued) is never freed under it. While the stream captures a graph
+// nothing is allocated: a call that would need to allocate returns FA_ERR_WORKSPACE,
+// and so does any call that needs scratch memory at all (a graph would keep using the
+// shared buffer on every replay); captured work takes the _ex entry points.
 struct OwnedWs {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, OwnedWs> g_ws;
+std::vector<std::pair<int, void*>> g_ws_retired;  // (device, buffer), freed by fa_shutdown
 
 int owned_workspace(int dev, hipStream_t stream, size_t need, void** out) {
+  if (stream_capturing(stream)) return FA_ERR_WORKSPACE;
   std::lock_guard<std::mutex> lk(g_ws_mu);
   OwnedWs& w = g_ws[{dev, stream}];
   if (w.bytes < need) {
-    if (w.ptr) {
-      if (hipStreamSynchronize(stream) != hipSuccess) return FA_ERR_ALLOC;
-      (void)hipFree(w.ptr);
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
+    const size_t grow = std::max(need, w.bytes + w.bytes / 2);
     void* p = nullptr;
-    if (hipMalloc(&p, need) != hipSuccess) return FA_ERR_ALLOC;
+    if (hipMalloc(&p, grow) != hipSuccess) {
+      (void)hipGetLastError();
+      return FA_ERR_ALLOC;
+    }
+    if (w.ptr) g_ws_retired.emplace_back(dev, w.ptr);
     w.ptr = p;
-    w.bytes = need;
+    w.bytes = grow;
   }
   *out = w.ptr;
   return FA_OK;
@@ -816,12 +847,13 @@ const char* fa_status_string(int status) {
 
 int fa_version(void) { return FA_VERSION; }
 
-int fa_plan_describe(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask_mode,
-                     int compute_units, fa_plan_info* info, uint32_t* unit_info, int max_units) {
+int fa_plan_describe_qk(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, int dtype,
+                        int mask_mode, int compute_units, fa_plan_info* info, uint32_t* unit_info,
+                        int max_units) {
   if (!info || compute_units < 1) return FA_ERR_NULL;
-  const int st = check_shape(B, H, N, d, dv, dtype, mask_mode);
+  const int st = check_shape_qk(B, H, Nq, Nk, d, dv, dtype, mask_mode);
   if (st != FA_OK) return st;
-  const std::shared_ptr<const Plan> plan = cached_plan(B, H, N, N, d, dv, dtype, mask_mode, compute_units);
+  const std::shared_ptr<const Plan> plan = cached_plan(B, H, Nq, Nk, d, dv, dtype, mask_mode, compute_units);
   const Plan& pl = *plan;
   info->split = pl.split ? 1 : 0;
   info->n_qtiles = pl.mfma ? pl.n_qt : 0;
@@ -830,16 +862,22 @@ int fa_plan_describe(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int
   info->units = pl.mfma ? pl.grid : 0;
   info->merge_blocks = pl.merge_blocks;
   info->workspace_bytes = pl.ws_bytes;
+  info->unit_tile_shift = pl.shift;
   if (pl.split && unit_info) {
     int u = 0;
     for (int qt = pl.n_qt - 1; qt >= 0; --qt) {
       const Plan::Ranges& r = pl.ranges[qt];
       for (int64_t bh = 0; bh < B * H; ++bh)
         for (int c = 0; c < r.nch; ++c, ++u)
-          if (u < max_units) unit_info[u] = pack_unit(qt, r.begin[c], r.len[c], bh, pl.n_qt == 1);
+          if (u < max_units) unit_info[u] = pack_unit(qt, r.begin[c], r.len[c], bh, pl.n_qt == 1, pl.shift);
     }
   }
   return FA_OK;
+}
+
+int fa_plan_describe(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask_mode,
+                     int compute_units, fa_plan_info* info, uint32_t* unit_info, int max_units) {
+  return fa_plan_describe_qk(B, H, N, N, d, dv, dtype, mask_mode, compute_units, info, unit_info, max_units);
 }
 
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -891,17 +929,19 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t
 
 void fa_shutdown(void) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  for (auto& kv : g_ws) {
-    if (kv.second.ptr) {
-      int cur = 0;
-      (void)hipGetDevice(&cur);
-      (void)hipSetDevice(kv.first.first);
-      (void)hipDeviceSynchronize();
-      (void)hipFree(kv.second.ptr);
-      (void)hipSetDevice(cur);
-    }
-  }
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  auto release = [](int dev, void* ptr) {
+    (void)hipSetDevice(dev);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(ptr);
+  };
+  for (auto& kv : g_ws)
+    if (kv.second.ptr) release(kv.first.first, kv.second.ptr);
+  for (auto& r : g_ws_retired) release(r.first, r.second);
   g_ws.clear();
+  g_ws_retired.clear();
+  (void)hipSetDevice(cur);
 }
 
 }  // extern "C"

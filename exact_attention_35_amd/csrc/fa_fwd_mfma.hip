@@ -159,10 +159,11 @@ __device__ __forceinline__ Unit decode_unit(const Params& p, int u, int BM, int 
   w.qt = split ? (one ? 0 : (int)(info & 0xff)) : (p.causal ? p.n_qt - 1 - (int)r : (int)r);
   w.bh = split ? (int)(one ? (info & 0xff) | (info >> 26) << 8 : info >> 26) : (int)((unsigned)u - r * BH);
   const int nt = qtile_ntiles(p, w.qt, BM, BN);
-  w.t_begin = split ? (int)((info >> 8) & 0x1ff) : 0;
-  const int len = split ? (int)((info >> 17) & 0x1ff) : nt;
-  w.t_end = w.t_begin + len;
-  w.partial = len < nt;
+  // first key tile and count in granules of 2^unit_shift tiles; the last range of a
+  // tile is clipped to the tile's key tiles
+  w.t_begin = split ? (int)((info >> 8) & 0x1ff) << p.unit_shift : 0;
+  w.t_end = split ? min(w.t_begin + ((int)((info >> 17) & 0x1ff) << p.unit_shift), nt) : nt;
+  w.partial = w.t_end - w.t_begin < nt;
   w.slot = u;
   return w;
 }

@@ -47,6 +47,7 @@ struct Params {
   uint64_t* part_flag;
   uint64_t seq;
   int n_units;        // forward units (blocks 0 .. n_units-1)
+  int unit_shift;     // split plans: the unit table counts key tiles in granules of 2^unit_shift
   int merge_groups;   // merge blocks per split tile and b*h (row groups that hold query rows)
   // Split plans: units enumerate query tiles from the last one; query tile qt owns
   // units ubase .. ubase + B*H*nch - 1, nch ranges for each (b, h), where
@@ -57,7 +58,8 @@ struct Params {
   // depends on the cost model, so they need not be the last ones).
   uint8_t split_qt[kMaxSplitQTiles];
   // Split plans: unit u is query tile (unit_info[u] & 0xff), key tiles from
-  // ((>> 8) & 0x1ff), count ((>> 17) & 0x1ff), b*h (>> 26), so a workgroup decodes its
+  // ((>> 8) & 0x1ff) << unit_shift, count ((>> 17) & 0x1ff) << unit_shift (the last range
+  // of a tile is clipped to the tile's key tiles), b*h (>> 26), so a workgroup decodes its
   // unit with one load. With a single query tile, bits 0-7 hold b*h's low 8 bits and
   // bits 26-31 its next 6 (b*h < 2^14).
   uint32_t unit_info[kMaxSplitUnits];

@@ -110,14 +110,22 @@ typedef struct {
  * recurrence in fp32 from the converted inputs.
  * Ownership: all pointers are caller-owned device memory; the library keeps none of
  * them after the call's device work finishes, and never mutates q, k, v or bias.
- * Split problems (few, long query tiles) need a scratch workspace: fa_fwd uses a
- * buffer the library allocates on first need per (device, stream) and keeps until
- * fa_shutdown(); calls on one stream are ordered, so they never share it unsafely.
- * Such problems run as one kernel on `stream`: workgroups over key ranges, then
- * workgroups that merge each query tile's ranges once those have published their
- * states; while `stream` is capturing a graph, the merge is a second kernel instead.
- * Returns FA_OK or a negative fa_status (see above). Asynchronous: the call returns
- * before the device work finishes.
+ * Scratch memory (the page "编译器与内核", section "生态系统也是目标的一部分", counts a
+ * library's workspace limits, determinism and stream semantics as part of its contract):
+ * split problems (few, long query tiles) need a workspace of
+ * fa_fwd_workspace_size() bytes. fa_fwd takes it from one library-owned buffer per
+ * (device, stream), shared with fa_bwd (calls on one stream run in order, so they
+ * never use it at once; calls on different streams use different buffers). The buffer
+ * only grows: a larger need allocates a new one and keeps the old one allocated until
+ * fa_shutdown(), so it is safe for several host threads to call on one stream. While
+ * `stream` is capturing a graph, fa_fwd returns FA_ERR_WORKSPACE for any problem that
+ * needs scratch memory (a captured graph would keep reusing the shared buffer); use
+ * fa_fwd_ex there. Split problems run as one kernel on `stream`: workgroups over key
+ * ranges, then workgroups that merge each query tile's ranges once those have
+ * published their states; under graph capture the merge is a second kernel instead.
+ * Returns FA_OK or a negative fa_status (see above). Asynchronous (the page
+ * "AI Infra 第5章图解: 算子与运行时", section 5.1, defines a launch as returning before
+ * the device computes): the call returns before the device work finishes.
  */
 int fa_fwd(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
            void* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
@@ -125,14 +133,20 @@ int fa_fwd(const void* q, const void* k, const void* v, const float* bias, int m
 
 /*
  * fa_fwd_workspace_size — bytes of scratch memory that fa_fwd_ex needs for this
- * problem (0 when the problem needs none). Depends only on its arguments and the
- * current device's compute-unit count. Returns 0 for invalid arguments as well.
+ * problem (0 when the problem needs none): the split partial states of the blockwise
+ * method (any partition of the keys into blocks gives the same result, the page
+ * "编译器与内核", section "FlashAttention 围绕 IO 改写算法"), one slot per key range of
+ * (128 * dv) output values in the input dtype, 2 * 128 fp32 row statistics and an
+ * 8-byte flag. Depends only on its arguments and the current device's compute-unit
+ * count. Returns 0 for invalid arguments as well.
  */
 size_t fa_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
                              int dtype, int mask_mode);
 
 /*
- * fa_fwd_ex — fa_fwd with caller-provided scratch memory; allocates nothing.
+ * fa_fwd_ex — fa_fwd with caller-provided scratch memory; allocates nothing (the
+ * workspace contract of the page "编译器与内核", section "生态系统也是目标的一部分").
+ * Safe under graph capture.
  * workspace: device memory of at least fa_fwd_workspace_size(...) bytes, 256-byte
  * aligned; its contents need no initialisation and are scratch after the call. It may
  * be NULL when the size is 0. Two calls that may run concurrently must not share a
@@ -144,7 +158,10 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias, in
               size_t workspace_bytes);
 
 /*
- * fa_fwd_qk — fa_fwd with N_q query rows against N_k keys (N_q, N_k >= 0).
+ * fa_fwd_qk — fa_fwd with N_q query rows against N_k keys (N_q, N_k >= 0). The
+ * definition (the page "编译器与内核", section "FlashAttention 围绕 IO 改写算法") is
+ * row-wise, so N_q rows against N_k keys are the same formula; the causal alignment
+ * below is this library's reading (the pages fix none for N_q != N_k).
  * q: [B, H, N_q, d]; k: [B, H, N_k, d]; v: [B, H, N_k, dv]; out: [B, H, N_q, dv];
  * lse: NULL or [B, H, N_q]; bias: NULL or fp32 [B, H, N_q, N_k] (strides as fa_strides,
  * whose n axes are then N_q for q, out, bias rows and lse, and N_k for k and v; NULL
@@ -157,24 +174,32 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, const float* bias, in
               void* out, float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
               int64_t dv, const fa_strides* strides, int dtype, void* stream);
 
-/* Scratch bytes fa_fwd_qk_ex needs (0 when none, or for invalid arguments). */
+/* Scratch bytes fa_fwd_qk_ex needs (0 when none, or for invalid arguments); as
+ * fa_fwd_workspace_size. */
 size_t fa_fwd_qk_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                                 int64_t dv, int dtype, int mask_mode);
 
-/* fa_fwd_qk with caller-provided scratch memory (as fa_fwd_ex); allocates nothing. */
+/* fa_fwd_qk with caller-provided scratch memory (as fa_fwd_ex); allocates nothing and
+ * is safe under graph capture. */
 int fa_fwd_qk_ex(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
                  void* out, float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                  int64_t dv, const fa_strides* strides, int dtype, void* stream, void* workspace,
                  size_t workspace_bytes);
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL). Errors are part of the contract
+ * surface (the page "编译器与内核", section "生成内核需要一名挑剔的评估者", item
+ * 契约表面); this library reports them as status codes only. */
 const char* fa_status_string(int status);
 
-/* FA_VERSION of the loaded library. */
+/* FA_VERSION of the loaded library (ABI compatibility is part of a library's contract:
+ * the page "编译器与内核", section "生态系统也是目标的一部分"). */
 int fa_version(void);
 
-/* Frees the library-owned workspaces of fa_fwd (synchronises each device first).
- * Safe to call at any time when no fa_fwd call is in flight. */
+/* Frees the library-owned workspaces of fa_fwd and fa_bwd, including the retired ones
+ * (synchronises each device first): the runtime's buffer lifetimes (the page
+ * "编译器与内核", section "内核实现一份有边界的契约", the runtime row of its table).
+ * Call it only when no call of this library is in flight and no captured graph that
+ * used fa_fwd or fa_bwd will be replayed. */
 void fa_shutdown(void);
 
 #ifdef __cplusplus

@@ -56,8 +56,14 @@ typedef struct {
  * dtype: FA_BF16 or FA_F16 (FA_F32 returns FA_ERR_DTYPE); d, dv: 64 or 128.
  * Alignment: every 16-bit tensor base and non-zero stride 16-byte aligned; bias and lse
  * 4-byte aligned. grad_q, grad_k, grad_v must not overlap any input or each other.
- * Workspace: 8 bytes per row (rounded up to 128 rows per (b, h)); fa_bwd uses a
- * library-owned buffer per (device, stream), kept until fa_shutdown().
+ * Workspace: fa_bwd_workspace_size() bytes (the authority): 8 bytes of row statistics
+ * per row (rounded up to 128 rows per (b, h)) and, for problems with few tiles whose
+ * loops are cut into chunks, fp32 partial sums of every chunk unit: units_kv * 128 *
+ * (d + dv) plus units_q * 128 * d floats (tens of MiB for one long head). fa_bwd takes
+ * it from the library-owned buffer of (device, stream) that fa_fwd also uses (include/
+ * fa.h: calls on one stream run in order; the buffer only grows and old buffers stay
+ * allocated until fa_shutdown()). While `stream` captures a graph, fa_bwd returns
+ * FA_ERR_WORKSPACE: captured work takes fa_bwd_ex.
  * Returns FA_OK or a negative fa_status; validation happens before any launch, and a
  * failed call launches nothing. Asynchronous.
  */
@@ -66,12 +72,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
            void* grad_v, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
            const fa_bwd_strides* strides, int dtype, void* stream);
 
-/* Bytes of scratch memory fa_bwd_ex needs (0 for invalid arguments or B*H*N == 0). */
+/* Bytes of scratch memory fa_bwd_ex needs (0 for invalid arguments or B*H*N == 0); the
+ * workspace contract of the page "编译器与内核", section "生态系统也是目标的一部分". */
 size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype,
                              int mask_mode);
 
 /* fa_bwd with caller-provided scratch memory (256-byte aligned, at least
- * fa_bwd_workspace_size bytes, no initialisation needed); allocates nothing. */
+ * fa_bwd_workspace_size bytes, no initialisation needed); allocates nothing and is safe
+ * under graph capture. Same method and numerics as fa_bwd. */
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* out, const float* lse,
               const void* grad_out, const float* bias, int mask_mode, void* grad_q, void* grad_k,
               void* grad_v, int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,

@@ -26,6 +26,7 @@ typedef struct {
   int32_t units;           /* forward workgroups */
   int32_t merge_blocks;    /* merge workgroups appended to the forward grid (split plans) */
   size_t workspace_bytes;  /* as fa_fwd_workspace_size */
+  int32_t unit_tile_shift; /* unit table: first key tile and count in granules of 2^shift tiles */
 } fa_plan_info;
 
 /*
@@ -33,13 +34,21 @@ typedef struct {
  * on a device with `compute_units` compute units. Writes *info (required). If the plan
  * splits and unit_info is not NULL, also writes its unit table, max_units entries at
  * most, one 32-bit word per unit in grid order: query tile (bits 0-7), first key tile
- * (8-16), number of key tiles (17-25), b*h (26-31). Units enumerate the query tiles
- * from the last one; a tile's units are b*h-major, key ranges in order.
+ * (8-16) and number of key tiles (17-25), both in granules of 2^info->unit_tile_shift
+ * key tiles (the count rounded up; the kernel clips a tile's last range to the tile's
+ * key tiles), b*h (26-31); with a single query tile, bits 0-7 hold b*h's low 8 bits and
+ * bits 26-31 its next 6. Units enumerate the query tiles from the last one; a tile's
+ * units are b*h-major, key ranges in order.
  * Returns FA_OK, FA_ERR_SHAPE / FA_ERR_DTYPE / FA_ERR_MASK for invalid arguments, or
  * FA_ERR_NULL when info is NULL or compute_units < 1. Thread-safe; no device calls.
  */
 int fa_plan_describe(int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv, int dtype, int mask_mode,
                      int compute_units, fa_plan_info* info, uint32_t* unit_info, int max_units);
+
+/* fa_plan_describe for N_q query rows against N_k keys (the plan fa_fwd_qk runs). */
+int fa_plan_describe_qk(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, int dtype,
+                        int mask_mode, int compute_units, fa_plan_info* info, uint32_t* unit_info,
+                        int max_units);
 
 #ifdef __cplusplus
 }

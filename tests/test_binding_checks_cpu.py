@@ -1,0 +1,88 @@
+"""CPU: the Python binding rejects tensors that do not match what the C ABI sizes them
+by, before anything reaches the library.
+
+The library derives every extent from q's shape and dereferences every pointer on the
+GPU, so an undersized out / lse / gradient tensor, a host tensor or a tensor on another
+device would be read or written out of bounds. These checks run without a GPU: shape
+and dtype mismatches are found first, then host tensors are refused.
+"""
+
+import pytest
+import torch
+
+from exact_attention_35_amd import capi
+
+
+def _qkv(B=1, H=2, N=10, d=64, dv=64, dtype=torch.bfloat16):
+    q = torch.zeros(B, H, N, d, dtype=dtype)
+    k = torch.zeros(B, H, N, d, dtype=dtype)
+    v = torch.zeros(B, H, N, dv, dtype=dtype)
+    return q, k, v
+
+
+def _status(exc):
+    return exc.value.status
+
+
+def test_out_and_lse_shapes_and_dtypes_are_checked():
+    q, k, v = _qkv()
+    with pytest.raises(capi.FaError) as e:
+        capi.fa_fwd(q, k, v, out=torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16))
+    assert _status(e) == capi.STATUS["FA_ERR_SHAPE"]
+    with pytest.raises(capi.FaError) as e:
+        capi.fa_fwd(q, k, v, out=torch.zeros(1, 2, 10, 64, dtype=torch.float32))
+    assert _status(e) == capi.STATUS["FA_ERR_DTYPE"]
+    with pytest.raises(capi.FaError) as e:
+        capi.fa_fwd(q, k, v, lse=torch.zeros(1, 2, 5))
+    assert _status(e) == capi.STATUS["FA_ERR_SHAPE"]
+    with pytest.raises(capi.FaError) as e:
+        capi.fa_fwd(q, k, v, lse=torch.zeros(1, 2, 10, dtype=torch.float64))
+    assert _status(e) == capi.STATUS["FA_ERR_DTYPE"]
+
+
+def test_bias_must_broadcast():
+    q, k, v = _qkv()
+    with pytest.raises(capi.FaError) as e:
+        capi.fa_fwd(q, k, v, bias=torch.zeros(1, 3, 10, 10))
+    assert _status(e) == capi.STATUS["FA_ERR_SHAPE"]
+    with pytest.raises(capi.FaError) as e:
+        capi.fa_fwd(q, k, v, bias=torch.zeros(1, 2, 10, 9))
+    assert _status(e) == capi.STATUS["FA_ERR_SHAPE"]
+
+
+def test_host_tensors_are_refused_before_any_launch():
+    q, k, v = _qkv()
+    with pytest.raises(capi.FaError, match="not a device tensor"):
+        capi.fa_fwd(q, k, v)
+    with pytest.raises(capi.FaError, match="not a device tensor"):
+        capi.fa_fwd_qk(q, k, v, causal=True)
+    with pytest.raises(capi.FaError, match="not a device tensor"):
+        capi.fa_fwd_ex(q, k, v, None)
+
+
+def test_workspace_must_be_uint8():
+    q, k, v = _qkv()
+    with pytest.raises(capi.FaError) as e:
+        capi.fa_fwd_ex(q, k, v, torch.zeros(16, dtype=torch.float32))
+    assert _status(e) in (capi.STATUS["FA_ERR_WORKSPACE"], capi.STATUS["FA_ERR_NULL"])
+
+
+def test_gradient_arguments_are_checked():
+    q, k, v = _qkv()
+    out = torch.zeros(1, 2, 10, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 10)
+    do = torch.zeros(1, 2, 10, 64, dtype=torch.bfloat16)
+    with pytest.raises(capi.FaError) as e:  # lse is required
+        capi.fa_bwd(q, k, v, out, None, do)
+    assert _status(e) == capi.STATUS["FA_ERR_NULL"]
+    with pytest.raises(capi.FaError) as e:
+        capi.fa_bwd(q, k, v, out, lse, do[:, :, :9])
+    assert _status(e) == capi.STATUS["FA_ERR_SHAPE"]
+    with pytest.raises(capi.FaError) as e:
+        capi.fa_bwd(q, k, v, out, lse, do, grad_q=torch.zeros(1, 2, 10, 32, dtype=torch.bfloat16))
+    assert _status(e) == capi.STATUS["FA_ERR_SHAPE"]
+    with pytest.raises(capi.FaError) as e:
+        capi.fa_bwd(q, k, v, out, lse, do, grad_v=torch.zeros(1, 2, 10, 64, dtype=torch.float16))
+    assert _status(e) == capi.STATUS["FA_ERR_DTYPE"]
+    with pytest.raises(capi.FaError, match="not a device tensor"):
+        capi.fa_bwd(q, k, v, out, lse, do)

@@ -255,6 +255,45 @@ def test_graph_capture_replays_match_eager(gpu_device):
         assert torch.equal(out, o_ref) and torch.equal(lse, l_ref)
 
 
+def test_owned_workspace_refused_under_capture(gpu_device):
+    """While a stream captures a graph, the entry points with a library-owned workspace
+    refuse problems that need scratch memory (a graph would keep reusing the shared
+    buffer) and launch nothing; problems that need none still capture and replay."""
+    import torch
+
+    w = workloads.workload(1).resized(N=1500)  # a split plan
+    _, gpu = _inputs(w, gpu_device)
+    assert capi.fa_fwd_workspace_size(w.B, w.H, w.N, w.d, w.dv, capi.FA_BF16, True) > 0
+    out = torch.empty(w.B, w.H, w.N, w.dv, dtype=torch.bfloat16, device=gpu_device)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=gpu_device)
+    graph = torch.cuda.CUDAGraph()
+    status = None
+    with torch.cuda.graph(graph):
+        try:
+            capi.fa_fwd(gpu["q"], gpu["k"], gpu["v"], causal=True, out=out, lse=lse)
+        except capi.FaError as e:
+            status = e.status
+    assert status == capi.STATUS["FA_ERR_WORKSPACE"]
+    # a problem without a split (enough query tiles) needs no workspace: captured as is
+    w2 = workloads.workload(2).resized(B=2, H=8, N=1024)
+    _, g2 = _inputs(w2, gpu_device)
+    assert capi.fa_fwd_workspace_size(w2.B, w2.H, w2.N, w2.d, w2.dv, capi.FA_BF16, True) == 0
+    o2 = torch.empty(w2.B, w2.H, w2.N, w2.dv, dtype=torch.bfloat16, device=gpu_device)
+    l2 = torch.empty(w2.B, w2.H, w2.N, dtype=torch.float32, device=gpu_device)
+    capi.fa_fwd(g2["q"], g2["k"], g2["v"], causal=True, out=o2, lse=l2)  # warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        capi.fa_fwd(g2["q"], g2["k"], g2["v"], causal=True, out=o2, lse=l2)
+    ref = capi.fa_fwd(g2["q"], g2["k"], g2["v"], causal=True)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        o2.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o2, ref[0]) and torch.equal(l2, ref[1])
+
+
 def test_single_allowed_key_and_constant_v_exact(gpu_device):
     import torch
 

@@ -17,8 +17,9 @@ pytestmark = pytest.mark.skipif(not os.path.exists(capi.library_path()),
                                 reason="libfa.so not built (run __graft_entry__.build())")
 
 
-def ntiles(N, qt, causal, bm=128, bn=64):
-    kv = min(N, (qt + 1) * bm) if causal else N
+def ntiles(N, qt, causal, bm=128, bn=64, Nq=None):
+    coff = 0 if Nq is None else N - Nq
+    kv = max(0, min(N, (qt + 1) * bm + coff)) if causal else N
     return (kv + bn - 1) // bn
 
 
@@ -31,31 +32,36 @@ SHAPES = [  # (B, H, N, d, dv, causal)
     (4, 32, 4096, 128, 128, True), (1, 8, 32768, 128, 128, True), (2, 16, 2048, 64, 128, False),
     (1, 4, 8192, 128, 128, True), (1, 3, 8192, 64, 64, False),
     (8, 32, 100, 128, 128, True), (2, 100, 40, 64, 64, False), (1, 300, 128, 128, 64, True),
+    (1, 1, 32768, 128, 128, False), (1, 1, 32768, 64, 64, True),
 ]
 
 
-@pytest.mark.parametrize("cus", [256, 80])
-@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s}" for s in SHAPES])
-def test_plan_covers_every_key_tile_once(shape, cus):
-    B, H, N, d, dv, causal = shape
-    info, table = capi.fa_plan_describe(B, H, N, d, dv, capi.FA_BF16, causal, cus)
+def check_plan(info, table, B, H, Nq, Nk, dv, causal, cus):
+    """Every (b*h, query tile) sees each of its key tiles in exactly one unit; the
+    packed fields fit; the table keeps the order and limits the kernels rely on."""
     BH = B * H
-    n_qt = math.ceil(N / 128)
+    n_qt = math.ceil(Nq / 128)
     assert (info.n_qtiles, info.qtile_rows, info.key_tile) == (n_qt, 128, 64)
     if not info.split:
         assert info.units == BH * n_qt and info.merge_blocks == 0 and info.workspace_bytes == 0
-        return
+        return 0
     # split only where the query tiles give the CUs fewer than two workgroups each,
     # within the table's limits (b*h < 64, or < 2^14 with a single query tile)
     assert BH * n_qt < 2 * cus and (BH <= 64 or n_qt == 1) and n_qt <= 256
     assert len(table) == info.units <= min(512, 2 * cus)
+    G = 1 << info.unit_tile_shift
+    assert 0 <= info.unit_tile_shift <= 15
     ranges, order = {}, []
     for w in table:
-        qt, t0, n, bh = w & 0xFF, (w >> 8) & 0x1FF, (w >> 17) & 0x1FF, w >> 26
+        qt, g0, gn, bh = w & 0xFF, (w >> 8) & 0x1FF, (w >> 17) & 0x1FF, w >> 26
         if n_qt == 1:  # the query-tile bits hold b*h's low 8 bits
             qt, bh = 0, (w & 0xFF) | (w >> 26) << 8
-        assert n >= 1 and qt < n_qt and bh < BH
-        ranges.setdefault((qt, bh), []).append((t0, n))
+        assert qt < n_qt and bh < BH
+        nt = ntiles(Nk, qt, causal, Nq=Nq)
+        t0, t1 = g0 * G, min(g0 * G + gn * G, nt)  # the kernel's decode: clipped to the tile
+        assert gn >= 1 or nt == 0
+        assert t0 < t1 or nt == 0
+        ranges.setdefault((qt, bh), []).append((t0, t1 - t0))
         order.append(qt)
     assert order == sorted(order, reverse=True)  # query tiles from the last one
     n_split = 0
@@ -67,13 +73,46 @@ def test_plan_covers_every_key_tile_once(shape, cus):
         for t0, n in cuts[0]:
             assert t0 == t
             t += n
-        assert t == ntiles(N, qt, causal)
+        assert t == ntiles(Nk, qt, causal, Nq=Nq)
         n_split += len(cuts[0]) > 1
     assert n_split > 0
     groups = 128 * dv // (1024 * 2)  # row groups of a query tile
-    used = groups if n_qt > 1 else min(groups, -(-N // (128 // groups)))  # groups holding rows
+    used = groups if n_qt > 1 else min(groups, -(-Nq // (128 // groups)))  # groups holding rows
     assert info.merge_blocks == n_split * BH * used
     assert info.workspace_bytes >= info.units * (8 + 2 * 128 * 4 + 128 * dv * 2)
+    return n_split
+
+
+@pytest.mark.parametrize("cus", [256, 80])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s}" for s in SHAPES])
+def test_plan_covers_every_key_tile_once(shape, cus):
+    B, H, N, d, dv, causal = shape
+    info, table = capi.fa_plan_describe(B, H, N, d, dv, capi.FA_BF16, causal, cus)
+    check_plan(info, table, B, H, N, N, dv, causal, cus)
+
+
+RECT = [  # (B, H, N_q, N_k, causal): query tiles whose key ranges need more than 9 bits
+    (1, 1, 1, 32769, True), (1, 1, 1, 40000, True), (1, 1, 1, 65536, False),
+    (1, 8, 1, 65536, True), (1, 32, 1, 131072, True), (1, 1, 1, 600000, True),
+    (1, 1, 128, 600000, False), (2, 2, 300, 70000, True), (1, 1, 1, 4097, True),
+    (8, 32, 1, 8192, True), (1, 1, 2000, 100, True),
+]
+
+
+@pytest.mark.parametrize("cus", [256, 200, 80])
+@pytest.mark.parametrize("shape", RECT, ids=[f"{s}" for s in RECT])
+def test_rectangular_plan_fields_fit(shape, cus):
+    B, H, Nq, Nk, causal = shape
+    info, table = capi.fa_plan_describe_qk(B, H, Nq, Nk, 128, 128, capi.FA_BF16, causal, cus)
+    n_split = check_plan(info, table, B, H, Nq, Nk, 128, causal, cus)
+    longest = max(ntiles(Nk, qt, causal, Nq=Nq) for qt in range(math.ceil(Nq / 128)))
+    if info.split:
+        # the granule is the smallest one whose fields hold the longest tile's key tiles
+        G = 1 << info.unit_tile_shift
+        assert -(-longest // G) <= 511
+        assert info.unit_tile_shift == 0 or -(-longest // (G // 2)) > 511
+    if Nq == 1 and Nk >= 32769 and B * H < cus:
+        assert info.split and n_split == 1  # long decoding rows are still split over keys
 
 
 def test_headline_plan_fills_the_chip():

@@ -33,6 +33,10 @@ CASES = [  # (N_q, N_k, causal, bias, d, dv, B, H)
     (300, 0, False, False, 128, 128, 1, 1),    # no keys at all
     (3, 2000, True, False, 128, 128, 4, 40),   # 160 heads of one query tile: wide b*h split
     (40, 900, True, True, 64, 64, 2, 50),      # a short single tile: merge only its row groups
+    # key ranges longer than the unit table's 9-bit fields (counted in granules of 2^s tiles)
+    (1, 40000, True, False, 128, 128, 1, 1),
+    (2, 65536, False, False, 64, 128, 1, 2),
+    (130, 70000, True, False, 128, 128, 1, 1),
 ]
 
 
