@@ -60,10 +60,11 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _row_block(qbh, kbh, vbh, c_rows, rows, causal, scale, allow_empty_rows):
+def _row_block(qbh, kbh, vbh, c_rows, rows, causal, scale, allow_empty_rows, with_scale=False):
     """Rows `rows` of one (batch, head): the definition, written out in float64.
 
     c_rows is None or the bias rows already selected ([len(rows), N_k]).
+    with_scale: also return the rounding-error scale of O (see `_error_scale`).
     """
     n_q = qbh.shape[0]
     # S = Q K^T / sqrt(d) + C  (C = bias + causal mask)
@@ -90,7 +91,23 @@ def _row_block(qbh, kbh, vbh, c_rows, rows, causal, scale, allow_empty_rows):
     lse = m_safe + np.log(ell_safe)
     o[empty] = 0.0
     lse[empty] = -np.inf
+    if with_scale:
+        return o, lse, _error_scale(p, vbh)
     return o, lse
+
+
+def _error_scale(p, vbh):
+    """Scale of the rounding errors of a 16-bit computation of O (tolerances only).
+
+    Not part of the result. A method that rounds each probability to a 16-bit type
+    before the products P V (relative error at most u per term, independent from term
+    to term) moves O_ik by sum_j delta_ij P_ij v_jk, whose size is set by the
+    root-sum-square of the terms it multiplies:
+        scale_ik = sqrt(sum_j P_ij^2 v_jk^2).
+    The same scale sizes the rounding of partial outputs over key ranges (each a convex
+    combination of its range's v_j, weighted by its share of the probability mass).
+    """
+    return np.sqrt((p ** 2) @ (vbh ** 2))
 
 
 def _bias_slice(bias, b, h):
@@ -103,14 +120,16 @@ def _bias_slice(bias, b, h):
 
 
 def sdpa_reference(q, k, v, bias=None, causal=False, *, row_chunk=2048,
-                   allow_empty_rows=False):
+                   allow_empty_rows=False, with_scale=False):
     """Exact attention forward of every (batch, head) in float64.
 
     q: [B, H, N_q, d], k: [B, H, N_k, d], v: [B, H, N_k, dv] (logical layout; any real
     dtype, torch or numpy; N_q = N_k = N in the square case). bias: None or
     [Bb, Hb, N_q, N_k] with Bb in {1, B} and Hb in {1, H}; -inf entries forbid keys.
     causal: add -inf for keys j > i + (N_k - N_q).
-    Returns (O [B, H, N_q, dv], lse [B, H, N_q]) as float64 numpy arrays.
+    Returns (O [B, H, N_q, dv], lse [B, H, N_q]) as float64 numpy arrays, and with
+    `with_scale` a third item: the rounding-error scale of O ([B, H, N_q, dv], see
+    `_error_scale`), used only to size test tolerances.
     Query rows are processed in chunks of `row_chunk`; rows are independent in the
     definition, so chunking rows changes nothing.
     """
@@ -129,26 +148,33 @@ def sdpa_reference(q, k, v, bias=None, causal=False, *, row_chunk=2048,
     scale = 1.0 / math.sqrt(d)
     out = np.empty((B, H, N, dv), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
+    err = np.empty((B, H, N, dv), dtype=np.float64) if with_scale else None
     for b in range(B):
         for h in range(H):
             cbh = _bias_slice(bias, b, h)
             for r0 in range(0, N, row_chunk):
                 rows = np.arange(r0, min(N, r0 + row_chunk))
                 c_rows = None if cbh is None else cbh[rows]
-                o_, l_ = _row_block(q[b, h], k[b, h], v[b, h], c_rows, rows, causal,
-                                    scale, allow_empty_rows)
-                out[b, h, rows] = o_
-                lse[b, h, rows] = l_
+                res = _row_block(q[b, h], k[b, h], v[b, h], c_rows, rows, causal,
+                                 scale, allow_empty_rows, with_scale)
+                out[b, h, rows] = res[0]
+                lse[b, h, rows] = res[1]
+                if with_scale:
+                    err[b, h, rows] = res[2]
+    if with_scale:
+        return out, lse, err
     return out, lse
 
 
-def sdpa_reference_rows(q, k, v, bias, causal, b, h, rows, *, allow_empty_rows=False):
+def sdpa_reference_rows(q, k, v, bias, causal, b, h, rows, *, allow_empty_rows=False,
+                        with_scale=False):
     """The same definition for selected query rows of one (batch, head).
 
     Used at sizes where the full N_q x N_k problem is too large for the CPU: each
     sampled row is computed on its own, exactly as in `sdpa_reference`.
     q is [B, H, N_q, *], k and v are [B, H, N_k, *] (torch or numpy, any layout; only the needed slices are
-    converted); bias as in `sdpa_reference`. Returns (O [len(rows), dv], lse [len(rows)]).
+    converted); bias as in `sdpa_reference`. Returns (O [len(rows), dv], lse [len(rows)]),
+    and with `with_scale` the rounding-error scale of those rows of O.
     """
     rows = np.asarray(rows, dtype=np.int64)
     qbh = _as_f64(q[b, h])
@@ -162,4 +188,4 @@ def sdpa_reference_rows(q, k, v, bias, causal, b, h, rows, *, allow_empty_rows=F
         sl = bias[b if bb > 1 else 0, h if bh > 1 else 0]
         c_rows = _as_f64(sl[rows.tolist()])
     return _row_block(qbh, kbh, vbh, c_rows, rows, causal, 1.0 / math.sqrt(d),
-                      allow_empty_rows)
+                      allow_empty_rows, with_scale)

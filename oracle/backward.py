@@ -80,27 +80,41 @@ def _row_block_grads(qbh, kbh, vbh, dobh, c_rows, rows, causal, scale, allow_emp
     return dq, dk_part, dv_part, _error_scales(p, ds, qbh[rows], kbh, vbh, do, scale)
 
 
-def _error_scales(p, ds, q_rows, kbh, vbh, do, scale, cols=None):
-    """Scales of the rounding errors of a bf16 gradient computation (tolerances only).
+# Rounding-error scales of a 16-bit gradient computation (tolerances only; not part of
+# the result). A rounded operand adds to a sum an error proportional to its term;
+# independent roundings add in quadrature, so each gradient element gets the
+# root-sum-square of its terms, plus the term of D_i = dO_i . O_i, whose error (O is
+# given in 16 bits) is proportional to A_i = sum_k |dO_ik O_ik| and is shared by every
+# key of row i (so it enters dQ_i in full, and dK_j in quadrature over rows):
+#     sv^2 = (P^2)^T (dO^2),
+#     sk^2 = scale^2 (dS^2 + (P A)^2)^T (Q^2),
+#     sq   = scale (sqrt((dS^2 + (u P A)^2) (K^2)) + A |P K|).
+# In sq, the dS that a kernel rounds carries D's error (up to u A_i P_ij, u = 2^-8 the
+# unit roundoff of bf16, the coarser 16-bit type), so its rounding scales with
+# |dS| + u P A; that second-order term matters only where P K cancels.
 
-    Not part of the result. A rounded operand adds to a sum an error proportional to
-    its term; independent roundings add in quadrature, so each gradient element gets
-    the root-sum-square of its terms, plus the term of D_i = dO_i . O_i, whose error
-    (O is given in bf16) is proportional to A_i = sum_k |dO_ik O_ik| and is shared by
-    every key of row i (so it enters dQ_i in full, and dK_j in quadrature over rows):
-        sv^2 = (P^2)^T (dO^2),
-        sk^2 = scale^2 (dS^2 + (P A)^2)^T (Q^2),
-        sq   = scale (sqrt((dS^2) (K^2)) + A |P K|).
-    Returns sq (rows), and the rows' contributions to sk^2 and sv^2 (of the key
-    columns `cols` only, when given)."""
-    o = p @ vbh
-    a = (np.abs(do) * np.abs(o)).sum(axis=1)
-    sq = scale * (np.sqrt((ds ** 2) @ kbh ** 2) + a[:, None] * np.abs(p @ kbh))
-    if cols is not None:
-        p, ds = p[:, cols], ds[:, cols]
+def _d_error_scale(o, do):
+    """A_i = sum_k |dO_ik O_ik|: the size of D_i's error per unit of relative error in O."""
+    return (np.abs(do) * np.abs(o)).sum(axis=1)
+
+
+def _dq_scale(p, ds, kbh, a, scale):
+    """sq for rows with probabilities p and dS ds over all keys."""
+    u = 2.0 ** -8
+    return scale * (np.sqrt((ds ** 2 + (u * p * a[:, None]) ** 2) @ kbh ** 2) + a[:, None] * np.abs(p @ kbh))
+
+
+def _dkdv_scales(p, ds, q_rows, a, do, scale):
+    """The rows' contributions to sk^2 and sv^2 of the key columns that p and ds hold."""
     sk2 = scale ** 2 * ((ds ** 2 + (p * a[:, None]) ** 2).T @ q_rows ** 2)
     sv2 = (p ** 2).T @ do ** 2
-    return sq, sk2, sv2
+    return sk2, sv2
+
+
+def _error_scales(p, ds, q_rows, kbh, vbh, do, scale):
+    """sq of the rows, and the rows' contributions to sk^2 and sv^2 (all keys)."""
+    a = _d_error_scale(p @ vbh, do)
+    return (_dq_scale(p, ds, kbh, a, scale),) + _dkdv_scales(p, ds, q_rows, a, do, scale)
 
 
 def _check_shapes(q, k, v, dout, bias):
@@ -158,9 +172,13 @@ def sdpa_backward_reference_sampled(q, k, v, dout, bias, causal, b, h, rows, key
     """dQ at query rows `rows` and dK, dV at key rows `keys` of one (batch, head).
 
     For sizes where the full gradients are too large for the CPU: dQ of a row needs only
-    that row; dK and dV of a key need every row's probabilities, so all rows are formed
-    chunk by chunk (S and dP in full, O(N^2 (d + dv)) work) and only the sampled key
-    columns of P and dS are kept. Same definition as `sdpa_backward_reference`.
+    that row; dK and dV of a key need every row's probability of it, so all rows are
+    formed chunk by chunk (S and P of each row in full, for its normaliser, and O = P V
+    for D_i = dO_i . O_i, which equals sum_k P_ik dP_ik) and dP, dS are formed only in
+    the sampled key columns. Under the causal mask, rows i see keys j <= i only, so a
+    chunk of rows needs no key past its last row, and rows before the first sampled key
+    add nothing to it (their probabilities of it are 0). Same definition as
+    `sdpa_backward_reference`.
     Returns (dQ [len(rows), d], dK [len(keys), d], dV [len(keys), dv]).
     """
     rows = np.asarray(rows, dtype=np.int64)
@@ -171,23 +189,32 @@ def sdpa_backward_reference_sampled(q, k, v, dout, bias, causal, b, h, rows, key
     sl = None
     if bias is not None:
         sl = bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0]
-    c_of = (lambda r: None) if sl is None else (lambda r: _as_f64(sl[r.tolist()]))
-    res = _row_block_grads(qbh, kbh, vbh, dobh, c_of(rows), rows, causal, scale, False, with_scales)
+    c_of = (lambda r, nk: None) if sl is None else (lambda r, nk: _as_f64(sl[r.tolist()])[:, :nk])
+    res = _row_block_grads(qbh, kbh, vbh, dobh, c_of(rows, N), rows, causal, scale, False, with_scales)
     dq = res[0]
     dk = np.zeros((len(keys), d))
     dv = np.zeros((len(keys), vbh.shape[1]))
     sk2, sv2 = np.zeros_like(dk), np.zeros_like(dv)
+    first = int(keys.min()) if len(keys) else N
     for r0 in range(0, N, row_chunk):
         rr = np.arange(r0, min(N, r0 + row_chunk))
-        p = _probabilities(qbh, kbh, c_of(rr), rr, causal, scale, False)
-        dp = dobh[rr] @ vbh.T
-        ds = p * (dp - (p * dp).sum(axis=1)[:, None])
-        dv += p[:, keys].T @ dobh[rr]
-        dk += (ds[:, keys].T @ qbh[rr]) * scale
+        if causal and rr[-1] < first:
+            continue
+        nk = int(rr[-1]) + 1 if causal else N    # keys any of these rows may see
+        sel = np.nonzero(keys < nk)[0]
+        p = _probabilities(qbh, kbh[:nk], c_of(rr, nk), rr, causal, scale, False)
+        o = p @ vbh[:nk]
+        do = dobh[rr]
+        dd = (do * o).sum(axis=1)                    # D_i = dO_i . O_i
+        pk = p[:, keys[sel]]
+        dpk = do @ vbh[keys[sel]].T                  # dP in the sampled columns
+        dsk = pk * (dpk - dd[:, None])               # dS in the sampled columns
+        dv[sel] += pk.T @ do
+        dk[sel] += (dsk.T @ qbh[rr]) * scale
         if with_scales:
-            _, k2, v2 = _error_scales(p, ds, qbh[rr], kbh, vbh, dobh[rr], scale, cols=keys)
-            sk2 += k2
-            sv2 += v2
+            k2, v2 = _dkdv_scales(pk, dsk, qbh[rr], _d_error_scale(o, do), do, scale)
+            sk2[sel] += k2
+            sv2[sel] += v2
     if with_scales:
         return dq, dk, dv, (res[3][0], np.sqrt(sk2), np.sqrt(sv2))
     return dq, dk, dv

@@ -25,14 +25,40 @@ F16_MFMA_ATOL = 5e-3
 F16_MFMA_RTOL = 2.5e-3
 
 
+# Error-scale bar for 16-bit inputs on the matrix cores, applied together with the bars
+# above. The probabilities are rounded to the 16-bit type (relative error <= u: 2^-8 for
+# bf16, 2^-11 for fp16) before the P V products, and split problems round each key
+# range's partial output once more; the oracle's scale S_ik = sqrt(sum_j P_ij^2 v_jk^2)
+# is the root-sum-square of the terms those roundings multiply. Bar:
+#   |dO| <= 4 u S + 2 u |O_ref|
+# four roundings' worth of the root-sum-square (the error of a sum of independent
+# roundings has standard deviation <= u S / sqrt(3) per source, so this is > 4.9
+# standard deviations with two sources), and two half-ulps of |O| (the output's own
+# rounding, plus the mean part of the partial outputs' rounding).
+SCALE_TOL = {"bf16": 2.0 ** -6, "f16_mfma": 2.0 ** -9}
+SCALE_RTOL = {"bf16": 2.0 ** -7, "f16_mfma": 2.0 ** -10}
+
+
 def to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def check_out(o_gpu, o_ref, dtype, where=""):
+def check_out(o_gpu, o_ref, dtype, where="", scale=None):
+    """Element-wise bar of the dtype; with the oracle's error scale (16-bit inputs on
+    the matrix cores), also the error-scale bar SCALE_TOL * S + SCALE_RTOL * |O_ref|.
+    Returns max |dO|; prints the worst ratio to the error-scale bar when it is used."""
     o = to_np(o_gpu) if not isinstance(o_gpu, np.ndarray) else o_gpu
     assert np.isfinite(o).all(), f"non-finite output {where}"
     err = np.abs(o - o_ref)
+    if scale is not None and dtype in SCALE_TOL and err.size:
+        bar = SCALE_TOL[dtype] * scale + SCALE_RTOL[dtype] * np.abs(o_ref)
+        tiny = bar <= 0  # rows whose every weight sits on zero values: exact results
+        ratio = np.where(tiny, np.where(err > 0, np.inf, 0.0), err / np.where(tiny, 1.0, bar))
+        worst = float(ratio.max())
+        print(f"[parity] {where}: worst |dO| / error-scale bar = {worst:.3g}", flush=True)
+        bad = ratio > 1.0
+        assert not bad.any(), (f"{int(bad.sum())} elements beyond the error-scale bar {where}; "
+                               f"worst |dO| / bar = {worst:.3g}")
     if dtype == "f32":
         worst = float(err.max()) if err.size else 0.0
         assert worst <= F32_ATOL, f"max |dO| = {worst:.3g} > {F32_ATOL} {where}"

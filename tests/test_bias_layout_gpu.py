@@ -68,7 +68,7 @@ def test_aligned_and_unaligned_bias_rows_agree_and_match_oracle(gpu_device, case
     o_r, l_r = fwd(qd, kd, vd, bias=regs, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o_s, o_r) and torch.equal(l_s, l_r), "vector and element bias loads differ"
-    o_ref, l_ref = sdpa_reference(q, k, v, bias, causal)
+    o_ref, l_ref, sc = sdpa_reference(q, k, v, bias, causal, with_scale=True)
     key = "bf16" if dtype == "bf16" else "f16_mfma"
-    check_out(o_s, o_ref, key, str(case))
+    check_out(o_s, o_ref, key, str(case), scale=sc)
     check_lse(l_s, l_ref, str(case))

@@ -123,6 +123,7 @@ FULL = [
     (1, [(0, 0)], [0, 1, 127, 128, 4095, 8000, 8191], [0, 1, 63, 64, 4000, 8190, 8191]),
     (2, [(3, 31), (1, 7)], [0, 100, 2047, 4095], [0, 64, 3000, 4095]),
     (3, [(1, 15), (0, 2)], [0, 1, 1023, 2047], [0, 5, 1500, 2047]),
+    (4, [(0, 3)], [0, 1, 127, 128, 16000, 32766, 32767], [0, 1, 63, 64, 20000, 32766, 32767]),
 ]
 
 

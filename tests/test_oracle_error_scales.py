@@ -1,0 +1,322 @@
+"""CPU: the oracle's rounding-error scales, which size the 16-bit parity bars, pinned
+against a plain emulation of 16-bit arithmetic and against planted mistakes.
+
+The oracle returns, beside each result, the scale of the rounding errors a 16-bit
+computation of it makes (forward: `oracle.attention._error_scale`; gradients:
+`oracle.backward._error_scales`). A scale that is too large would let real bugs pass;
+one that is too small would fail correct kernels. Both directions are pinned here
+without a GPU:
+
+  * an emulation of the rounding steps a 16-bit kernel takes (numpy fp32 arithmetic,
+    round-to-nearest-even to bf16 / fp16 where the kernel rounds) stays well inside
+    the bar built from the scale (worst |error| / bar <= 0.6; <= 0.75 for the forward
+    with keys cut into ranges, whose partial outputs are rounded once more) on tiny and
+    mid-size cases, including a case built so that the error of D_i = dO_i . O_i (O given in
+    16 bits) dominates the gradients;
+  * each planted slip in the scale formulas (a dropped term, 1/d for 1/sqrt(d)) makes
+    that emulation exceed its bar somewhere;
+  * the forward bar rejects three plausible kernel bugs on the last query tile of the
+    single causal head of length 8192 (a value tile read from its neighbour, O scaled
+    by 0.9, a 512-key range dropped), which the benchmark spec bar alone does not see;
+  * closed forms: one allowed key gives scale |v_j|; uniform weights over n keys with
+    values +-1 give 1/sqrt(n).
+
+The tolerance follows the page "编译器与内核", section "生成内核需要一名挑剔的评估者",
+item 隐藏语义: it is derived from the dtype and the reduction length, independently of
+the kernel under test.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.backward as ob
+from exact_attention_35_amd import workloads
+from oracle import sdpa_backward_reference, sdpa_reference, sdpa_reference_rows
+from parity_util import (GRAD_RTOL, GRAD_RTOL_F16, GRAD_SCALE_TOL, GRAD_SCALE_TOL_F16, SCALE_RTOL,
+                         SCALE_TOL, check_out)
+
+LOG2E = 1.4426950408889634
+
+
+def r16(x, dt):
+    """Round an fp32 array to bf16 / fp16 (round to nearest even), back as fp32."""
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(tdt).float().numpy()
+
+
+def f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+def _mask(nq, nk, causal, bias):
+    c = np.zeros((nq, nk), dtype=np.float32) if bias is None else f32(bias)
+    if causal:
+        c = np.where(np.arange(nk)[None, :] > np.arange(nq)[:, None] + (nk - nq), -np.inf, c)
+    return f32(c)
+
+
+def emulate_fwd(q, k, v, bias, causal, dt, rows=None, range_keys=None):
+    """One head of the forward in the arithmetic a 16-bit matrix-core kernel uses:
+    fp32 scores, base-2 exponentials against the row max, probabilities rounded to the
+    16-bit type for P V (the normaliser sums them unrounded), fp32 accumulation; with
+    range_keys, keys are cut into ranges whose normalised partial outputs are rounded to
+    16 bits and merged with fp32 weights. Returns O rounded to 16 bits."""
+    q, k, v = f32(q), f32(k), f32(v)
+    nq_all, nk = q.shape[0], k.shape[0]
+    rows = np.arange(nq_all) if rows is None else np.asarray(rows)
+    d = q.shape[1]
+    c = _mask(nq_all, nk, causal, bias)[rows]
+    s = q[rows] @ k.T
+    x = f32((s * f32(1.0 / math.sqrt(d)) + c) * f32(LOG2E))
+    cuts = [(0, nk)] if range_keys is None else [(a, min(nk, a + range_keys)) for a in range(0, nk, range_keys)]
+    parts = []
+    for a, b in cuts:
+        xb = x[:, a:b]
+        m = xb.max(axis=1)
+        m_safe = np.where(np.isfinite(m), m, 0.0).astype(np.float32)
+        p = np.exp2(xb - m_safe[:, None]).astype(np.float32)
+        ell = p.sum(axis=1, dtype=np.float32)
+        num = r16(p, dt) @ v[a:b]
+        with np.errstate(invalid="ignore", divide="ignore"):
+            o = num / np.where(ell > 0, ell, 1.0)[:, None]
+        parts.append((r16(o, dt) if len(cuts) > 1 else o, m, ell))
+    if len(parts) == 1:
+        return r16(parts[0][0], dt)
+    m = np.max([pm for _, pm, _ in parts], axis=0)
+    w = [np.where(np.isfinite(pm), np.exp2(pm - m), 0.0).astype(np.float32) * pl for _, pm, pl in parts]
+    ell = np.sum(w, axis=0, dtype=np.float32)
+    o = sum(wp[:, None] * op for (op, _, _), wp in zip(parts, w)) / ell[:, None]
+    return r16(o, dt)
+
+
+def emulate_bwd(q, k, v, o16, lse, do, bias, causal, dt):
+    """One head of the gradients in the arithmetic of a 16-bit matrix-core kernel:
+    P = exp(S / sqrt(d) + C - lse) in fp32, D_i = dO_i . O_i from the 16-bit O, dP in
+    fp32, dS = P (dP - D) rounded to 16 bits, P rounded to 16 bits, products accumulated
+    in fp32, each gradient rounded to 16 bits once."""
+    q, k, v, do, o16 = f32(q), f32(k), f32(v), f32(do), f32(o16)
+    n, d = q.shape
+    sc = f32(1.0 / math.sqrt(d))
+    c = _mask(n, n, causal, bias)
+    s = (q @ k.T) * sc + c
+    p = np.exp(s - f32(lse)[:, None]).astype(np.float32)
+    dd = (do * o16).sum(axis=1, dtype=np.float32)
+    dp = do @ v.T
+    ds = p * (dp - dd[:, None])
+    p16, ds16 = r16(p, dt), r16(ds, dt)
+    dv = r16(p16.T @ do, dt)
+    dk = r16((ds16.T @ q) * sc, dt)
+    dq = r16((ds16 @ k) * sc, dt)
+    return dq, dk, dv
+
+
+def fwd_ratio(o_emu, o_ref, scale, dt):
+    bar = SCALE_TOL[dt] * scale + SCALE_RTOL[dt] * np.abs(o_ref)
+    return float((np.abs(o_emu - o_ref) / bar).max())
+
+
+def grad_ratio(g_emu, g_ref, sc, dt):
+    tol, rtol = (GRAD_SCALE_TOL, GRAD_RTOL) if dt == "bf16" else (GRAD_SCALE_TOL_F16, GRAD_RTOL_F16)
+    bound = tol * sc + rtol * np.abs(g_ref) + 1e-6 * float(sc.max())
+    return float((np.abs(g_emu - g_ref) / bound).max())
+
+
+def _case(N, d, dv, causal, bias, dt, seed, qk_sigma=1.0, mask_p=0.1):
+    w = workloads.Workload("emu", B=1, H=1, N=N, d=d, dv=dv, dtype=dt, layout="bhnd", causal=causal,
+                           bias=bias, mask_p=mask_p if bias else 0.0, q_sigma=qk_sigma, k_sigma=qk_sigma,
+                           seed=seed)
+    inp = workloads.make_inputs(w)
+    do = workloads.make_grad_out(w)
+    f = lambda t: None if t is None else t[0, 0].float().numpy()  # noqa: E731
+    return w, {n: f(t) for n, t in inp.items()}, f(do), inp, do
+
+
+CASES = [  # (N, d, dv, causal, bias, dtype, seed, qk_sigma)
+    (64, 128, 128, True, False, "bf16", 1, 1.0),
+    (300, 128, 128, True, False, "bf16", 2, 1.0),
+    (1000, 128, 128, True, False, "bf16", 3, 1.0),
+    (700, 64, 128, False, True, "bf16", 4, 1.0),
+    (900, 128, 128, True, False, "bf16", 5, 2.0),   # peaked scores
+    (500, 128, 64, False, False, "bf16", 6, 1.0),
+    (300, 128, 128, True, False, "f16", 7, 1.0),
+    (700, 64, 128, False, True, "f16", 8, 1.0),
+]
+
+
+def _constant_mean_case(dt):
+    """Built so that the error of D_i = dO_i . O_i dominates: every value is 1 or 1 + 2^-7
+    (a quarter of them), so each O_ik lies near 1 + 2^-9 and its 16-bit rounding moves it
+    by about -2^-9, the same way in every element; with dO = 1, D_i then carries an error
+    of about -d_v 2^-9 while dP_ij - D_i is small."""
+    rng = np.random.default_rng(123)
+    N, d, dv = 256, 128, 128
+    q = r16(rng.standard_normal((N, d)).astype(np.float32), dt)
+    k = r16(rng.standard_normal((N, d)).astype(np.float32), dt)
+    v = np.where(rng.random((N, dv)) < 0.25, 1.0 + 2.0 ** -7, 1.0).astype(np.float32)
+    do = np.ones((N, dv), dtype=np.float32)
+    return q, k, v, do
+
+
+def _emulate_both(q, k, v, do, bias, causal, dt):
+    o16 = emulate_fwd(q, k, v, bias, causal, dt)
+    o_ref, lse_ref = sdpa_reference(q[None, None], k[None, None], v[None, None],
+                                    None if bias is None else bias[None, None], causal)
+    # the forward kernel's lse is accurate to fp32 rounding: take the oracle's, in fp32
+    g_emu = emulate_bwd(q, k, v, o16, lse_ref[0, 0], do, bias, causal, dt)
+    refs = sdpa_backward_reference(q[None, None], k[None, None], v[None, None], do[None, None],
+                                   None if bias is None else bias[None, None], causal, with_scales=True)
+    return g_emu, refs
+
+
+# ---------------------------------------------------------------- forward scale
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[5]}-n{c[0]}-d{c[1]}-{c[2]}-c{int(c[3])}-b{int(c[4])}" for c in CASES])
+@pytest.mark.parametrize("range_keys", [None, 512, 64])
+def test_forward_emulation_inside_error_scale_bar(case, range_keys):
+    N, d, dv, causal, bias, dt, seed, sig = case
+    dtk = "bf16" if dt == "bf16" else "f16_mfma"
+    w, x, _, inp, _ = _case(N, d, dv, causal, bias, dt, seed, sig)
+    o_ref, _, sc = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], causal, with_scale=True)
+    b = None if x["bias"] is None else x["bias"]
+    o_emu = emulate_fwd(x["q"], x["k"], x["v"], b, causal, dt, range_keys=range_keys)
+    ratio = fwd_ratio(o_emu, o_ref[0, 0], sc[0, 0], dtk)
+    print(f"forward {case} ranges={range_keys}: worst |err| / bar = {ratio:.3f}")
+    # one rounding of P~ per term: <= 0.6; a split adds the partial outputs' rounding
+    assert ratio <= (0.6 if range_keys is None else 0.75)
+    check_out(o_emu, o_ref[0, 0], dtk, str(case), scale=sc[0, 0])
+
+
+def test_forward_scale_closed_forms():
+    # one allowed key (the diagonal of a causal row 0, or a bias row with one finite
+    # entry): P = 1 on that key, so the scale is |v_j|
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 6, 8))
+    k = rng.standard_normal((1, 1, 6, 8))
+    v = rng.standard_normal((1, 1, 6, 4))
+    bias = np.full((1, 1, 6, 6), -np.inf)
+    bias[0, 0, np.arange(6), [3, 0, 5, 5, 1, 2]] = 0.7
+    _, _, sc = sdpa_reference(q, k, v, bias, False, with_scale=True)
+    assert np.allclose(sc[0, 0], np.abs(v[0, 0, [3, 0, 5, 5, 1, 2]]), rtol=1e-15)
+    # uniform weights (Q = 0) over n keys with values +-1: sqrt(n * (1/n)^2) = 1/sqrt(n)
+    n = 37
+    vv = np.where(rng.random((1, 1, n, 5)) < 0.5, -1.0, 1.0)
+    _, _, sc = sdpa_reference(np.zeros((1, 1, 1, 3)), rng.standard_normal((1, 1, n, 3)), vv, None, False,
+                              with_scale=True)
+    assert np.allclose(sc, 1.0 / math.sqrt(n), rtol=1e-14)
+    # the row-sampled variant returns the same scale rows
+    qq, kk, v2 = (rng.standard_normal((1, 2, 50, 16)) for _ in range(3))
+    _, _, full = sdpa_reference(qq, kk, v2, None, True, with_scale=True)
+    _, _, part = sdpa_reference_rows(qq, kk, v2, None, True, 0, 1, [0, 7, 49], with_scale=True)
+    assert np.allclose(part, full[0, 1, [0, 7, 49]], rtol=1e-14)
+
+
+@pytest.fixture(scope="module")
+def headline_last_tile():
+    w = workloads.workload(1)  # the single causal head, N = 8192, d = dv = 128
+    inp = workloads.make_inputs(w)
+    rows = np.arange(w.N - 128, w.N)
+    o_ref, _, sc = sdpa_reference_rows(inp["q"], inp["k"], inp["v"], None, True, 0, 0, rows, with_scale=True)
+    return w, inp, rows, o_ref, sc
+
+
+def test_forward_bar_accepts_emulated_kernel_on_headline_tile(headline_last_tile):
+    w, inp, rows, o_ref, sc = headline_last_tile
+    f = lambda t: t[0, 0].float().numpy()  # noqa: E731
+    for range_keys in (None, 512):
+        o_emu = emulate_fwd(f(inp["q"]), f(inp["k"]), f(inp["v"]), None, True, "bf16", rows=rows,
+                            range_keys=range_keys)
+        ratio = fwd_ratio(o_emu, o_ref, sc, "bf16")
+        print(f"headline last tile, ranges={range_keys}: worst |err| / bar = {ratio:.3f}")
+        assert ratio <= (0.6 if range_keys is None else 0.75)
+
+
+def test_forward_bar_rejects_planted_bugs_on_headline_tile(headline_last_tile):
+    """Three kernel bugs, planted in oracle runs on the CPU, on rows 8064..8191 of the
+    single causal head of 8192: each must fail the error-scale bar."""
+    w, inp, rows, o_ref, sc = headline_last_tile
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    # (i) one 64-key value tile read from its neighbour
+    v_bad = v.clone()
+    v_bad[0, 0, 40 * 64:41 * 64] = v[0, 0, 41 * 64:42 * 64]
+    o_swap, _ = sdpa_reference_rows(q, k, v_bad, None, True, 0, 0, rows)
+    # (ii) O scaled by 0.9
+    o_scaled = 0.9 * o_ref
+    # (iii) a 512-key range left out (the rest renormalised)
+    drop = torch.zeros(1, 1, w.N, w.N)
+    drop[0, 0, :, 1024:1536] = float("-inf")
+    o_drop, _ = sdpa_reference_rows(q, k, v, drop, True, 0, 0, rows)
+    for name, o_bad in (("value tile swap", o_swap), ("O x 0.9", o_scaled), ("dropped key range", o_drop)):
+        # the benchmark spec bar alone: how many elements it flags (reported, not asserted)
+        ns_bad = int((np.abs(o_bad - o_ref) > 2e-2 + 1e-2 * np.abs(o_ref)).sum())
+        with pytest.raises(AssertionError):
+            check_out(o_bad, o_ref, "bf16", name, scale=sc)
+        print(f"{name}: north_star bar flags {ns_bad} of {o_ref.size} elements; error-scale bar rejects")
+
+
+# ---------------------------------------------------------------- gradient scales
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[5]}-n{c[0]}-d{c[1]}-{c[2]}-c{int(c[3])}-b{int(c[4])}" for c in CASES])
+def test_gradient_emulation_inside_error_scale_bar(case):
+    N, d, dv, causal, bias, dt, seed, sig = case
+    _, x, do, _, _ = _case(N, d, dv, causal, bias, dt, seed, sig)
+    g_emu, refs = _emulate_both(x["q"], x["k"], x["v"], do, x["bias"], causal, dt)
+    for name, ge, gr, sc in zip(("dQ", "dK", "dV"), g_emu, refs[:3], refs[3]):
+        ratio = grad_ratio(ge, gr[0, 0], sc[0, 0], dt)
+        print(f"{case} {name}: worst |err| / bound = {ratio:.3f}")
+        assert ratio <= 0.6, f"{name} {ratio}"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_gradient_emulation_inside_bar_when_d_error_dominates(dt):
+    q, k, v, do = _constant_mean_case(dt)
+    g_emu, refs = _emulate_both(q, k, v, do, None, False, dt)
+    for name, ge, gr, sc in zip(("dQ", "dK", "dV"), g_emu, refs[:3], refs[3]):
+        ratio = grad_ratio(ge, gr[0, 0], sc[0, 0], dt)
+        print(f"D-dominated {dt} {name}: worst |err| / bound = {ratio:.3f}")
+        assert ratio <= 0.6, f"{name} {ratio}"
+
+
+# Planted slips in the gradient scale formulas (each a plausible mistake in writing
+# them): the emulation must then exceed the bar somewhere.
+_DQ, _DKDV = ob._dq_scale, ob._dkdv_scales
+
+
+def _slip_drop_pa_in_sk(p, ds, q_rows, a, do, scale):
+    sk2, sv2 = _DKDV(p, ds, q_rows, a, do, scale)
+    return scale ** 2 * ((ds ** 2).T @ q_rows ** 2), sv2
+
+
+def _slip_drop_a_in_sq(p, ds, kbh, a, scale):
+    return _DQ(p, ds, kbh, a, scale) - scale * a[:, None] * np.abs(p @ kbh)
+
+
+def _slip_inv_d_in_sq(p, ds, kbh, a, scale):
+    return _DQ(p, ds, kbh, a, scale) * scale  # 1/d where 1/sqrt(d) belongs
+
+
+def _slip_inv_d_in_sk(p, ds, q_rows, a, do, scale):
+    sk2, sv2 = _DKDV(p, ds, q_rows, a, do, scale)
+    return sk2 * scale ** 2, sv2  # 1/d^2 where 1/d belongs
+
+
+@pytest.mark.parametrize("slip,target,grad", [(_slip_drop_pa_in_sk, "_dkdv_scales", "dK"),
+                                              (_slip_drop_a_in_sq, "_dq_scale", "dQ"),
+                                              (_slip_inv_d_in_sq, "_dq_scale", "dQ"),
+                                              (_slip_inv_d_in_sk, "_dkdv_scales", "dK")],
+                         ids=["drop-PA-in-sk", "drop-A|PK|-in-sq", "1/d-for-1/sqrt(d)-in-sq",
+                              "1/d^2-for-1/d-in-sk"])
+def test_planted_scale_slips_fail(monkeypatch, slip, target, grad):
+    monkeypatch.setattr(ob, target, slip)
+    worst = 0.0
+    cases = [(_constant_mean_case("bf16"), None, False, "bf16")]
+    _, x, do, _, _ = _case(300, 128, 128, True, False, "bf16", 2)
+    cases.append(((x["q"], x["k"], x["v"], do), None, True, "bf16"))
+    for (q, k, v, g), bias, causal, dt in cases:
+        g_emu, refs = _emulate_both(q, k, v, g, bias, causal, dt)
+        i = ("dQ", "dK", "dV").index(grad)
+        worst = max(worst, grad_ratio(g_emu[i], refs[i][0, 0], refs[3][i][0, 0], dt))
+    print(f"{slip.__name__}: worst {grad} |err| / bound = {worst:.3g}")
+    assert worst > 1.0

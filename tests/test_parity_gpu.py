@@ -71,8 +71,8 @@ def test_bf16_small_elementwise(gpu_device, idx, over):
     w = workloads.workload(idx).resized(**over)
     inp, gpu = _inputs(w, gpu_device)
     out, lse = _run(gpu, w, gpu_device)
-    o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
-    check_out(out, o_ref, "bf16", w.name + str(over))
+    o_ref, l_ref, sc = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal, with_scale=True)
+    check_out(out, o_ref, "bf16", w.name + str(over), scale=sc)
     check_lse(lse, l_ref, w.name + str(over))
 
 
@@ -86,8 +86,8 @@ def test_edge_shapes(gpu_device, N, d, dv, dtype):
                                seed=N * 1000 + d + dv)
         inp, gpu = _inputs(w, gpu_device)
         out, lse = _run(gpu, w, gpu_device)
-        o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
-        check_out(out, o_ref, dtype, f"N={N} d={d} dv={dv} causal={causal}")
+        o_ref, l_ref, sc = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal, with_scale=True)
+        check_out(out, o_ref, dtype, f"N={N} d={d} dv={dv} causal={causal}", scale=sc)
         check_lse(lse, l_ref, f"N={N} d={d} dv={dv}")
 
 
@@ -111,10 +111,60 @@ def test_bf16_full_size_sampled(gpu_device, idx):
     pairs += [(0, 0), (w.B - 1, w.H - 1)]
     for b, h in sorted(set(pairs)):
         rows = _sample_rows(w.N, rng)
-        o_ref, l_ref = sdpa_reference_rows(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal,
-                                           b, h, rows)
-        check_out(to_np(out_c[b, h, rows]), o_ref, "bf16", f"{w.name} b={b} h={h}")
+        o_ref, l_ref, sc = sdpa_reference_rows(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal,
+                                               b, h, rows, with_scale=True)
+        check_out(to_np(out_c[b, h, rows]), o_ref, "bf16", f"{w.name} b={b} h={h}", scale=sc)
         check_lse(to_np(lse_c[b, h, rows]), l_ref, f"{w.name} b={b} h={h}")
+
+
+# ---------------------------------------------------------------- full size, whole heads
+
+@pytest.mark.parametrize("idx", [1, 3])
+def test_bf16_whole_workload_elementwise(gpu_device, idx):
+    """Every element of the single causal head of 8192 (split over keys: every query
+    tile and every key range of the plan the benchmark times) and of the bias workload
+    (all 32 heads), against the oracle on the whole problem."""
+    w = workloads.workload(idx)
+    print(f"\n[fwd] whole {w.name}", flush=True)
+    inp, gpu = _inputs(w, gpu_device)
+    out, lse = _run(gpu, w, gpu_device)
+    o_ref, l_ref, sc = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal, with_scale=True)
+    check_out(out, o_ref, "bf16", w.name, scale=sc)
+    check_lse(lse, l_ref, w.name)
+
+
+def test_bf16_batched_heads_whole(gpu_device):
+    """Sixteen whole heads of the batched causal workload (B=4, H=32, N=4096, [B,N,H,d]
+    storage), element by element."""
+    w = workloads.workload(2)
+    inp, gpu = _inputs(w, gpu_device)
+    out, lse = _run(gpu, w, gpu_device)
+    out_c, lse_c = out.cpu(), lse.cpu()
+    rng = np.random.default_rng(202)
+    pairs = {(0, 0), (w.B - 1, w.H - 1), (1, 17), (2, 5)}
+    while len(pairs) < 16:
+        pairs.add((int(rng.integers(0, w.B)), int(rng.integers(0, w.H))))
+    for b, h in sorted(pairs):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ref, l_ref, sc = sdpa_reference(inp["q"][sl], inp["k"][sl], inp["v"][sl], None, True, with_scale=True)
+        check_out(out_c[sl], o_ref, "bf16", f"{w.name} b={b} h={h}", scale=sc)
+        check_lse(lse_c[sl], l_ref, f"{w.name} b={b} h={h}")
+
+
+def test_bf16_long_heads_whole_query_tiles(gpu_device):
+    """The long-sequence workload (H=8, N=32768, peaked scores): every row of the first,
+    a middle and the last query tile of three heads."""
+    w = workloads.workload(4)
+    inp, gpu = _inputs(w, gpu_device)
+    out, lse = _run(gpu, w, gpu_device)
+    out_c, lse_c = out.cpu(), lse.cpu()
+    for h in (0, 3, 7):
+        for t in (0, 131, 255):
+            rows = list(range(t * 128, t * 128 + 128))
+            o_ref, l_ref, sc = sdpa_reference_rows(inp["q"], inp["k"], inp["v"], None, True, 0, h, rows,
+                                                   with_scale=True)
+            check_out(to_np(out_c[0, h, rows]), o_ref, "bf16", f"{w.name} h={h} tile {t}", scale=sc)
+            check_lse(to_np(lse_c[0, h, rows]), l_ref, f"{w.name} h={h} tile {t}")
 
 
 # ---------------------------------------------------------------- properties and contract
@@ -195,8 +245,8 @@ def test_split_merge_paths_agree(gpu_device, monkeypatch, idx, over):
     for o, l in runs[1:]:  # same arithmetic in the same order: bitwise equal
         assert torch.equal(o1, o) and torch.equal(l1, l)
     if w.N <= 2048:
-        o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
-        check_out(o1, o_ref, "bf16", w.name + str(over))
+        o_ref, l_ref, sc = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal, with_scale=True)
+        check_out(o1, o_ref, "bf16", w.name + str(over), scale=sc)
         check_lse(l1, l_ref, w.name + str(over))
     else:
         assert bool(o1.float().isfinite().all()) and bool(l1.isfinite().all())
@@ -216,8 +266,8 @@ def test_split_plans_under_other_unit_targets(gpu_device, monkeypatch, units, id
     print(f"\n[fwd] {w.name} {over} units={units}", flush=True)
     inp, gpu = _inputs(w, gpu_device)
     o, l = _run(gpu, w, gpu_device)
-    o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal)
-    check_out(o, o_ref, "bf16", w.name + str(over))
+    o_ref, l_ref, sc = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal, with_scale=True)
+    check_out(o, o_ref, "bf16", w.name + str(over), scale=sc)
     check_lse(l, l_ref, w.name + str(over))
 
 
@@ -275,7 +325,7 @@ def test_owned_workspace_refused_under_capture(gpu_device):
             status = e.status
     assert status == capi.STATUS["FA_ERR_WORKSPACE"]
     # a problem without a split (enough query tiles) needs no workspace: captured as is
-    w2 = workloads.workload(2).resized(B=2, H=8, N=1024)
+    w2 = workloads.workload(2).resized(B=4, H=16, N=1024)  # 512 query tiles: no split
     _, g2 = _inputs(w2, gpu_device)
     assert capi.fa_fwd_workspace_size(w2.B, w2.H, w2.N, w2.d, w2.dv, capi.FA_BF16, True) == 0
     o2 = torch.empty(w2.B, w2.H, w2.N, w2.dv, dtype=torch.bfloat16, device=gpu_device)

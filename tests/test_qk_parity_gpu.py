@@ -54,8 +54,9 @@ def test_rectangular_elementwise(gpu_device, case, dtype):
     lse = torch.full((B, H, nq), float("nan"), dtype=torch.float32, device=gpu_device)
     capi.fa_fwd_qk(gpu["q"], gpu["k"], gpu["v"], bias=gpu["bias"], causal=causal, out=out, lse=lse)
     torch.cuda.synchronize()
-    o_ref, l_ref = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], causal, allow_empty_rows=True)
-    check_out(out, o_ref, dtype, str(case))
+    o_ref, l_ref, sc = sdpa_reference(inp["q"], inp["k"], inp["v"], inp["bias"], causal, allow_empty_rows=True,
+                                      with_scale=True)
+    check_out(out, o_ref, dtype, str(case), scale=sc)
     check_lse(lse, l_ref, str(case))
 
 
@@ -80,8 +81,9 @@ def test_decode_workload_full_size_sampled(gpu_device):
     out, lse = capi.fa_fwd_qk(gpu["q"], gpu["k"], gpu["v"], causal=True)
     torch.cuda.synchronize()
     for b, h in [(0, 0), (3, 17), (7, 31)]:
-        o_ref, l_ref = sdpa_reference_rows(inp["q"], inp["k"], inp["v"], None, True, b, h, [0])
-        check_out(to_np(out[b, h, [0]]), o_ref, "bf16", f"decode b={b} h={h}")
+        o_ref, l_ref, sc = sdpa_reference_rows(inp["q"], inp["k"], inp["v"], None, True, b, h, [0],
+                                               with_scale=True)
+        check_out(to_np(out[b, h, [0]]), o_ref, "bf16", f"decode b={b} h={h}", scale=sc)
         check_lse(to_np(lse[b, h, [0]]), l_ref, f"decode b={b} h={h}")
 
 
