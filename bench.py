@@ -6,10 +6,14 @@ d = dv = 128, causal (the single-head L = 8192 example of the page
 "AI Infra 第5章图解: 算子与运行时", section "FlashAttention: Softmax 也能逐块算").
 Inputs are drawn once and resident in HBM before timing starts.
 
-Printed: one JSON line with the throughput in algorithmic TFLOP/s
-(2*(d+dv) per allowed query/key pair, softmax not counted), the roofline of the
-dominant kernel (its average launch duration measured with HIP events on the stream
-it is launched on), and the CPU oracle timed on this host as a reported baseline.
+Printed: one JSON line with the throughput in algorithmic TFLOP/s over the timed steps
+(2*(d+dv) per allowed query/key pair, softmax not counted); the roofline of the
+dominant kernel: the median (with p10, p90) of at least 50 launches, each timed by its own
+HIP events on the stream it is launched on, warm (back to back) and cold (a 1 GiB cache
+flush, untimed, before each launch), against the published peak and against the
+ceilings the library's probes measure on this device (streaming copy for B_max, bf16
+MFMA chains for P_max); and the CPU oracle timed on this host as a reported baseline
+(all threads, and one thread for a per-core figure).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
   python bench.py --pass bwd [...]  # the gradients (fa_bwd) of the same workload instead
@@ -60,6 +64,90 @@ def read_traffic(workload: str, kind: str = "fwd_mfma", src: str = KERNEL_SRC):
         return float(kv["hbm_bytes_per_dispatch"])
     except (KeyError, ValueError):
         return None
+
+
+def launch_stats(launch, stream, reps, flush=None):
+    """Device time of `reps` launches, each bracketed by its own pair of HIP events on
+    `stream` (the stream the library launches on). With `flush`, that untimed work runs
+    on the stream before every launch (a cold-cache run). Returns the sorted times (s)."""
+    import numpy as np
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return np.sort(np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e-3)
+
+
+def summary_us(t):
+    """Median, p10, p90 and mean of launch times t (s), in microseconds."""
+    import numpy as np
+
+    return {"median": float(np.median(t)) * 1e6, "p10": float(np.percentile(t, 10)) * 1e6,
+            "p90": float(np.percentile(t, 90)) * 1e6, "mean": float(np.mean(t)) * 1e6, "n": int(len(t))}
+
+
+def make_flush(dev, stream, nbytes=1 << 30):
+    """Untimed cache flush for cold runs: read and write a 1 GiB buffer (four times the
+    256 MB last-level cache, so neither the L2s nor the Infinity Cache keep the inputs)."""
+    import torch
+
+    buf = torch.zeros(nbytes // 4, dtype=torch.float32, device=dev)
+
+    def flush():
+        with torch.cuda.stream(stream):
+            buf.add_(1.0)
+    return flush
+
+
+def measured_ceilings(dev, stream):
+    """B_max from the library's streaming copy probe (2 GiB each way, far beyond the last-level
+    cache) and the bf16 matrix-core ceiling from its MFMA probe (two workgroups of four waves
+    per compute unit, as the attention kernel runs), each the median over 20 launches."""
+    import torch
+
+    from exact_attention_35_amd import capi
+
+    n = 2 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        capi.fa_probe_copy(src, dst, stream)
+    t = launch_stats(lambda: capi.fa_probe_copy(src, dst, stream), stream, 20)
+    bw = 2.0 * n / float(t[len(t) // 2])
+    del src, dst
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks, iters = 2 * cus, 4000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    flops = capi.fa_probe_mfma(out, blocks, iters, stream)
+    t = launch_stats(lambda: capi.fa_probe_mfma(out, blocks, iters, stream), stream, 20)
+    return {"hbm_GBps": bw / 1e9, "mfma_bf16_TFLOPs": flops / float(t[len(t) // 2]) / 1e12,
+            "copy_probe_bytes": 2 * n, "mfma_probe": f"{blocks} workgroups x 4 waves x {iters} x 4 MFMA 32x32x16"}
+
+
+def cpu_host_info():
+    """The host's CPU model, the cores this process may use and the BLAS threads."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": threads}
 
 
 def copy_probe(steps: int) -> None:
@@ -123,8 +211,37 @@ def cpu_baseline(w, inp, budget_s=10.0):
             flops += int(2 * (w.d + w.dv) * keys.sum())
             rows_done += len(rows)
         sample = f"{rows_done} whole query rows of head (0, 0) of {w.name}, fp64 numpy, {total:.1f} s"
-    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": sample, "seconds": total}
+    res = {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": sample, "seconds": total, **cpu_host_info()}
+    res["one_thread"] = cpu_baseline_one_thread(w, inp)
+    return res
+
+
+def cpu_baseline_one_thread(w, inp, budget_s=4.0):
+    """The same oracle with BLAS held to one thread, on whole query rows of head (0, 0)
+    (64 rows a call, spread over the sequence), for a per-core figure."""
+    import numpy as np
+
+    from oracle import sdpa_reference_rows
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return None
+    rng = np.random.default_rng(1)
+    flops, total, done = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        while total < budget_s and done < w.n_q:
+            rows = np.sort(rng.choice(w.n_q, size=min(64, w.n_q), replace=False))
+            t0 = time.perf_counter()
+            sdpa_reference_rows(inp["q"], inp["k"], inp["v"], inp["bias"], w.causal, 0, 0, rows)
+            total += time.perf_counter() - t0
+            off = w.N - w.n_q
+            keys = np.minimum(rows + 1 + off, w.N) if w.causal else np.full(len(rows), w.N)
+            flops += int(2 * (w.d + w.dv) * keys.sum())
+            done += len(rows)
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": 1,
+            "sample": f"{done} whole query rows of head (0, 0), BLAS limited to one thread, {total:.1f} s"}
 
 
 def main() -> int:
@@ -154,6 +271,8 @@ def main() -> int:
         return 0
     if args.tile_sweep:
         return tile_sweep(args)
+
+    import numpy as np
 
     from exact_attention_35_amd import capi, roofline as rf, workloads
 
@@ -205,30 +324,31 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # the timed steps (wall clock, synchronised on both sides): `value`
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
     for _ in range(args.steps):
         step()
-    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # Launches are back to back on one stream, so the event interval over the region
-    # divided by the launch count is the average launch duration (plus launch gaps).
-    avg_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    # the dominant kernel's launch time: each launch bracketed by its own events on the
+    # library's stream, warm (back to back) and cold (a 1 GiB flush before each)
+    reps = max(50, args.steps)
+    warm = launch_stats(step, stream, reps)
+    cold = launch_stats(step, stream, reps, flush=make_flush(dev, stream))
+    ceil = measured_ceilings(dev, stream)
 
     flops = rf.alg_flops(w.B, w.H, w.N, w.d, w.dv, w.causal, Nq=w.n_q)
-    elem = 2 if w.dtype == "bf16" else 4
+    elem = 2 if w.dtype in ("bf16", "f16") else 4
     bias_bytes = (w.H * w.n_q * w.N * 4) if w.bias else 0
     min_b = rf.min_bytes(w.B, w.H, w.N, w.d, w.dv, elem, bias_bytes=bias_bytes, Nq=w.n_q)
     value = flops * args.steps / wall / 1e12
-    achieved = flops / avg_launch_s / 1e12
-    if w.dtype == "bf16":
-        peak, bound = rf.MI355X_PEAK_BF16_FLOPS / 1e12, "mfma"
-    else:
-        peak, bound = rf.MI355X_PEAK_F32_FLOPS / 1e12, "mfma"
+    med_w, med_c = float(np.median(warm)), float(np.median(cold))
+    # the ceiling of the kernel that runs: bf16 on the matrix cores; fp32 on the general
+    # kernel's vector ALUs
+    mfma = w.dtype in ("bf16", "f16")
+    peak = (rf.MI355X_PEAK_BF16_FLOPS if mfma else rf.MI355X_PEAK_F32_FLOPS) / 1e12
+    bound = "mfma" if mfma else "alu"
     # which ceiling binds at I = F/Q: the bias stream (and a decoding step, which reads
     # every key and value for one row) make a workload memory-bound
     _, _, which = rf.roofline_bound(flops, min_b, peak * 1e12, rf.MI355X_HBM_BYTES_PER_S)
@@ -236,15 +356,25 @@ def main() -> int:
         bound = "hbm"
     traffic = read_traffic(w.name)
     if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": min_b / avg_launch_s / 1e9, "peak": 8000.0,
-                "unit": "GB/s", "frac": min_b / avg_launch_s / 8e12, "traffic": traffic}
+        meas = ceil["hbm_GBps"]
+        roof = {"bound": "hbm", "achieved": min_b / med_w / 1e9, "peak": 8000.0, "unit": "GB/s",
+                "frac": min_b / med_w / 8e12, "traffic": traffic,
+                "measured_peak": meas, "frac_of_measured": min_b / med_w / 1e9 / meas,
+                "cold_achieved": min_b / med_c / 1e9, "cold_frac": min_b / med_c / 8e12}
     else:
-        roof = {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": traffic}
-    roof.update({"kernel": "fwd_mfma" if w.dtype == "bf16" else "fwd_generic",
-                 "avg_launch_us": avg_launch_s * 1e6,
+        meas = ceil["mfma_bf16_TFLOPs"] if mfma else None
+        roof = {"bound": bound, "achieved": flops / med_w / 1e12, "peak": peak, "unit": "TFLOP/s",
+                "frac": flops / med_w / 1e12 / peak, "traffic": traffic,
+                "measured_peak": meas, "frac_of_measured": (flops / med_w / 1e12 / meas) if meas else None,
+                "cold_achieved": flops / med_c / 1e12, "cold_frac": flops / med_c / 1e12 / peak}
+    roof.update({"kernel": "fwd_mfma" if mfma else "fwd_generic",
+                 "avg_launch_us": med_w * 1e6,
+                 "launch_us_warm": summary_us(warm), "launch_us_cold": summary_us(cold),
                  "alg_flops_per_launch": flops, "min_bytes_per_launch": min_b,
+                 "measured_ceilings": ceil,
                  "kernel_source_sha256_16": kernel_sha()})
+    ws_bytes = capi.fa_fwd_qk_workspace_size(w.B, w.H, w.n_q, w.N, w.d, w.dv,
+                                             capi.FA_BF16 if w.dtype == "bf16" else capi.FA_F32, w.causal)
 
     res = {
         "metric": METRIC if args.workload == DEFAULT_WORKLOAD else OTHER_METRIC,
@@ -261,8 +391,9 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv,
                    "causal": w.causal, "bias": w.bias, "layout": w.layout,
-                   "parallelism": "single GPU", **({"N_q": w.n_q} if rect else {})},
-        "pct_of_peak": 100.0 * value / (rf.MI355X_PEAK_BF16_FLOPS / 1e12),
+                   "parallelism": "single GPU", "workspace_bytes": int(ws_bytes),
+                   **({"N_q": w.n_q} if rect else {})},
+        "pct_of_peak": 100.0 * value / peak,
         "roofline": roof,
     }
     if not args.no_cpu:
@@ -352,6 +483,8 @@ def bench_bwd(args, w, inp, gpu, out, lse) -> int:
     with O and lse from one fa_fwd call and a seeded dO, all resident in HBM."""
     import torch
 
+    import numpy as np
+
     from exact_attention_35_amd import capi, roofline as rf, workloads
 
     if w.dtype != "bf16":
@@ -377,16 +510,16 @@ def bench_bwd(args, w, inp, gpu, out, lse) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev0.record(stream)
     for _ in range(args.steps):
         step()
-    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    avg_call_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    # one fa_bwd call (all its kernels) bracketed by its own events, warm and cold
+    reps = max(50, args.steps)
+    warm = launch_stats(step, stream, reps)
+    cold = launch_stats(step, stream, reps, flush=make_flush(dev, stream))
+    avg_call_s = float(np.median(warm))
 
     flops = rf.alg_flops_bwd(w.B, w.H, w.N, w.d, w.dv, w.causal)
     peak = rf.MI355X_PEAK_BF16_FLOPS / 1e12
@@ -409,8 +542,11 @@ def bench_bwd(args, w, inp, gpu, out, lse) -> int:
                    "causal": w.causal, "bias": w.bias, "layout": w.layout, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": read_traffic(w.name, "bwd", BWD_SRC),
+                     "cold_achieved": flops / float(np.median(cold)) / 1e12,
+                     "cold_frac": flops / float(np.median(cold)) / 1e12 / peak,
                      "kernel": "bwd_rowstat + bwd_mfma [+ bwd_reduce] (one fa_bwd call)",
-                     "avg_launch_us": avg_call_s * 1e6, "alg_flops_per_launch": flops,
+                     "avg_launch_us": avg_call_s * 1e6, "launch_us_warm": summary_us(warm),
+                     "launch_us_cold": summary_us(cold), "alg_flops_per_launch": flops,
                      "min_bytes_per_launch": rf.min_bytes_bwd(w.B, w.H, w.N, w.d, w.dv, 2, bias_bytes),
                      "kernel_source_sha256_16": hashlib.sha256(open(BWD_SRC, "rb").read()).hexdigest()[:16]},
     }

@@ -18,6 +18,7 @@ __all__ = [
     "fa_status_string", "fa_version", "fa_shutdown", "fa_plan_describe", "make_strides", "FaStrides",
     "FaPlanInfo", "EXPORTED", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "FaBwdStrides",
     "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size", "fa_plan_describe_qk",
+    "fa_probe_copy", "fa_probe_mfma", "fa_probe_mfma_flops",
 ]
 
 FA_OK = 0
@@ -36,7 +37,8 @@ STATUS = {
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
             "fa_version", "fa_shutdown", "fa_plan_describe", "fa_bwd", "fa_bwd_ex",
             "fa_bwd_workspace_size", "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size",
-            "fa_plan_describe_qk")
+            "fa_plan_describe_qk", "fa_probe_copy", "fa_probe_mfma",
+            "fa_probe_mfma_flops")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -119,6 +121,12 @@ def lib():
     L.fa_bwd_ex.restype = ctypes.c_int
     L.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     L.fa_bwd_workspace_size.restype = sz
+    L.fa_probe_copy.argtypes = [vp, vp, i64, vp]
+    L.fa_probe_copy.restype = ctypes.c_int
+    L.fa_probe_mfma.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+    L.fa_probe_mfma.restype = ctypes.c_int
+    L.fa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.fa_probe_mfma_flops.restype = ctypes.c_double
     _lib = L
     return L
 
@@ -402,3 +410,24 @@ def fa_bwd_ex(q, k, v, out, lse, grad_out, workspace, bias=None, causal=False, g
                          dt, _stream_handle(stream, q.device), _ptr(workspace), nbytes)
     _check(st)
     return grad_q, grad_k, grad_v
+
+
+def fa_probe_copy(src, dst, stream=None):
+    """The streaming copy probe: dst <- src (device tensors of equal byte size)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise FaError(STATUS["FA_ERR_SHAPE"], "src and dst sizes differ")
+    _same_device((("src", src), ("dst", dst)))
+    _check(lib().fa_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream_handle(stream, src.device)))
+
+
+def fa_probe_mfma(out, blocks, iters, stream=None):
+    """The bf16 matrix-core probe; out: float32 device tensor of blocks * 256 elements.
+    Returns the FLOPs the launch performs."""
+    import torch
+
+    if out.dtype != torch.float32 or out.numel() < blocks * 256:
+        raise FaError(STATUS["FA_ERR_SHAPE"], "out must hold blocks * 256 float32 values")
+    _same_device((("out", out),))
+    _check(lib().fa_probe_mfma(_ptr(out), int(blocks), int(iters), _stream_handle(stream, out.device)))
+    return float(lib().fa_probe_mfma_flops(int(blocks), int(iters)))

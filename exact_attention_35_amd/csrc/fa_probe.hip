@@ -1,0 +1,85 @@
+// Measurement probes for the roofline of the attention kernels (include/fa_probe.h).
+//
+// The page "编译器与内核" (Compilers and kernels), section "屋顶线是上界，不是秒表", bounds a
+// kernel by min(P_max, B_max * I) and asks for P_max on the same dtype and instruction
+// path as the kernel's FLOP count, and for B_max as the bandwidth the access pattern
+// actually reaches, measured rather than copied from a specification sheet. These two
+// kernels measure both ceilings on the device at hand:
+//  * copy: a streaming copy with 16-byte loads and stores (the widest per-lane global
+//    access of gfx950), grid-stride, over buffers much larger than the 256 MB
+//    last-level cache, so every byte crosses the HBM boundary once each way;
+//  * mfma: back-to-back v_mfma_f32_32x32x16_bf16 (the instruction the attention kernel
+//    spends its FLOPs on), four independent accumulator chains per wave and two waves
+//    per SIMD, as the attention kernel runs, with no memory traffic in the loop.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "fa_mfma_common.h"
+#include "fa_probe.h"
+
+namespace {
+
+__global__ __launch_bounds__(256) void copy_probe(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                  int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// Each wave runs `iters` rounds of four independent 32x32x16 bf16 MFMA chains on
+// register operands and stores its accumulators once (so the chains are not removed).
+__global__ __launch_bounds__(256, 2) void mfma_probe(float* __restrict__ out, int iters) {
+  using fa::bf16x8;
+  using fa::floatx16;
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(0.001f * (float)(lane + e));
+    b[e] = (__bf16)(0.002f * (float)(lane - e));
+  }
+  floatx16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+    c0 = fa::mfma32(a, b, c0);
+    c1 = fa::mfma32(b, a, c1);
+    c2 = fa::mfma32(a, a, c2);
+    c3 = fa::mfma32(b, b, c3);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst || bytes <= 0 || bytes % 16 != 0 || ((uintptr_t)src | (uintptr_t)dst) % 16 != 0)
+    return FA_ERR_NULL;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return FA_ERR_DEVICE;
+  const int64_t n16 = bytes / 16;
+  const int64_t want = (n16 + 255) / 256;
+  const int grid = (int)(want < (int64_t)cus * 16 ? want : (int64_t)cus * 16);
+  hipLaunchKernelGGL(copy_probe, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_probe_mfma(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks <= 0 || iters <= 0) return FA_ERR_NULL;
+  hipLaunchKernelGGL(mfma_probe, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), out, iters);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+double fa_probe_mfma_flops(int blocks, int iters) {
+  // four waves per block, four MFMAs per round, 2 * 32 * 32 * 16 FLOP each
+  return (double)blocks * 4.0 * (double)iters * 4.0 * 32768.0;
+}
+
+}  // extern "C"
