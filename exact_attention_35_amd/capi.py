@@ -17,7 +17,7 @@ __all__ = [
     "STATUS", "lib", "library_path", "fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size",
     "fa_status_string", "fa_version", "fa_shutdown", "fa_plan_describe", "make_strides", "FaStrides",
     "FaPlanInfo", "EXPORTED", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "FaBwdStrides",
-    "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size", "fa_plan_describe_qk",
+    "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size", "fa_plan_describe_qk", "fa_fwd_qk_noalloc",
     "fa_probe_copy", "fa_probe_mfma", "fa_probe_mfma_flops",
 ]
 
@@ -37,7 +37,7 @@ STATUS = {
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
             "fa_version", "fa_shutdown", "fa_plan_describe", "fa_bwd", "fa_bwd_ex",
             "fa_bwd_workspace_size", "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size",
-            "fa_plan_describe_qk", "fa_probe_copy", "fa_probe_mfma",
+            "fa_plan_describe_qk", "fa_fwd_qk_noalloc", "fa_probe_copy", "fa_probe_mfma",
             "fa_probe_mfma_flops")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -99,6 +99,8 @@ def lib():
     L.fa_fwd_qk.restype = ctypes.c_int
     L.fa_fwd_qk_ex.argtypes = qk_args + [vp, sz]
     L.fa_fwd_qk_ex.restype = ctypes.c_int
+    L.fa_fwd_qk_noalloc.argtypes = qk_args
+    L.fa_fwd_qk_noalloc.restype = ctypes.c_int
     L.fa_fwd_qk_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     L.fa_fwd_qk_workspace_size.restype = sz
     L.fa_status_string.argtypes = [ctypes.c_int]
@@ -309,6 +311,20 @@ def fa_fwd_qk(q, k, v, bias=None, causal=False, out=None, lse=None, stream=None)
     B, H, Nq, Nk, d, dv, dt, mask, bias, out, lse, strides = _prepare(q, k, v, bias, causal, out, lse, rect=True)
     st = lib().fa_fwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), mask, _ptr(out), _ptr(lse),
                          B, H, Nq, Nk, d, dv, ctypes.byref(strides), dt, _stream_handle(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def fa_fwd_qk_noalloc(q, k, v, out, lse, bias=None, causal=False, stream=None):
+    """fa_fwd_qk through fa_fwd_qk_noalloc, which allocates no device memory: out and lse
+    must be given (the binding allocates nothing either). Split problems use the
+    library's fixed per-GPU scratch array, so overlapping calls on one GPU race.
+    Returns (out, lse)."""
+    if out is None or lse is None:
+        raise FaError(STATUS["FA_ERR_NULL"], "fa_fwd_qk_noalloc needs out and lse")
+    B, H, Nq, Nk, d, dv, dt, mask, bias, out, lse, strides = _prepare(q, k, v, bias, causal, out, lse, rect=True)
+    st = lib().fa_fwd_qk_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), mask, _ptr(out), _ptr(lse),
+                                 B, H, Nq, Nk, d, dv, ctypes.byref(strides), dt, _stream_handle(stream, q.device))
     _check(st)
     return out, lse
 

@@ -528,6 +528,38 @@ int owned_workspace(int dev, hipStream_t stream, size_t need, void** out) {
   return FA_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+// Scratch memory of fa_fwd_qk_noalloc: a fixed device array per GPU (each device that
+// loads this library holds its own copy until the process ends). The largest forward
+// plan needs kMaxSplitUnits units of dv = 128: 8-byte flags, 2 * 128 fp32 row
+// statistics and 128 * 128 16-bit partial outputs per unit, each part 256-byte aligned.
+constexpr size_t kStaticScratchBytes =
+    ((size_t)fa::kMaxSplitUnits * 8 + 255) / 256 * 256 + (size_t)fa::kMaxSplitUnits * 2 * fa::kMfmaBM * 4 +
+    (size_t)fa::kMaxSplitUnits * fa::kMfmaBM * 128 * 2;
+static_assert(kStaticScratchBytes % 256 == 0, "scratch parts are 256-byte aligned");
+static_assert(kStaticScratchBytes == FA_NOALLOC_SCRATCH_BYTES, "fa.h states the scratch size");
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};  // device address of `scratch` per device (host-side name is not it)
+
+// The device address of this device's `scratch`, looked up once per device with the
+// device current (the caller's current device is the one fa_fwd_qk_noalloc runs on).
+int static_scratch(int dev, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return FA_ERR_DEVICE;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 // ---------------------------------------------------------------- gradients
 struct BwdProblem {
   const void *q, *k, *v, *out, *dout;
@@ -794,6 +826,26 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, const float* bias, in
   if (pl.ws_bytes > 0) {
     st = owned_workspace(dev, static_cast<hipStream_t>(stream), pl.ws_bytes, &ws);
     if (st != FA_OK) return st;
+  }
+  return run(P, pl, ws, static_cast<hipStream_t>(stream));
+}
+
+int fa_fwd_qk_noalloc(const void* q, const void* k, const void* v, const float* bias, int mask_mode, void* out,
+                      float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv,
+                      const fa_strides* strides, int dtype, void* stream) {
+  const Problem P = make_problem(q, k, v, bias, mask_mode, out, lse, B, H, Nq, Nk, d, dv, strides, dtype);
+  int st = validate(P);
+  if (st != FA_OK) return st;
+  if (B * H * Nq == 0) return FA_OK;
+  int dev = 0;
+  DevInfo di;
+  if ((st = device_info(&dev, &di)) != FA_OK) return st;
+  const std::shared_ptr<const Plan> plan = cached_plan(B, H, Nq, Nk, d, dv, dtype, mask_mode, di.cus);
+  const Plan& pl = *plan;
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    if (pl.ws_bytes > kStaticScratchBytes) return FA_ERR_WORKSPACE;
+    if ((st = static_scratch(dev, &ws)) != FA_OK) return st;
   }
   return run(P, pl, ws, static_cast<hipStream_t>(stream));
 }

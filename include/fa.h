@@ -186,6 +186,23 @@ int fa_fwd_qk_ex(const void* q, const void* k, const void* v, const float* bias,
                  int64_t dv, const fa_strides* strides, int dtype, void* stream, void* workspace,
                  size_t workspace_bytes);
 
+/*
+ * fa_fwd_qk_noalloc — fa_fwd_qk for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc): it calls
+ * no allocating routine. Split problems take their scratch memory from a fixed device
+ * array of FA_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it runs on
+ * until the process ends (every forward plan fits: at most 512 key-range units of
+ * dv <= 128); a problem whose plan needed more would return FA_ERR_WORKSPACE. All calls
+ * on one GPU share that array and leave their partial states in it, so calls that may
+ * overlap on one GPU (other streams, other host threads) race: serialise them, or use
+ * fa_fwd_qk_ex with separate workspaces. The array needs no clearing between calls.
+ * Arguments, results and other errors as fa_fwd_qk (with N_q = N_k = N it is fa_fwd).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES 17305600
+int fa_fwd_qk_noalloc(const void* q, const void* k, const void* v, const float* bias, int mask_mode,
+                      void* out, float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                      int64_t dv, const fa_strides* strides, int dtype, void* stream);
+
 /* Static description of a status code (never NULL). Errors are part of the contract
  * surface (the page "编译器与内核", section "生成内核需要一名挑剔的评估者", item
  * 契约表面); this library reports them as status codes only. */
