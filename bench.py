@@ -251,6 +251,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--reps", type=int, default=50,
+                    help="individually timed launches, warm and cold each (at least --steps)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the copy and MFMA probes (e.g. under a counter profiler)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the gradients of the workload")
@@ -333,10 +337,10 @@ def main() -> int:
     wall = time.perf_counter() - t0
     # the dominant kernel's launch time: each launch bracketed by its own events on the
     # library's stream, warm (back to back) and cold (a 1 GiB flush before each)
-    reps = max(50, args.steps)
+    reps = max(args.reps, args.steps)
     warm = launch_stats(step, stream, reps)
     cold = launch_stats(step, stream, reps, flush=make_flush(dev, stream))
-    ceil = measured_ceilings(dev, stream)
+    ceil = {"hbm_GBps": None, "mfma_bf16_TFLOPs": None} if args.no_ceilings else measured_ceilings(dev, stream)
 
     flops = rf.alg_flops(w.B, w.H, w.N, w.d, w.dv, w.causal, Nq=w.n_q)
     elem = 2 if w.dtype in ("bf16", "f16") else 4
@@ -359,7 +363,7 @@ def main() -> int:
         meas = ceil["hbm_GBps"]
         roof = {"bound": "hbm", "achieved": min_b / med_w / 1e9, "peak": 8000.0, "unit": "GB/s",
                 "frac": min_b / med_w / 8e12, "traffic": traffic,
-                "measured_peak": meas, "frac_of_measured": min_b / med_w / 1e9 / meas,
+                "measured_peak": meas, "frac_of_measured": (min_b / med_w / 1e9 / meas) if meas else None,
                 "cold_achieved": min_b / med_c / 1e9, "cold_frac": min_b / med_c / 8e12}
     else:
         meas = ceil["mfma_bf16_TFLOPs"] if mfma else None
@@ -516,7 +520,7 @@ def bench_bwd(args, w, inp, gpu, out, lse) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # one fa_bwd call (all its kernels) bracketed by its own events, warm and cold
-    reps = max(50, args.steps)
+    reps = max(args.reps, args.steps)
     warm = launch_stats(step, stream, reps)
     cold = launch_stats(step, stream, reps, flush=make_flush(dev, stream))
     avg_call_s = float(np.median(warm))

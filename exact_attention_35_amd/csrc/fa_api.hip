@@ -348,7 +348,7 @@ Plan make_plan(int64_t B, int64_t H, int64_t Nq, int64_t N, int64_t d, int64_t d
   if (n_split == 0) return pl;
   pl.split = true;
   pl.grid = (int)units;
-  pl.merge_grid = (int)(tiles * fa::merge_groups((int)dv, 1));
+  pl.merge_grid = (int)(n_split * BH * fa::merge_groups((int)dv, 1));
   pl.merge_blocks = (int)(n_split * BH * merge_groups_used(Nq, pl.n_qt, dv));
   pl.off_flag = 0;
   pl.off_ml = round_up(units * sizeof(uint64_t), 256);
@@ -447,13 +447,13 @@ int run(const Problem& P, const Plan& pl_in, void* ws, hipStream_t stream) {
     int n_split = 0;
     for (int qt = pl.n_qt - 1; qt >= 0; --qt) {
       const Plan::Ranges& r = pl.ranges[qt];
-      p.qtile_info[qt] = (uint32_t)acc | (uint32_t)r.nch << 24;
-      if (r.nch > 1) p.split_qt[n_split++] = (uint8_t)qt;
+      if (r.nch > 1) p.split_info[n_split++] = fa::split_word(acc, r.nch, qt);
       for (int64_t bh = 0; bh < P.B * P.H; ++bh)
         for (int c = 0; c < r.nch; ++c)
           p.unit_info[acc + bh * r.nch + c] = pack_unit(qt, r.begin[c], r.len[c], bh, pl.n_qt == 1, pl.shift);
       acc += (int32_t)(P.B * P.H * r.nch);
     }
+    p.n_split = n_split;
   }
   // Split query tiles are merged by blocks appended to the forward grid, except under
   // graph capture (a replay would reuse this call's number, so the flags of the previous

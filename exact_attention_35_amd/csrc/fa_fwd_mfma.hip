@@ -70,6 +70,10 @@ constexpr int kStoreWriteThrough = 1 | 16;
 
 constexpr float kTau = 8.0f;  // lazy-reference slack, log2 units
 
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations
+// are outstanding and leaves the export and LDS/scalar counters unconstrained.
+constexpr int vmcnt_wait(int n) { return (n & 0xf) | ((n >> 4) & 0x3) << 14 | 0x7 << 4 | 0xf << 8; }
+
 template <int D, int DV>
 struct Cfg {
   static constexpr int NT = 256;
@@ -259,9 +263,9 @@ struct MergeItems {
   u32x2 raw[IT][kMaxRanges];   // o_p / l_p, 4 bf16 values per item
   float mp[kMaxRanges], lp[kMaxRanges];
 
-  __device__ __forceinline__ void init(const Params& p, int qt, int bh, int rg_, int nch) {
+  __device__ __forceinline__ void init(const Params& p, int ubase, int bh, int rg_, int nch) {
     rg = rg_;
-    const int slot0 = (int)(p.qtile_info[qt] & 0xffffffu) + bh * nch;
+    const int slot0 = ubase + bh * nch;
     // slot j holds [BM/32][dv/4][32][4] bf16: row r, chunk c4 at ((r/32)*NC4 + c4)*32 + r%32
     ro = __builtin_amdgcn_make_buffer_rsrc(static_cast<E*>(p.part_o) + (int64_t)slot0 * (BM * DV), 0, nch * BM * DV * 2, kBufferWord3);
     rml = __builtin_amdgcn_make_buffer_rsrc(p.part_ml + (int64_t)slot0 * (2 * BM), 0, nch * 2 * BM * 4, kBufferWord3);
@@ -339,7 +343,7 @@ struct MergeItems {
 };
 
 // Merge blocks of the forward kernel itself (blocks n_units on): the split query tiles
-// (p.split_qt, from the last one), then b*h, then groups of rows. The units of the tile
+// (p.split_info, from the last one), then b*h, then groups of rows. The units of the tile
 // publish their partial states by storing this call's number into their flags once the states are
 // written through to memory; wave 0 polls the flags (one lane per range) with
 // agent-scope loads until all of them hold it. The merge blocks come after every unit
@@ -355,13 +359,12 @@ __device__ void merge_block(const Params& p, int m, float* w_s) {
   const int rg = m % groups;
   const int t = m / groups;
   const int bh = t % BH;
-  const int qt = kernarg_byte(p.split_qt, (t / BH) % kMaxSplitQTiles);
-  const uint32_t qinfo = p.qtile_info[qt];
-  const int nch = (int)(qinfo >> 24);
-  const uint64_t* flag = p.part_flag + (qinfo & 0xffffffu) + bh * nch;
+  const uint32_t info = p.split_info[(t / BH) % kMaxSplitQTiles];
+  const int qt = split_qtile(info), nch = split_nch(info), ubase = split_ubase(info);
+  const uint64_t* flag = p.part_flag + ubase + bh * nch;
   int* ready_s = reinterpret_cast<int*>(w_s + kMaxRanges * MI::RG);
   MI items;
-  items.init(p, qt, bh, rg, nch);
+  items.init(p, ubase, bh, rg, nch);
   // Each range's loads are issued as soon as its flag holds this call's number, so a
   // block that waits for the last ranges already holds the others.
   const unsigned all = (1u << nch) - 1u;
@@ -386,18 +389,17 @@ __device__ void merge_block(const Params& p, int m, float* w_s) {
 }
 
 // Separate merge kernel (used where the forward kernel runs without merge blocks):
-// block = (group of rows, b*h, query tile) = (blockIdx.x, .y, .z).
+// block = (group of rows, b*h, split query tile) = (blockIdx.x, .y, .z).
 template <typename E, int DV>
 __global__ __launch_bounds__(256) void merge_split(Params p) {
   using MI = MergeItems<E, DV, 1>;
   __shared__ float w_s[kMaxRanges * MI::RG];
-  const int qt = blockIdx.z;
-  // the argument cache lines used below and the tile's table entries in one round trip
-  asm volatile("" ::"s"(p.out), "s"(p.o_sn), "s"(p.Nq), "s"(p.part_ml), "s"(p.qtile_info[qt]));
-  const int nch = (int)(p.qtile_info[qt] >> 24);
-  if (nch == 1) return;  // written directly by the forward kernel
+  const uint32_t info = p.split_info[blockIdx.z];
+  // the argument cache lines used below and the tile's table entry in one round trip
+  asm volatile("" ::"s"(p.out), "s"(p.o_sn), "s"(p.Nq), "s"(p.part_ml), "s"(info));
+  const int qt = split_qtile(info), nch = split_nch(info);
   MI items;
-  items.init(p, qt, blockIdx.y, blockIdx.x, nch);
+  items.init(p, split_ubase(info), blockIdx.y, blockIdx.x, nch);
   static_for<0, kMaxRanges>([&](auto J) {
     if (decltype(J)::value < nch) items.template load<decltype(J)::value, 0>();
   });
@@ -414,6 +416,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[C::KTILE], k_lds1[C::KTILE];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[C::VTILE], v_lds1[C::VTILE];
 
+  // One word of each cache line of the kernel arguments that the prologue reads, and the
+  // unit's table entry, are read before anything depends on them (before the branch to
+  // the merge blocks too): these scalar loads share one memory round trip, and later
+  // argument reads hit the scalar cache (a dependent chain of argument reads costs a
+  // round trip per cache line).
+  asm volatile("" ::"s"(p.q), "s"(p.k_sn), "s"(p.b_si), "s"(p.split), "s"(p.n_units),
+               "s"(p.unit_info[blockIdx.x & (kMaxSplitUnits - 1)]));
   if ((int)blockIdx.x >= p.n_units) {  // merge block (the LDS stages are free for it)
     merge_block<E, DV>(p, blockIdx.x - p.n_units, reinterpret_cast<float*>(k_lds0));
     return;
@@ -424,12 +433,6 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   const int g = lane >> 5;    // half-wave
   const int l32 = lane & 31;  // query within the wave's 32-row block
 
-  // One word of each cache line of the kernel arguments that the prologue reads, and the
-  // unit's table entry, are read before anything depends on them: these scalar loads
-  // share one memory round trip, and later argument reads hit the scalar cache (a
-  // dependent chain of argument reads costs a round trip per cache line).
-  asm volatile("" ::"s"(p.q), "s"(p.k_sn), "s"(p.b_si), "s"(p.split),
-               "s"(p.unit_info[blockIdx.x & (kMaxSplitUnits - 1)]));
   const Unit U = decode_unit(p, blockIdx.x, C::BM, C::BN);
   const int b = U.bh / p.H;
   const int h = U.bh % p.H;
@@ -700,9 +703,16 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
   auto copy_v = [&](unsigned char* st, int t) { vcp.copy(st, tile_rsrc(vp, p.v_sn, t * C::BN, N), wave); };
 
   // ---- prologue: K(t_begin), K(t_begin+1) into LDS; scores of t_begin ----
+  // Vector-memory loads complete in issue order, so waiting until only the last KLD
+  // loads (K(t_begin+1)) are outstanding means Q and K(t_begin) have landed; K(t_begin+1)
+  // keeps arriving while the first scores are formed (the first loop step waits for it).
   copy_k(k_lds0, t_begin);
-  if (t_begin + 1 < t_end) copy_k(k_lds1, t_begin + 1);
-  __builtin_amdgcn_s_waitcnt(0);
+  if (t_begin + 1 < t_end) {
+    copy_k(k_lds1, t_begin + 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(C::KLD));
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   __syncthreads();
 
   // Iteration t (stage parity PAR = (t - t_begin) mod 2): the matrix cores add
@@ -845,7 +855,7 @@ hipError_t launch_dd(const Params& p, int grid, bool merge, hipStream_t stream) 
     hipLaunchKernelGGL((fwd_mfma<E, D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !merge) return e;
-  hipLaunchKernelGGL((merge_split<E, DV>), dim3(merge_groups(DV, 1), p.B * p.H, p.n_qt), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((merge_split<E, DV>), dim3(merge_groups(DV, 1), p.B * p.H, p.n_split), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -49,14 +49,14 @@ struct Params {
   int n_units;        // forward units (blocks 0 .. n_units-1)
   int unit_shift;     // split plans: the unit table counts key tiles in granules of 2^unit_shift
   int merge_groups;   // merge blocks per split tile and b*h (row groups that hold query rows)
-  // Split plans: units enumerate query tiles from the last one; query tile qt owns
-  // units ubase .. ubase + B*H*nch - 1, nch ranges for each (b, h), where
-  // qtile_info[qt] = ubase | nch << 24 (one 32-bit word, see kernarg_byte).
-  uint32_t qtile_info[kMaxSplitQTiles];
   // Split plans: the query tiles cut into more than one range, from the last one (the
-  // merge blocks of the forward kernel take them in this order; which tiles are cut
-  // depends on the cost model, so they need not be the last ones).
-  uint8_t split_qt[kMaxSplitQTiles];
+  // merge blocks take them in this order; which tiles are cut depends on the cost model,
+  // so they need not be the last ones). Units enumerate query tiles from the last one;
+  // split tile i is query tile qt, which owns units ubase .. ubase + B*H*nch - 1, nch
+  // ranges for each (b, h): split_info[i] = ubase | nch << 10 | qt << 16, so a merge
+  // block finds everything about its tile in one word.
+  uint32_t split_info[kMaxSplitQTiles];
+  int n_split;        // split query tiles
   // Split plans: unit u is query tile (unit_info[u] & 0xff), key tiles from
   // ((>> 8) & 0x1ff) << unit_shift, count ((>> 17) & 0x1ff) << unit_shift (the last range
   // of a tile is clipped to the tile's key tiles), b*h (>> 26), so a workgroup decodes its
@@ -142,6 +142,14 @@ __device__ __forceinline__ int kernarg_byte(const uint8_t* table, int i) {
   const uint32_t w = reinterpret_cast<const uint32_t*>(table)[i >> 2];
   return (int)((w >> (8 * (i & 3))) & 0xffu);
 }
+
+// Fields of a split tile's word (Params::split_info).
+__device__ __host__ __forceinline__ constexpr uint32_t split_word(int ubase, int nch, int qt) {
+  return (uint32_t)ubase | (uint32_t)nch << 10 | (uint32_t)qt << 16;
+}
+__device__ __forceinline__ int split_ubase(uint32_t w) { return (int)(w & 0x3ffu); }
+__device__ __forceinline__ int split_nch(uint32_t w) { return (int)((w >> 10) & 0x1fu); }
+__device__ __forceinline__ int split_qtile(uint32_t w) { return (int)((w >> 16) & 0xffu); }
 
 // Kernel arguments are passed by value; keep them within the 4 KiB argument block.
 static_assert(sizeof(Params) <= 4096, "forward kernel arguments exceed 4 KiB");

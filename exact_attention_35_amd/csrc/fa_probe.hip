@@ -21,10 +21,23 @@
 
 namespace {
 
-__global__ __launch_bounds__(256) void copy_probe(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                                  int64_t n16) {
+// Each thread keeps four 16-byte loads in flight before it stores them (one load at a time
+// leaves the memory system idle between round trips).
+__global__ __launch_bounds__(256) void copy_probe(const fa::u32x4* __restrict__ src,
+                                                  fa::u32x4* __restrict__ dst, int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const fa::u32x4 a = __builtin_nontemporal_load(src + i);
+    const fa::u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const fa::u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const fa::u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    __builtin_nontemporal_store(a, dst + i);
+    __builtin_nontemporal_store(b, dst + i + stride);
+    __builtin_nontemporal_store(c, dst + i + 2 * stride);
+    __builtin_nontemporal_store(d, dst + i + 3 * stride);
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
 }
 
 // Each wave runs `iters` rounds of four independent 32x32x16 bf16 MFMA chains on
@@ -67,7 +80,7 @@ int fa_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   const int64_t want = (n16 + 255) / 256;
   const int grid = (int)(want < (int64_t)cus * 16 ? want : (int64_t)cus * 16);
   hipLaunchKernelGGL(copy_probe, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
+                     static_cast<const fa::u32x4*>(src), static_cast<fa::u32x4*>(dst), n16);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

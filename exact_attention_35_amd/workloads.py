@@ -91,6 +91,16 @@ WORKLOADS = {
 # The order the workloads are listed in (small fp32 case first, headline case second).
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# The traffic sweep: causal bf16 heads of d = dv = 128 at a fixed B*H*N = 32768 rows, from
+# 16 heads of 2048 to one head of 32768, with the headline's distribution (N(0, 1)). The
+# pages' IO analysis of the blockwise method puts its K/V traffic at Theta(N^2 d^2 / M);
+# at fixed B*H*N the quadratic term grows with N while the minimum bytes stay fixed.
+for _h, _n in ((16, 2048), (8, 4096), (4, 8192), (2, 16384), (1, 32768)):
+    _name = f"bf16_causal_sweep_h{_h}_n{_n}_d128"
+    WORKLOADS[_name] = Workload(_name, B=1, H=_h, N=_n, d=128, dv=128, dtype="bf16", layout="bhnd",
+                                causal=True, bias=False, seed=36000 + _n)
+del _h, _n, _name
+
 
 def workload(name_or_index) -> Workload:
     if isinstance(name_or_index, int):
