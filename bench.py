@@ -7,13 +7,16 @@ d = dv = 128, causal (the single-head L = 8192 example of the page
 Inputs are drawn once and resident in HBM before timing starts.
 
 Printed: one JSON line with the throughput in algorithmic TFLOP/s over the timed steps
-(2*(d+dv) per allowed query/key pair, softmax not counted); the roofline of the
-dominant kernel: the median (with p10, p90) of at least 50 launches, each timed by its own
-HIP events on the stream it is launched on, warm (back to back) and cold (a 1 GiB cache
-flush, untimed, before each launch), against the published peak and against the
-ceilings the library's probes measure on this device (streaming copy for B_max, bf16
-MFMA chains for P_max); and the CPU oracle timed on this host as a reported baseline
-(all threads, and one thread for a per-core figure).
+(2*(d+dv) per allowed query/key pair, softmax not counted; wall clock, nothing
+instrumented); the roofline of the dominant kernel: its own launch duration, stamped at
+the kernel's start and end by HIP events attached to each dispatch on the stream it is
+launched on (the library's launch timer), as the mean, median, p10 and p90 over at least
+50 back-to-back launches (warm) and over as many launches each after a 1 GiB cache flush
+(cold), against the published peak and against the ceilings the library's probes measure
+on this device (streaming copy for B_max, bf16 MFMA chains for P_max); the step period
+(HIP events around the timed steps, which adds the gap between consecutive kernels); and
+the CPU oracle timed on this host as a reported baseline (all threads, and one thread for
+a per-core figure).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
   python bench.py --pass bwd [...]  # the gradients (fa_bwd) of the same workload instead
@@ -69,7 +72,8 @@ def read_traffic(workload: str, kind: str = "fwd_mfma", src: str = KERNEL_SRC):
 def launch_stats(launch, stream, reps, flush=None):
     """Device time of `reps` launches, each bracketed by its own pair of HIP events on
     `stream` (the stream the library launches on). With `flush`, that untimed work runs
-    on the stream before every launch (a cold-cache run). Returns the sorted times (s)."""
+    on the stream before every launch (a cold-cache run). Returns the sorted times (s).
+    Each time includes the gap between the start event and the kernel's start."""
     import numpy as np
     import torch
 
@@ -82,6 +86,41 @@ def launch_stats(launch, stream, reps, flush=None):
         e1.record(stream)
     torch.cuda.synchronize()
     return np.sort(np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e-3)
+
+
+def kernel_stats(launch, reps, flush=None):
+    """Durations of the main kernel in `reps` calls of `launch`, from the library's launch
+    timer: each launch's own dispatch stamps its pair of events at the kernel's start and
+    end, the interval a kernel-trace profiler reports. With `flush`, that untimed work runs
+    before every call (a cold-cache run). Returns the sorted times (s)."""
+    import numpy as np
+
+    from exact_attention_35_amd import capi
+
+    capi.fa_probe_timer_arm(reps)
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        launch()
+    return np.sort(np.array(capi.fa_probe_timer_read(reps)) * 1e-6)
+
+
+def timed_region(step, stream, steps):
+    """The timed steps: wall clock around them, synchronised on both sides (`value`), and a
+    pair of HIP events on the library's stream around the same steps (the step period).
+    Nothing in them is instrumented. Returns (wall s, event s)."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) * 1e-3
 
 
 def summary_us(t):
@@ -328,18 +367,15 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    # the timed steps (wall clock, synchronised on both sides): `value`
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # the dominant kernel's launch time: each launch bracketed by its own events on the
-    # library's stream, warm (back to back) and cold (a 1 GiB flush before each)
+    # the timed steps: wall clock (`value`) and HIP events on the library's stream around
+    # them (the step period: the kernel plus the gap before the next one starts)
+    wall, ev_s = timed_region(step, stream, args.steps)
+    # the kernel's own launch duration: the timed steps again, back to back, each launch
+    # stamped at its start and end by its dispatch (warm), and the same after a 1 GiB flush
+    # (cold); stamping adds work between launches, so it stays out of the timed steps
     reps = max(args.reps, args.steps)
-    warm = launch_stats(step, stream, reps)
-    cold = launch_stats(step, stream, reps, flush=make_flush(dev, stream))
+    warm = kernel_stats(step, reps)
+    cold = kernel_stats(step, reps, flush=make_flush(dev, stream))
     ceil = {"hbm_GBps": None, "mfma_bf16_TFLOPs": None} if args.no_ceilings else measured_ceilings(dev, stream)
 
     flops = rf.alg_flops(w.B, w.H, w.N, w.d, w.dv, w.causal, Nq=w.n_q)
@@ -347,6 +383,8 @@ def main() -> int:
     bias_bytes = (w.H * w.n_q * w.N * 4) if w.bias else 0
     min_b = rf.min_bytes(w.B, w.H, w.N, w.d, w.dv, elem, bias_bytes=bias_bytes, Nq=w.n_q)
     value = flops * args.steps / wall / 1e12
+    period = ev_s / args.steps
+    avg = float(np.mean(warm))
     med_w, med_c = float(np.median(warm)), float(np.median(cold))
     # the ceiling of the kernel that runs: bf16 on the matrix cores; fp32 on the general
     # kernel's vector ALUs
@@ -361,19 +399,24 @@ def main() -> int:
     traffic = read_traffic(w.name)
     if bound == "hbm":
         meas = ceil["hbm_GBps"]
-        roof = {"bound": "hbm", "achieved": min_b / med_w / 1e9, "peak": 8000.0, "unit": "GB/s",
-                "frac": min_b / med_w / 8e12, "traffic": traffic,
-                "measured_peak": meas, "frac_of_measured": (min_b / med_w / 1e9 / meas) if meas else None,
-                "cold_achieved": min_b / med_c / 1e9, "cold_frac": min_b / med_c / 8e12}
+        rate = lambda t: min_b / t / 1e9
+        roof = {"bound": "hbm", "peak": 8000.0, "unit": "GB/s"}
     else:
         meas = ceil["mfma_bf16_TFLOPs"] if mfma else None
-        roof = {"bound": bound, "achieved": flops / med_w / 1e12, "peak": peak, "unit": "TFLOP/s",
-                "frac": flops / med_w / 1e12 / peak, "traffic": traffic,
-                "measured_peak": meas, "frac_of_measured": (flops / med_w / 1e12 / meas) if meas else None,
-                "cold_achieved": flops / med_c / 1e12, "cold_frac": flops / med_c / 1e12 / peak}
+        rate = lambda t: flops / t / 1e12
+        roof = {"bound": bound, "peak": peak, "unit": "TFLOP/s"}
+    roof.update({"achieved": rate(avg), "frac": rate(avg) / roof["peak"], "traffic": traffic,
+                 "median_achieved": rate(med_w), "median_frac": rate(med_w) / roof["peak"],
+                 "measured_peak": meas, "frac_of_measured": (rate(avg) / meas) if meas else None,
+                 "cold_achieved": rate(med_c), "cold_frac": rate(med_c) / roof["peak"]})
     roof.update({"kernel": "fwd_mfma" if mfma else "fwd_generic",
-                 "avg_launch_us": med_w * 1e6,
+                 "avg_launch_us": avg * 1e6, "step_period_us": period * 1e6,
                  "launch_us_warm": summary_us(warm), "launch_us_cold": summary_us(cold),
+                 "timing": ("avg_launch_us / launch_us_warm: the kernel's own start/end stamps (HIP events "
+                            "that hipExtLaunchKernelGGL attaches to the dispatch, on the library's stream) "
+                            "over max(reps, steps) back-to-back repeats of the timed step; launch_us_cold: "
+                            "the same after a 1 GiB flush each; step_period_us: HIP events around the "
+                            "uninstrumented timed steps, per step (adds the gap between consecutive kernels)"),
                  "alg_flops_per_launch": flops, "min_bytes_per_launch": min_b,
                  "measured_ceilings": ceil,
                  "kernel_source_sha256_16": kernel_sha()})
@@ -514,16 +557,18 @@ def bench_bwd(args, w, inp, gpu, out, lse) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # one fa_bwd call (all its kernels) bracketed by its own events, warm and cold
+    # the timed steps: wall clock (`value`) and HIP events around them on the library's
+    # stream (the average fa_bwd call, all its kernels)
+    wall, ev_s, _ = timed_region(step, stream, args.steps)
+    avg_call_s = ev_s / args.steps
+    # one fa_bwd call (all its kernels) bracketed by its own events, warm and cold; and
+    # the dK/dV/dQ kernel alone, from its own start/end stamps
     reps = max(args.reps, args.steps)
+    flush = make_flush(dev, stream)
     warm = launch_stats(step, stream, reps)
-    cold = launch_stats(step, stream, reps, flush=make_flush(dev, stream))
-    avg_call_s = float(np.median(warm))
+    cold = launch_stats(step, stream, reps, flush=flush)
+    main_warm = kernel_stats(step, reps)
+    main_cold = kernel_stats(step, reps, flush=flush)
 
     flops = rf.alg_flops_bwd(w.B, w.H, w.N, w.d, w.dv, w.causal)
     peak = rf.MI355X_PEAK_BF16_FLOPS / 1e12
@@ -543,14 +588,21 @@ def bench_bwd(args, w, inp, gpu, out, lse) -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs and dO of the workload's shape)",
         "config": {"workload": w.name, "pass": "bwd", "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv,
-                   "causal": w.causal, "bias": w.bias, "layout": w.layout, "parallelism": "single GPU"},
+                   "causal": w.causal, "bias": w.bias, "layout": w.layout, "parallelism": "single GPU",
+                   "workspace_bytes": int(capi.fa_bwd_workspace_size(w.B, w.H, w.N, w.d, w.dv, capi.FA_BF16,
+                                                                     w.causal))},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": read_traffic(w.name, "bwd", BWD_SRC),
                      "cold_achieved": flops / float(np.median(cold)) / 1e12,
                      "cold_frac": flops / float(np.median(cold)) / 1e12 / peak,
                      "kernel": "bwd_rowstat + bwd_mfma [+ bwd_reduce] (one fa_bwd call)",
                      "avg_launch_us": avg_call_s * 1e6, "launch_us_warm": summary_us(warm),
-                     "launch_us_cold": summary_us(cold), "alg_flops_per_launch": flops,
+                     "launch_us_cold": summary_us(cold),
+                     "main_kernel_us_warm": summary_us(main_warm), "main_kernel_us_cold": summary_us(main_cold),
+                     "timing": ("avg_launch_us: HIP events on the library's stream around the timed calls, "
+                                "per call; launch_us_*: one call between its own pair of events; "
+                                "main_kernel_us_*: bwd_mfma's own start/end stamps (hipExtLaunchKernelGGL events)"),
+                     "alg_flops_per_launch": flops,
                      "min_bytes_per_launch": rf.min_bytes_bwd(w.B, w.H, w.N, w.d, w.dv, 2, bias_bytes),
                      "kernel_source_sha256_16": hashlib.sha256(open(BWD_SRC, "rb").read()).hexdigest()[:16]},
     }

@@ -18,7 +18,8 @@ __all__ = [
     "fa_status_string", "fa_version", "fa_shutdown", "fa_plan_describe", "make_strides", "FaStrides",
     "FaPlanInfo", "EXPORTED", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "FaBwdStrides",
     "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size", "fa_plan_describe_qk", "fa_fwd_qk_noalloc",
-    "fa_probe_copy", "fa_probe_mfma", "fa_probe_mfma_flops",
+    "fa_probe_copy", "fa_probe_mfma", "fa_probe_mfma_flops", "fa_probe_timer_arm", "fa_probe_timer_read",
+    "FA_PROBE_TIMER_MAX",
 ]
 
 FA_OK = 0
@@ -38,7 +39,8 @@ EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
             "fa_version", "fa_shutdown", "fa_plan_describe", "fa_bwd", "fa_bwd_ex",
             "fa_bwd_workspace_size", "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size",
             "fa_plan_describe_qk", "fa_fwd_qk_noalloc", "fa_probe_copy", "fa_probe_mfma",
-            "fa_probe_mfma_flops")
+            "fa_probe_mfma_flops", "fa_probe_timer_arm", "fa_probe_timer_read")
+FA_PROBE_TIMER_MAX = 4096
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -129,6 +131,10 @@ def lib():
     L.fa_probe_mfma.restype = ctypes.c_int
     L.fa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     L.fa_probe_mfma_flops.restype = ctypes.c_double
+    L.fa_probe_timer_arm.argtypes = [ctypes.c_int]
+    L.fa_probe_timer_arm.restype = ctypes.c_int
+    L.fa_probe_timer_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int]
+    L.fa_probe_timer_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -447,3 +453,17 @@ def fa_probe_mfma(out, blocks, iters, stream=None):
     _same_device((("out", out),))
     _check(lib().fa_probe_mfma(_ptr(out), int(blocks), int(iters), _stream_handle(stream, out.device)))
     return float(lib().fa_probe_mfma_flops(int(blocks), int(iters)))
+
+
+def fa_probe_timer_arm(n):
+    """Arms kernel-timestamp timing for the calling thread's next n main-kernel launches."""
+    if not 0 <= int(n) <= FA_PROBE_TIMER_MAX:
+        raise FaError(STATUS["FA_ERR_NULL"], f"n must lie in [0, {FA_PROBE_TIMER_MAX}]")
+    _check(lib().fa_probe_timer_arm(int(n)))
+
+
+def fa_probe_timer_read(n):
+    """Waits for the n armed launches and returns their durations in microseconds."""
+    buf = (ctypes.c_float * max(int(n), 1))()
+    _check(lib().fa_probe_timer_read(buf, int(n)))
+    return [float(buf[i]) for i in range(int(n))]

@@ -644,9 +644,9 @@ hipError_t launch_bwd_dd(const BwdParams& p, int grid, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.bias)
-    hipLaunchKernelGGL((bwd_mfma<E, D, DV, true>), dim3(grid), dim3(256), 0, stream, p);
+    FA_LAUNCH_MAIN((bwd_mfma<E, D, DV, true>), dim3(grid), dim3(256), stream, p);
   else
-    hipLaunchKernelGGL((bwd_mfma<E, D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
+    FA_LAUNCH_MAIN((bwd_mfma<E, D, DV, false>), dim3(grid), dim3(256), stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || !p.split) return e;
   hipLaunchKernelGGL((bwd_reduce<E, D, DV>), dim3(kBwdKT / kReduceRows, p.B * p.H, 2 * p.n_tiles), dim3(256), 0,

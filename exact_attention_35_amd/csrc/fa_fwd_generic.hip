@@ -150,10 +150,10 @@ inline int width_bin(int x) { return x <= 32 ? 32 : x <= 64 ? 64 : x <= 128 ? 12
 template <typename T, int D>
 hipError_t launch_dv(const Params& p, dim3 grid, hipStream_t stream) {
   switch (width_bin(p.dv)) {
-    case 32: hipLaunchKernelGGL((fwd_generic<T, D, 32>), grid, dim3(256), 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((fwd_generic<T, D, 64>), grid, dim3(256), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((fwd_generic<T, D, 128>), grid, dim3(256), 0, stream, p); break;
-    default: hipLaunchKernelGGL((fwd_generic<T, D, 256>), grid, dim3(256), 0, stream, p); break;
+    case 32: FA_LAUNCH_MAIN((fwd_generic<T, D, 32>), grid, dim3(256), stream, p); break;
+    case 64: FA_LAUNCH_MAIN((fwd_generic<T, D, 64>), grid, dim3(256), stream, p); break;
+    case 128: FA_LAUNCH_MAIN((fwd_generic<T, D, 128>), grid, dim3(256), stream, p); break;
+    default: FA_LAUNCH_MAIN((fwd_generic<T, D, 256>), grid, dim3(256), stream, p); break;
   }
   return hipGetLastError();
 }
@@ -164,10 +164,10 @@ template <int D, int DV>
 hipError_t launch_tile(const Params& p, hipStream_t stream) {
   auto grid = [&](int bm) { return dim3((unsigned)(((p.Nq + bm - 1) / bm) * (int64_t)p.B * p.H)); };
   switch (p.gtile) {
-    case 1: hipLaunchKernelGGL((fwd_generic<float, D, DV, 32, 32>), grid(32), dim3(128), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((fwd_generic<float, D, DV, 64, 16>), grid(64), dim3(256), 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((fwd_generic<float, D, DV, 64, 64>), grid(64), dim3(256), 0, stream, p); break;
-    default: hipLaunchKernelGGL((fwd_generic<float, D, DV, 128, 32>), grid(128), dim3(512), 0, stream, p); break;
+    case 1: FA_LAUNCH_MAIN((fwd_generic<float, D, DV, 32, 32>), grid(32), dim3(128), stream, p); break;
+    case 2: FA_LAUNCH_MAIN((fwd_generic<float, D, DV, 64, 16>), grid(64), dim3(256), stream, p); break;
+    case 3: FA_LAUNCH_MAIN((fwd_generic<float, D, DV, 64, 64>), grid(64), dim3(256), stream, p); break;
+    default: FA_LAUNCH_MAIN((fwd_generic<float, D, DV, 128, 32>), grid(128), dim3(512), stream, p); break;
   }
   return hipGetLastError();
 }

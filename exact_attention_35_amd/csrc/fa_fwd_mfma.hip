@@ -850,9 +850,9 @@ FA_FWD_VARIANTS(_Float16)
 template <typename E, int D, int DV>
 hipError_t launch_dd(const Params& p, int grid, bool merge, hipStream_t stream) {
   if (p.bias)
-    hipLaunchKernelGGL((fwd_mfma<E, D, DV, true>), dim3(grid), dim3(256), 0, stream, p);
+    FA_LAUNCH_MAIN((fwd_mfma<E, D, DV, true>), dim3(grid), dim3(256), stream, p);
   else
-    hipLaunchKernelGGL((fwd_mfma<E, D, DV, false>), dim3(grid), dim3(256), 0, stream, p);
+    FA_LAUNCH_MAIN((fwd_mfma<E, D, DV, false>), dim3(grid), dim3(256), stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !merge) return e;
   hipLaunchKernelGGL((merge_split<E, DV>), dim3(merge_groups(DV, 1), p.B * p.H, p.n_split), dim3(256), 0, stream, p);

@@ -1,6 +1,7 @@
 // Internal interface between the host dispatcher (fa_api.cpp) and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -169,4 +170,25 @@ hipError_t launch_generic(const Params& p, int dtype, hipStream_t stream);
 // dK/dV and dQ units, then (split plans) the reduction of the chunk partials.
 hipError_t launch_bwd(const BwdParams& p, int grid, bool fp16, hipStream_t stream);
 
+// Kernel-timestamp timing of the main kernels (fwd_mfma, fwd_generic, bwd_mfma). The timing
+// probe arms pairs of events on the calling thread; each main-kernel launch on that thread
+// takes the next armed pair, or none when nothing is armed (the normal case).
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+LaunchEvents next_launch_events();
+
 }  // namespace fa
+
+// Launches a main kernel: with an armed pair of events, through hipExtLaunchKernelGGL,
+// which stamps the events with the kernel's own start and end; otherwise as usual.
+#define FA_LAUNCH_MAIN(kernel, grid, block, stream, ...)                                        \
+  do {                                                                                         \
+    const ::fa::LaunchEvents fa_ev_ = ::fa::next_launch_events();                              \
+    if (fa_ev_.start)                                                                          \
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, fa_ev_.start, fa_ev_.stop, 0u,     \
+                            __VA_ARGS__);                                                      \
+    else                                                                                       \
+      hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);                         \
+  } while (0)

@@ -11,11 +11,18 @@
 //  * mfma: back-to-back v_mfma_f32_32x32x16_bf16 (the instruction the attention kernel
 //    spends its FLOPs on), four independent accumulator chains per wave and two waves
 //    per SIMD, as the attention kernel runs, with no memory traffic in the loop.
+// The same page asks for repetitions, quantiles and cold against warm runs. The launch
+// timer below gives each main-kernel launch its own pair of events stamped by the kernel's
+// dispatch itself, so one launch's time excludes the queue gap that a pair of events
+// recorded around the launch would add.
 
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 
+#include <vector>
+
+#include "fa_internal.h"
 #include "fa_mfma_common.h"
 #include "fa_probe.h"
 
@@ -65,9 +72,53 @@ __global__ __launch_bounds__(256, 2) void mfma_probe(float* __restrict__ out, in
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// The calling thread's launch timer: a grow-only pool of event pairs (created on the device
+// current when armed, kept until the process ends), how many are armed, and how many of
+// those the main-kernel launches have taken.
+struct LaunchTimer {
+  std::vector<hipEvent_t> ev;  // start, stop, start, stop, ...
+  int armed = 0;
+  int taken = 0;
+};
+thread_local LaunchTimer t_timer;
+
 }  // namespace
 
+fa::LaunchEvents fa::next_launch_events() {
+  LaunchTimer& t = t_timer;
+  if (t.taken >= t.armed) return {nullptr, nullptr};
+  const int i = t.taken++;
+  return {t.ev[2 * i], t.ev[2 * i + 1]};
+}
+
 extern "C" {
+
+int fa_probe_timer_arm(int n) {
+  LaunchTimer& t = t_timer;
+  if (n < 0 || n > FA_PROBE_TIMER_MAX) return FA_ERR_NULL;
+  while ((int)t.ev.size() < 2 * n) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return FA_ERR_DEVICE;
+    t.ev.push_back(e);
+  }
+  t.armed = n;
+  t.taken = 0;
+  return FA_OK;
+}
+
+int fa_probe_timer_read(float* us, int n) {
+  LaunchTimer& t = t_timer;
+  if (!us || n < 0 || n != t.taken) return FA_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]) != hipSuccess)
+      return FA_ERR_DEVICE;
+    us[i] = ms * 1000.f;
+  }
+  t.armed = t.taken = 0;
+  return FA_OK;
+}
 
 int fa_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   if (!src || !dst || bytes <= 0 || bytes % 16 != 0 || ((uintptr_t)src | (uintptr_t)dst) % 16 != 0)

@@ -43,6 +43,31 @@ int fa_probe_mfma(float* out, int blocks, int iters, void* stream);
 /* The FLOPs one fa_probe_mfma launch performs: blocks * 4 waves * iters * 4 * 32768. */
 double fa_probe_mfma_flops(int blocks, int iters);
 
+/* Most launches one fa_probe_timer_arm call can arm. */
+#define FA_PROBE_TIMER_MAX 4096
+
+/*
+ * fa_probe_timer_arm — arms kernel-timestamp timing for the next n launches, made by the
+ * calling thread, of the main attention kernels (the forward kernel of fa_fwd, fa_fwd_qk
+ * and their variants, and the dK/dV/dQ kernel of fa_bwd; not the merge, row-statistics or
+ * reduction kernels). Each such launch then goes through hipExtLaunchKernelGGL with its
+ * own pair of events, which the kernel's dispatch stamps at its start and at its end, so
+ * the time excludes the host and queue gaps around the launch (the same interval a
+ * kernel-trace profiler reports). The events are created by the library on the device
+ * current at this call (a grow-only pool per thread, released at process end). Arming
+ * again drops the pairs not yet read. 0 <= n <= FA_PROBE_TIMER_MAX, else FA_ERR_NULL;
+ * FA_ERR_DEVICE if an event cannot be created. The launches themselves are unchanged.
+ */
+int fa_probe_timer_arm(int n);
+
+/*
+ * fa_probe_timer_read — waits for the armed launches and writes the duration of each, in
+ * microseconds, in launch order, to us[0 .. n-1] (host memory, caller-owned); n must
+ * equal the number of armed launches made since fa_probe_timer_arm (else FA_ERR_NULL).
+ * Disarms the timer. FA_ERR_DEVICE if the events cannot be read.
+ */
+int fa_probe_timer_read(float* us, int n);
+
 #ifdef __cplusplus
 }
 #endif

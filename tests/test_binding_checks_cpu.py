@@ -86,3 +86,17 @@ def test_gradient_arguments_are_checked():
     assert _status(e) == capi.STATUS["FA_ERR_DTYPE"]
     with pytest.raises(capi.FaError, match="not a device tensor"):
         capi.fa_bwd(q, k, v, out, lse, do)
+
+
+def test_launch_timer_arguments_are_checked():
+    # out-of-range counts are refused by the binding and by the library itself, before any
+    # event is created; arming zero launches and reading zero back touches no device
+    for n in (-1, capi.FA_PROBE_TIMER_MAX + 1):
+        with pytest.raises(capi.FaError):
+            capi.fa_probe_timer_arm(n)
+        assert capi.lib().fa_probe_timer_arm(n) == capi.STATUS["FA_ERR_NULL"]
+    assert capi.lib().fa_probe_timer_read(None, 0) == capi.STATUS["FA_ERR_NULL"]
+    capi.fa_probe_timer_arm(0)
+    assert capi.fa_probe_timer_read(0) == []
+    with pytest.raises(capi.FaError):
+        capi.fa_probe_timer_read(1)      # nothing was armed and launched

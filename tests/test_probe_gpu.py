@@ -1,0 +1,94 @@
+"""The measurement probes of include/fa_probe.h on the GPU: the streaming copy copies, the
+matrix-core probe reports its FLOP count, and the launch timer stamps each armed main-kernel
+launch with an interval that lies inside the launch's own event bracket, without changing
+what the launch computes.
+"""
+
+import numpy as np
+import pytest
+
+from exact_attention_35_amd import capi, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def test_copy_probe_copies(gpu_device):
+    import torch
+
+    src = torch.arange(1 << 22, dtype=torch.float32, device=gpu_device)
+    dst = torch.zeros_like(src)
+    capi.fa_probe_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    odd = torch.arange(1000, dtype=torch.float32, device=gpu_device)   # a ragged tail: 4000 bytes
+    dodd = torch.zeros_like(odd)
+    capi.fa_probe_copy(odd, dodd)
+    torch.cuda.synchronize()
+    assert torch.equal(odd, dodd)
+
+
+def test_mfma_probe_flops(gpu_device):
+    import torch
+
+    out = torch.full((8 * 256,), float("nan"), dtype=torch.float32, device=gpu_device)
+    flops = capi.fa_probe_mfma(out, 8, 10)
+    torch.cuda.synchronize()
+    assert flops == 8 * 4 * 10 * 4 * 32768
+    assert torch.isfinite(out).all()
+
+
+def _fwd_setup(dev, name="bf16_causal_sweep_h8_n4096_d128"):
+    import torch
+
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w, device="cpu")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    out = torch.empty(w.B, w.H, w.N, w.dv, dtype=q.dtype, device=dev)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    return q, k, v, out, lse
+
+
+def test_launch_timer_stamps_inside_event_bracket(gpu_device):
+    import torch
+
+    q, k, v, out, lse = _fwd_setup(gpu_device)
+    stream = torch.cuda.current_stream(gpu_device)
+    call = lambda: capi.fa_fwd(q, k, v, causal=True, out=out, lse=lse, stream=stream)
+    call()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+
+    n = 12
+    brackets = []
+    capi.fa_probe_timer_arm(n)
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        brackets.append((e0, e1))
+    stamps = np.array(capi.fa_probe_timer_read(n))
+    torch.cuda.synchronize()
+    outer = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in brackets])
+    print(f"kernel stamps us: median {np.median(stamps):.2f}; event brackets us: median {np.median(outer):.2f}")
+    assert stamps.shape == (n,) and (stamps > 0).all()
+    # the kernel's own interval is a sub-interval of the bracket around its launch
+    assert (stamps <= outer * 1.01 + 1.0).all(), (stamps, outer)
+    # timing a launch does not change what it computes
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+    # after a read the timer is disarmed: further launches take no events
+    call()
+    assert capi.fa_probe_timer_read(0) == []
+
+
+def test_launch_timer_count_mismatch_is_an_error(gpu_device):
+    import torch
+
+    q, k, v, out, lse = _fwd_setup(gpu_device, "bf16_causal_sweep_h16_n2048_d128")
+    capi.fa_probe_timer_arm(3)
+    capi.fa_fwd(q, k, v, causal=True, out=out, lse=lse)
+    capi.fa_fwd(q, k, v, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    with pytest.raises(capi.FaError):
+        capi.fa_probe_timer_read(3)      # only two of the three armed launches happened
+    assert len(capi.fa_probe_timer_read(2)) == 2
