@@ -4,7 +4,9 @@
 A step is one fa_fwd call over the headline workload: one bf16 head, N = 8192,
 d = dv = 128, causal (the single-head L = 8192 example of the page
 "AI Infra 第5章图解: 算子与运行时", section "FlashAttention: Softmax 也能逐块算").
-Inputs are drawn once and resident in HBM before timing starts.
+Inputs are drawn once and resident in HBM before timing starts. Warm-up: W untimed steps,
+continued until at least 0.2 s of GPU work has run (the clocks settle under the load),
+reported as warmup_steps_run.
 
 Printed: one JSON line with the throughput in algorithmic TFLOP/s over the timed steps
 (2*(d+dv) per allowed query/key pair, softmax not counted; wall clock, nothing
@@ -103,6 +105,31 @@ def kernel_stats(launch, reps, flush=None):
             flush()
         launch()
     return np.sort(np.array(capi.fa_probe_timer_read(reps)) * 1e-6)
+
+
+WARMUP_MIN_S = 0.2
+
+
+def warm_up(step, steps, min_s=WARMUP_MIN_S):
+    """Untimed warm-up: `steps` steps, continued in batches of 16 until at least `min_s`
+    seconds of GPU work have passed. Under a new load the GPU's clocks take tens of
+    milliseconds to settle: on the headline workload 20 warm-up steps leave the step period
+    at 30.4-31.3 us and the kernel at 27.5 us, 2000 steps at 27.0 and 26.4 us. Returns the
+    number of steps run."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(steps):
+        step()
+        n += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_s:
+        for _ in range(16):
+            step()
+        n += 16
+        torch.cuda.synchronize()
+    return n
 
 
 def timed_region(step, stream, steps):
@@ -363,9 +390,7 @@ def main() -> int:
         if st:
             raise capi.FaError(st, capi.fa_status_string(st))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmed = warm_up(step, args.warmup)
 
     # the timed steps: wall clock (`value`) and HIP events on the library's stream around
     # them (the step period: the kernel plus the gap before the next one starts)
@@ -430,6 +455,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warmed,
         "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -554,12 +580,10 @@ def bench_bwd(args, w, inp, gpu, out, lse) -> int:
         capi.fa_bwd(gpu["q"], gpu["k"], gpu["v"], out, lse, do, bias=gpu["bias"], causal=w.causal,
                     grad_q=dq, grad_k=dk, grad_v=dv, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmed = warm_up(step, args.warmup)
     # the timed steps: wall clock (`value`) and HIP events around them on the library's
     # stream (the average fa_bwd call, all its kernels)
-    wall, ev_s, _ = timed_region(step, stream, args.steps)
+    wall, ev_s = timed_region(step, stream, args.steps)
     avg_call_s = ev_s / args.steps
     # one fa_bwd call (all its kernels) bracketed by its own events, warm and cold; and
     # the dK/dV/dQ kernel alone, from its own start/end stamps
@@ -581,6 +605,7 @@ def bench_bwd(args, w, inp, gpu, out, lse) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warmed,
         "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
