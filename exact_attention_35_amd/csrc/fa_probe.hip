@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256, 2) void mfma_probe(float* __restrict__ out, in
 // those the main-kernel launches have taken.
 struct LaunchTimer {
   std::vector<hipEvent_t> ev;  // start, stop, start, stop, ...
+  int dev = -1;                // the device the events belong to
   int armed = 0;
   int taken = 0;
 };
@@ -96,6 +97,15 @@ extern "C" {
 int fa_probe_timer_arm(int n) {
   LaunchTimer& t = t_timer;
   if (n < 0 || n > FA_PROBE_TIMER_MAX) return FA_ERR_NULL;
+  t.armed = t.taken = 0;
+  if (n == 0) return FA_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_DEVICE;
+  if (dev != t.dev) {  // events of another device: start a new pool on this one
+    for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+    t.ev.clear();
+    t.dev = dev;
+  }
   while ((int)t.ev.size() < 2 * n) {
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) return FA_ERR_DEVICE;

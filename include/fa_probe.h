@@ -54,9 +54,11 @@ double fa_probe_mfma_flops(int blocks, int iters);
  * own pair of events, which the kernel's dispatch stamps at its start and at its end, so
  * the time excludes the host and queue gaps around the launch (the same interval a
  * kernel-trace profiler reports). The events are created by the library on the device
- * current at this call (a grow-only pool per thread, released at process end). Arming
- * again drops the pairs not yet read. 0 <= n <= FA_PROBE_TIMER_MAX, else FA_ERR_NULL;
- * FA_ERR_DEVICE if an event cannot be created. The launches themselves are unchanged.
+ * current at this call (a grow-only pool per thread, released at process end, or when the
+ * thread arms the timer on another device); the armed launches must be made on that
+ * device. Arming again drops the pairs not yet read; n = 0 disarms. 0 <= n <=
+ * FA_PROBE_TIMER_MAX, else FA_ERR_NULL; FA_ERR_DEVICE if an event cannot be created. The
+ * launches themselves are unchanged.
  */
 int fa_probe_timer_arm(int n);
 
