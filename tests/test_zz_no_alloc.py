@@ -66,3 +66,30 @@ def test_noalloc_requires_outputs(gpu_device):
     torch.cuda.synchronize()
     assert torch.equal(o2, ref[0]) and torch.equal(l2, ref[1])
     assert np.isfinite(l2.cpu().numpy()).all()
+
+
+def test_noalloc_fp16_then_bf16(gpu_device):
+    """fp16 partial states in the same scratch array, then a bf16 call over them."""
+    import torch
+
+    w = workloads.workload(1).resized(N=2600)
+    inp, g, _, _ = _case(w, gpu_device)
+    h = {n: g[n].to(torch.float16) for n in ("q", "k", "v")}
+    out = torch.full((w.B, w.H, w.N, w.dv), float("nan"), dtype=torch.float16, device=gpu_device)
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=gpu_device)
+    assert capi.fa_fwd_qk_workspace_size(w.B, w.H, w.N, w.N, w.d, w.dv, capi.FA_F16, True) > 0
+    capi.fa_fwd_qk_noalloc(h["q"], h["k"], h["v"], out, lse, causal=True)
+    ref_o, ref_l = capi.fa_fwd_qk(h["q"], h["k"], h["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    q16, k16, v16 = (h[n].cpu() for n in ("q", "k", "v"))
+    o_ref, l_ref, sc = sdpa_reference(q16, k16, v16, None, True, with_scale=True)
+    check_out(out, o_ref, "f16_mfma", "noalloc fp16", scale=sc)
+    check_lse(lse, l_ref, "noalloc fp16")
+    # a smaller bf16 call after it
+    w2 = workloads.workload(1).resized(N=1500)
+    inp2, g2, o2, l2 = _case(w2, gpu_device)
+    capi.fa_fwd_qk_noalloc(g2["q"], g2["k"], g2["v"], o2, l2, causal=True)
+    r2 = capi.fa_fwd_qk(g2["q"], g2["k"], g2["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, r2[0]) and torch.equal(l2, r2[1])
