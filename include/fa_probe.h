@@ -58,7 +58,9 @@ double fa_probe_mfma_flops(int blocks, int iters);
  * thread arms the timer on another device); the armed launches must be made on that
  * device. Arming again drops the pairs not yet read; n = 0 disarms. 0 <= n <=
  * FA_PROBE_TIMER_MAX, else FA_ERR_NULL; FA_ERR_DEVICE if an event cannot be created. The
- * launches themselves are unchanged.
+ * launches compute the same results; they cost a little more (the events add work between
+ * consecutive kernels), so a measured step should not be armed. Not for launches made
+ * while the stream is being captured into a graph.
  */
 int fa_probe_timer_arm(int n);
 
