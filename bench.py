@@ -434,6 +434,16 @@ def main() -> int:
                  "median_achieved": rate(med_w), "median_frac": rate(med_w) / roof["peak"],
                  "measured_peak": meas, "frac_of_measured": (rate(avg) / meas) if meas else None,
                  "cold_achieved": rate(med_c), "cold_frac": rate(med_c) / roof["peak"]})
+    # the attainable rate on the measured ceilings, min(P_max, B_max * I) with I = FLOPs per
+    # minimum byte (matrix-core kernels: P_max from the MFMA probe, B_max from the copy probe)
+    if mfma and ceil["mfma_bf16_TFLOPs"] and ceil["hbm_GBps"]:
+        p_max = ceil["mfma_bf16_TFLOPs"]
+        b_i = ceil["hbm_GBps"] * 1e9 * (flops / min_b) / 1e12
+        attain = min(p_max, b_i)
+        roof["measured_roofline"] = {"P_max_TFLOPs": p_max, "B_max_x_I_TFLOPs": b_i,
+                                     "intensity_flop_per_byte": flops / min_b, "attainable_TFLOPs": attain,
+                                     "achieved_TFLOPs": flops / avg / 1e12, "frac": flops / avg / 1e12 / attain,
+                                     "bound": "mfma" if p_max <= b_i else "hbm"}
     roof.update({"kernel": "fwd_mfma" if mfma else "fwd_generic",
                  "avg_launch_us": avg * 1e6, "step_period_us": period * 1e6,
                  "launch_us_warm": summary_us(warm), "launch_us_cold": summary_us(cold),
