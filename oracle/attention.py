@@ -34,6 +34,12 @@ Readings taken where the page is silent (each is listed in the design notes):
 
 Inputs are taken exactly as the GPU saw them (bf16 or fp32 values) and upcast to
 float64; upcasting bf16 or fp32 to float64 is exact.
+
+With ``with_scale=True`` the oracle also returns, per output element, the scale of the
+rounding errors a 16-bit kernel makes, S_ik = sqrt(sum_j P_ij^2 v_jk^2) (the terms that
+rounding the probabilities to 16 bits before P V multiplies), which sizes the 16-bit
+parity bar. It is pinned in tests/test_oracle_error_scales.py against an emulation of
+16-bit rounding, closed forms and planted kernel bugs.
 """
 
 from __future__ import annotations

@@ -30,6 +30,12 @@ Readings (each is listed in the design notes): the same ones as the forward orac
 aligned; bias and mask add; bias broadcasts over batch or heads). A row with no
 allowed key has no gradient (dQ row = 0, and it adds nothing to dK, dV): a
 convention, parity unpinned.
+
+With ``with_scales=True`` the oracle also returns the rounding-error scales sq, sk, sv of
+every gradient element (the root-sum-square of the terms that 16-bit roundings of P, dS
+and O multiply, plus the shared error of D_i = dO_i . O_i), which size the gradient
+parity bar; they are pinned in tests/test_oracle_error_scales.py against an emulation of
+16-bit arithmetic and against planted slips in their formulas.
 """
 
 from __future__ import annotations
