@@ -171,6 +171,47 @@ def make_flush(dev, stream, nbytes=1 << 30):
     return flush
 
 
+def issue_probe():
+    """The issue probe of include/fa_probe.h on every CU: cycles per MFMA of an MFMA wave
+    with K vector ops (or E exponentials) after each MFMA, one wave per SIMD; and, with two
+    waves per SIMD, an MFMA wave beside a vector-ALU wave, each alone and together, and two
+    vector-ALU waves. Cycles are the shader clock's (s_memtime); MHz from s_memrealtime."""
+    import torch
+
+    from exact_attention_35_amd import capi
+
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    iters = 20000
+
+    def run(role, k, e):
+        capi.fa_probe_issue(role, k, e, cus, iters)
+        cyc, rt, waves = capi.fa_probe_issue(role, k, e, cus, iters)
+        return cyc, waves, 100.0 * sum(cyc) / max(sum(rt), 1)
+
+    rows = []
+    for k, e in ((0, 0), (2, 0), (4, 0), (6, 0), (8, 0), (12, 0), (0, 1), (0, 2), (0, 4), (4, 1), (4, 2)):
+        cyc, _, mhz = run(0, k, e)
+        rows.append({"waves_per_simd": 1, "mfma_wave": {"valu_ops_per_mfma": k, "exps_per_mfma": e,
+                                                        "cycles_per_mfma": sum(cyc) / len(cyc) / (2 * iters)},
+                     "MHz": mhz})
+    for e in (0, 1):
+        ops = 4 if e else 12
+        kind = "v_exp_f32" if e else "v_fma_f32"
+        for role, what in ((2, "MFMA wave alone"), (3, "VALU wave alone"), (1, "MFMA wave beside a VALU wave"),
+                           (4, "two VALU waves")):
+            cyc, waves, mhz = run(role, 0, e)
+            mf = [c for c, w in zip(cyc, waves) if role != 4 and w % 8 < 4]
+            va = [c for c, w in zip(cyc, waves) if role == 4 or w % 8 >= 4]
+            row = {"waves_per_simd": 2, "case": what, "valu_op": kind, "MHz": mhz}
+            if mf:
+                row["cycles_per_mfma"] = sum(mf) / len(mf) / (2 * iters)
+            if va:
+                row["cycles_per_valu_op_per_wave"] = sum(va) / len(va) / (iters * ops)
+            rows.append(row)
+    print(json.dumps({"probe": "issue", "device_cus": cus, "iters": iters, "rows": rows}), flush=True)
+    return 0
+
+
 def measured_ceilings(dev, stream):
     """B_max from the library's streaming copy probe (2 GiB each way, far beyond the last-level
     cache) and the bf16 matrix-core ceiling from its MFMA probe (two workgroups of four waves
@@ -322,6 +363,8 @@ def main() -> int:
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the copy and MFMA probes (e.g. under a counter profiler)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="how one SIMD shares MFMA and vector-ALU issue (fa_probe_issue); prints one JSON line")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the gradients of the workload")
     ap.add_argument("--tile-sweep", action="store_true",
@@ -336,6 +379,8 @@ def main() -> int:
 
     import torch
 
+    if args.issue_probe:
+        return issue_probe()
     if args.copy_probe:
         copy_probe(args.steps)
         return 0

@@ -19,7 +19,7 @@ __all__ = [
     "FaPlanInfo", "EXPORTED", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "FaBwdStrides",
     "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size", "fa_plan_describe_qk", "fa_fwd_qk_noalloc",
     "fa_probe_copy", "fa_probe_mfma", "fa_probe_mfma_flops", "fa_probe_timer_arm", "fa_probe_timer_read",
-    "FA_PROBE_TIMER_MAX",
+    "FA_PROBE_TIMER_MAX", "fa_probe_issue",
 ]
 
 FA_OK = 0
@@ -39,7 +39,7 @@ EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
             "fa_version", "fa_shutdown", "fa_plan_describe", "fa_bwd", "fa_bwd_ex",
             "fa_bwd_workspace_size", "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size",
             "fa_plan_describe_qk", "fa_fwd_qk_noalloc", "fa_probe_copy", "fa_probe_mfma",
-            "fa_probe_mfma_flops", "fa_probe_timer_arm", "fa_probe_timer_read")
+            "fa_probe_mfma_flops", "fa_probe_timer_arm", "fa_probe_timer_read", "fa_probe_issue")
 FA_PROBE_TIMER_MAX = 4096
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -135,6 +135,8 @@ def lib():
     L.fa_probe_timer_arm.restype = ctypes.c_int
     L.fa_probe_timer_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int]
     L.fa_probe_timer_read.restype = ctypes.c_int
+    L.fa_probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    L.fa_probe_issue.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -467,3 +469,19 @@ def fa_probe_timer_read(n):
     buf = (ctypes.c_float * max(int(n), 1))()
     _check(lib().fa_probe_timer_read(buf, int(n)))
     return [float(buf[i]) for i in range(int(n))]
+
+
+def fa_probe_issue(role, valu_ops, exps, blocks, iters, stream=None):
+    """The issue probe (include/fa_probe.h): returns per-wave (shader cycles, 100 MHz
+    ticks) of the waves that worked, as two lists, after the launch completes."""
+    import torch
+
+    waves = blocks * (4 if role == 0 else 8)
+    dev = torch.device("cuda", torch.cuda.current_device())
+    out = torch.empty(waves * 64, dtype=torch.float32, device=dev)
+    ticks = torch.zeros(2 * waves, dtype=torch.int64, device=dev)
+    _check(lib().fa_probe_issue(int(role), int(valu_ops), int(exps), int(blocks), int(iters), _ptr(out),
+                                _ptr(ticks), _stream_handle(stream, dev)))
+    torch.cuda.synchronize(dev)
+    t = ticks.view(-1, 2).cpu().tolist()
+    return [a for a, b in t if a > 0], [b for a, b in t if a > 0], [w for w, (a, b) in enumerate(t) if a > 0]

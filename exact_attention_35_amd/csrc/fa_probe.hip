@@ -47,6 +47,89 @@ __global__ __launch_bounds__(256) void copy_probe(const fa::u32x4* __restrict__ 
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Issue probe: how the matrix core and the vector ALU of one SIMD share a wave's and two
+// waves' instruction streams. MFMA waves run two alternating accumulator chains of
+// v_mfma_f32_32x32x16_bf16 and, after each MFMA, K independent v_fma_f32 and E independent
+// v_exp_f32 (written in asm so the compiler keeps exactly these); VALU waves run steps of
+// 12 independent v_fma_f32 (or 4 v_exp_f32 with E > 0). Each wave times its loop with
+// s_memtime (the shader clock) and s_memrealtime (100 MHz, to convert).
+// ROLE 0: every wave of a 4-wave block (one per SIMD) is an MFMA wave; ROLE 1: 8-wave
+// blocks, waves 0-3 MFMA and 4-7 VALU (waves w and w + 4 share a SIMD); ROLE 2: the same
+// blocks with only the MFMA waves working; ROLE 3: only the VALU waves; ROLE 4: all eight
+// are VALU waves (two per SIMD).
+template <int ROLE, int K, int E>
+__global__ __launch_bounds__(512) void issue_probe(float* __restrict__ out, long long* __restrict__ ticks,
+                                                   int iters) {
+  using fa::bf16x8;
+  using fa::floatx16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool mfma_wave = ROLE == 0 || ((ROLE == 1 || ROLE == 2) && wave < 4);
+  const bool valu_wave = (ROLE == 1 || ROLE == 3) ? wave >= 4 : ROLE == 4;
+  float acc = 0.f;
+  long long t = 0, r = 0;
+  if (mfma_wave) {
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = (__bf16)(0.001f * (float)(lane + e));
+      b[e] = (__bf16)(0.002f * (float)(lane - e));
+    }
+    floatx16 c0 = {}, c1 = {};
+    float x[K > 0 ? K : 1], y[E > 0 ? E : 1];
+#pragma unroll
+    for (int i = 0; i < (K > 0 ? K : 1); ++i) x[i] = 1.0f + 1e-3f * (float)(lane + i);
+#pragma unroll
+    for (int i = 0; i < (E > 0 ? E : 1); ++i) y[i] = -1.0f - 1e-3f * (float)(lane + i);
+    const float m = 0.999f, sm = 1e-6f;
+    const long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+      c0 = fa::mfma32(a, b, c0);
+#pragma unroll
+      for (int k = 0; k < K; ++k) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[k]) : "v"(m), "v"(sm));
+#pragma unroll
+      for (int e = 0; e < E; ++e) asm volatile("v_exp_f32 %0, %0" : "+v"(y[e]));
+      c1 = fa::mfma32(b, a, c1);
+#pragma unroll
+      for (int k = 0; k < K; ++k) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[k]) : "v"(m), "v"(sm));
+#pragma unroll
+      for (int e = 0; e < E; ++e) asm volatile("v_exp_f32 %0, %0" : "+v"(y[e]));
+    }
+    t = __builtin_amdgcn_s_memtime() - t0;
+    r = __builtin_amdgcn_s_memrealtime() - r0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc += c0[q] + c1[q];
+#pragma unroll
+    for (int i = 0; i < (K > 0 ? K : 1); ++i) acc += x[i];
+#pragma unroll
+    for (int i = 0; i < (E > 0 ? E : 1); ++i) acc += y[i];
+  } else if (valu_wave) {
+    float x[12];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) x[i] = (E > 0 ? -1.0f : 1.0f) + 1e-3f * (float)(lane + i);
+    const float m = 0.999f, sm = 1e-6f;
+    const long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+      if constexpr (E > 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) asm volatile("v_exp_f32 %0, %0" : "+v"(x[k]));
+      } else {
+#pragma unroll
+        for (int k = 0; k < 12; ++k) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[k]) : "v"(m), "v"(sm));
+      }
+    }
+    t = __builtin_amdgcn_s_memtime() - t0;
+    r = __builtin_amdgcn_s_memrealtime() - r0;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) acc += x[i];
+  }
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  out[gid] = acc;
+  if (lane == 0) {
+    ticks[2 * (gid / 64)] = t;
+    ticks[2 * (gid / 64) + 1] = r;
+  }
+}
+
 // Each wave runs `iters` rounds of four independent 32x32x16 bf16 MFMA chains on
 // register operands and stores its accumulators once (so the chains are not removed).
 __global__ __launch_bounds__(256, 2) void mfma_probe(float* __restrict__ out, int iters) {
@@ -148,6 +231,42 @@ int fa_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
 int fa_probe_mfma(float* out, int blocks, int iters, void* stream) {
   if (!out || blocks <= 0 || iters <= 0) return FA_ERR_NULL;
   hipLaunchKernelGGL(mfma_probe, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), out, iters);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_probe_issue(int role, int valu_ops, int exps, int blocks, int iters, float* out, long long* ticks,
+                   void* stream) {
+  if (!out || !ticks || blocks <= 0 || iters <= 0 || role < 0 || role > 4) return FA_ERR_NULL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(blocks), block(role == 0 ? 256 : 512);
+#define FA_ISSUE(R, K, E) hipLaunchKernelGGL((issue_probe<R, K, E>), grid, block, 0, st, out, ticks, iters)
+  if (role == 0) {
+    const int key = valu_ops * 8 + exps;
+    switch (key) {
+      case 0 * 8 + 0: FA_ISSUE(0, 0, 0); break;
+      case 2 * 8 + 0: FA_ISSUE(0, 2, 0); break;
+      case 4 * 8 + 0: FA_ISSUE(0, 4, 0); break;
+      case 6 * 8 + 0: FA_ISSUE(0, 6, 0); break;
+      case 8 * 8 + 0: FA_ISSUE(0, 8, 0); break;
+      case 12 * 8 + 0: FA_ISSUE(0, 12, 0); break;
+      case 0 * 8 + 1: FA_ISSUE(0, 0, 1); break;
+      case 0 * 8 + 2: FA_ISSUE(0, 0, 2); break;
+      case 0 * 8 + 4: FA_ISSUE(0, 0, 4); break;
+      case 4 * 8 + 1: FA_ISSUE(0, 4, 1); break;
+      case 4 * 8 + 2: FA_ISSUE(0, 4, 2); break;
+      default: return FA_ERR_SHAPE;
+    }
+  } else {
+    if (valu_ops != 0) return FA_ERR_SHAPE;
+    const bool e = exps > 0;
+    switch (role) {
+      case 1: if (e) FA_ISSUE(1, 0, 1); else FA_ISSUE(1, 0, 0); break;
+      case 2: if (e) FA_ISSUE(2, 0, 1); else FA_ISSUE(2, 0, 0); break;
+      case 3: if (e) FA_ISSUE(3, 0, 1); else FA_ISSUE(3, 0, 0); break;
+      default: if (e) FA_ISSUE(4, 0, 1); else FA_ISSUE(4, 0, 0); break;
+    }
+  }
+#undef FA_ISSUE
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -43,6 +43,27 @@ int fa_probe_mfma(float* out, int blocks, int iters, void* stream);
 /* The FLOPs one fa_probe_mfma launch performs: blocks * 4 waves * iters * 4 * 32768. */
 double fa_probe_mfma_flops(int blocks, int iters);
 
+/*
+ * fa_probe_issue — how one SIMD's matrix core and vector ALU share instruction streams
+ * (the steady state of the attention kernels interleaves MFMAs with the softmax's vector
+ * work). Launches `blocks` workgroups; each "MFMA wave" runs `iters` rounds of two
+ * alternating accumulator chains of v_mfma_f32_32x32x16_bf16 with `valu_ops` independent
+ * v_fma_f32 and `exps` independent v_exp_f32 after each MFMA; each "VALU wave" runs
+ * `iters` steps of 12 independent v_fma_f32 (or 4 v_exp_f32 when exps > 0).
+ *   role 0: 4-wave workgroups (one wave per SIMD), all MFMA waves; valu_ops in
+ *           {0, 2, 4, 6, 8, 12} with exps 0, or valu_ops 0 with exps in {1, 2, 4}, or
+ *           valu_ops 4 with exps in {1, 2};
+ *   role 1: 8-wave workgroups (waves w and w + 4 share a SIMD), waves 0-3 MFMA, 4-7 VALU;
+ *   role 2: the same workgroups, only waves 0-3 working; role 3: only waves 4-7 working;
+ *   role 4: all eight waves VALU waves (two per SIMD); valu_ops must be 0 for roles 1-4.
+ * Writes blocks * threads floats to out and, per wave i, ticks[2i] = s_memtime cycles (the
+ * shader clock) and ticks[2i+1] = s_memrealtime ticks (100 MHz) of its loop, 0 for idle
+ * waves (device memory, caller-owned, 2 * blocks * 8 entries). Returns FA_OK, FA_ERR_NULL,
+ * FA_ERR_SHAPE for an unsupported (valu_ops, exps) or FA_ERR_LAUNCH.
+ */
+int fa_probe_issue(int role, int valu_ops, int exps, int blocks, int iters, float* out, long long* ticks,
+                   void* stream);
+
 /* Most launches one fa_probe_timer_arm call can arm. */
 #define FA_PROBE_TIMER_MAX 4096
 
