@@ -7,6 +7,8 @@ device would be read or written out of bounds. These checks run without a GPU: s
 and dtype mismatches are found first, then host tensors are refused.
 """
 
+import ctypes
+
 import pytest
 import torch
 
@@ -100,3 +102,15 @@ def test_launch_timer_arguments_are_checked():
     assert capi.fa_probe_timer_read(0) == []
     with pytest.raises(capi.FaError):
         capi.fa_probe_timer_read(1)      # nothing was armed and launched
+
+
+def test_issue_probe_arguments_are_checked():
+    # refused before any launch: null buffers, roles outside 0..4, unsupported op counts
+    L = capi.lib()
+    assert L.fa_probe_issue(0, 0, 0, 1, 1, None, None, None) == capi.STATUS["FA_ERR_NULL"]
+    buf = ctypes.c_void_p(16)  # never dereferenced: every call below fails its checks first
+    assert L.fa_probe_issue(5, 0, 0, 1, 1, buf, buf, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_issue(-1, 0, 0, 1, 1, buf, buf, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_issue(0, 0, 0, 0, 1, buf, buf, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_issue(0, 3, 0, 1, 1, buf, buf, None) == capi.STATUS["FA_ERR_SHAPE"]
+    assert L.fa_probe_issue(1, 4, 0, 1, 1, buf, buf, None) == capi.STATUS["FA_ERR_SHAPE"]

@@ -92,3 +92,19 @@ def test_launch_timer_count_mismatch_is_an_error(gpu_device):
     with pytest.raises(capi.FaError):
         capi.fa_probe_timer_read(3)      # only two of the three armed launches happened
     assert len(capi.fa_probe_timer_read(2)) == 2
+
+
+def test_issue_probe_times_every_working_wave(gpu_device):
+    # one MFMA wave per SIMD: 64 workgroups of 4 waves, every wave times its loop; a
+    # 32x32x16 MFMA holds the matrix core at least 32 shader cycles
+    cyc, rt, waves = capi.fa_probe_issue(0, 2, 0, 64, 500)
+    assert len(cyc) == 64 * 4 and all(r > 0 for r in rt)
+    per_mfma = sum(cyc) / len(cyc) / (2 * 500)
+    assert 30.0 <= per_mfma < 200.0, per_mfma
+    # roles with idle halves: only the working waves report
+    cyc, rt, waves = capi.fa_probe_issue(2, 0, 0, 64, 200)
+    assert len(cyc) == 64 * 4 and all(w % 8 < 4 for w in waves)
+    cyc, rt, waves = capi.fa_probe_issue(3, 0, 1, 64, 200)
+    assert len(cyc) == 64 * 4 and all(w % 8 >= 4 for w in waves)
+    cyc, rt, waves = capi.fa_probe_issue(1, 0, 0, 64, 200)
+    assert len(cyc) == 64 * 8
