@@ -214,8 +214,9 @@ def issue_probe():
 
 def measured_ceilings(dev, stream):
     """B_max from the library's streaming copy probe (2 GiB each way, far beyond the last-level
-    cache) and the bf16 matrix-core ceiling from its MFMA probe (two workgroups of four waves
-    per compute unit, as the attention kernel runs), each the median over 20 launches."""
+    cache) and from its read-only probe (the same 2 GiB read), and the bf16 matrix-core
+    ceiling from its MFMA probe (two workgroups of four waves per compute unit, as the
+    attention kernel runs), each the median over 20 launches."""
     import torch
 
     from exact_attention_35_amd import capi
@@ -227,14 +228,20 @@ def measured_ceilings(dev, stream):
         capi.fa_probe_copy(src, dst, stream)
     t = launch_stats(lambda: capi.fa_probe_copy(src, dst, stream), stream, 20)
     bw = 2.0 * n / float(t[len(t) // 2])
-    del src, dst
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(16 * cus, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        capi.fa_probe_read(src, sink, stream)
+    t = launch_stats(lambda: capi.fa_probe_read(src, sink, stream), stream, 20)
+    rbw = n / float(t[len(t) // 2])
+    del src, dst
     blocks, iters = 2 * cus, 4000
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     flops = capi.fa_probe_mfma(out, blocks, iters, stream)
     t = launch_stats(lambda: capi.fa_probe_mfma(out, blocks, iters, stream), stream, 20)
-    return {"hbm_GBps": bw / 1e9, "mfma_bf16_TFLOPs": flops / float(t[len(t) // 2]) / 1e12,
-            "copy_probe_bytes": 2 * n, "mfma_probe": f"{blocks} workgroups x 4 waves x {iters} x 4 MFMA 32x32x16"}
+    return {"hbm_GBps": bw / 1e9, "hbm_read_GBps": rbw / 1e9, "mfma_bf16_TFLOPs": flops / float(t[len(t) // 2]) / 1e12,
+            "copy_probe_bytes": 2 * n, "read_probe_bytes": n,
+            "mfma_probe": f"{blocks} workgroups x 4 waves x {iters} x 4 MFMA 32x32x16"}
 
 
 def cpu_host_info():
@@ -481,11 +488,18 @@ def main() -> int:
                  "cold_achieved": rate(med_c), "cold_frac": rate(med_c) / roof["peak"]})
     # the attainable rate on the measured ceilings, min(P_max, B_max * I) with I = FLOPs per
     # minimum byte (matrix-core kernels: P_max from the MFMA probe, B_max from the copy probe)
+    # (B_max: the read-only probe's bandwidth for kernels whose minimum bytes are at least 90%
+    # reads, as a decoding step and the bias stream are; else the copy probe's)
     if mfma and ceil["mfma_bf16_TFLOPs"] and ceil["hbm_GBps"]:
         p_max = ceil["mfma_bf16_TFLOPs"]
-        b_i = ceil["hbm_GBps"] * 1e9 * (flops / min_b) / 1e12
+        writes = w.B * w.H * w.n_q * (w.dv * elem + 4)
+        reads_share = 1.0 - writes / min_b
+        b_src = "read probe" if reads_share >= 0.9 and ceil.get("hbm_read_GBps") else "copy probe"
+        b_max = ceil["hbm_read_GBps"] if b_src == "read probe" else ceil["hbm_GBps"]
+        b_i = b_max * 1e9 * (flops / min_b) / 1e12
         attain = min(p_max, b_i)
-        roof["measured_roofline"] = {"P_max_TFLOPs": p_max, "B_max_x_I_TFLOPs": b_i,
+        roof["measured_roofline"] = {"P_max_TFLOPs": p_max, "B_max_GBps": b_max, "B_max_source": b_src,
+                                     "read_share_of_min_bytes": reads_share, "B_max_x_I_TFLOPs": b_i,
                                      "intensity_flop_per_byte": flops / min_b, "attainable_TFLOPs": attain,
                                      "achieved_TFLOPs": flops / avg / 1e12, "frac": flops / avg / 1e12 / attain,
                                      "bound": "mfma" if p_max <= b_i else "hbm"}

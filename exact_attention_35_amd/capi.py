@@ -19,7 +19,7 @@ __all__ = [
     "FaPlanInfo", "EXPORTED", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "FaBwdStrides",
     "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size", "fa_plan_describe_qk", "fa_fwd_qk_noalloc",
     "fa_probe_copy", "fa_probe_mfma", "fa_probe_mfma_flops", "fa_probe_timer_arm", "fa_probe_timer_read",
-    "FA_PROBE_TIMER_MAX", "fa_probe_issue",
+    "FA_PROBE_TIMER_MAX", "fa_probe_issue", "fa_probe_read",
 ]
 
 FA_OK = 0
@@ -39,7 +39,8 @@ EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
             "fa_version", "fa_shutdown", "fa_plan_describe", "fa_bwd", "fa_bwd_ex",
             "fa_bwd_workspace_size", "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size",
             "fa_plan_describe_qk", "fa_fwd_qk_noalloc", "fa_probe_copy", "fa_probe_mfma",
-            "fa_probe_mfma_flops", "fa_probe_timer_arm", "fa_probe_timer_read", "fa_probe_issue")
+            "fa_probe_mfma_flops", "fa_probe_timer_arm", "fa_probe_timer_read", "fa_probe_issue",
+            "fa_probe_read")
 FA_PROBE_TIMER_MAX = 4096
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -137,6 +138,8 @@ def lib():
     L.fa_probe_timer_read.restype = ctypes.c_int
     L.fa_probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     L.fa_probe_issue.restype = ctypes.c_int
+    L.fa_probe_read.argtypes = [vp, i64, vp, ctypes.c_int, vp]
+    L.fa_probe_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -485,3 +488,15 @@ def fa_probe_issue(role, valu_ops, exps, blocks, iters, stream=None):
     torch.cuda.synchronize(dev)
     t = ticks.view(-1, 2).cpu().tolist()
     return [a for a, b in t if a > 0], [b for a, b in t if a > 0], [w for w, (a, b) in enumerate(t) if a > 0]
+
+
+def fa_probe_read(src, sink, stream=None):
+    """The read-only streaming probe over a device tensor; sink: int32 device tensor with
+    at least 16 * CU-count elements."""
+    import torch
+
+    if sink.dtype != torch.int32:
+        raise FaError(STATUS["FA_ERR_SHAPE"], "sink must be int32")
+    _same_device((("src", src), ("sink", sink)))
+    nbytes = src.numel() * src.element_size()
+    _check(lib().fa_probe_read(_ptr(src), nbytes, _ptr(sink), int(sink.numel()), _stream_handle(stream, src.device)))

@@ -47,6 +47,26 @@ __global__ __launch_bounds__(256) void copy_probe(const fa::u32x4* __restrict__ 
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Each thread keeps four 16-byte loads in flight and folds them into one word, which each
+// workgroup stores once (so the loads are not removed): a read-only stream.
+__global__ __launch_bounds__(256) void read_probe(const fa::u32x4* __restrict__ src, int64_t n16,
+                                                  unsigned* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  fa::u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const fa::u32x4 a = __builtin_nontemporal_load(src + i);
+    const fa::u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const fa::u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const fa::u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= src[i];
+  const unsigned w = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  const unsigned any = (unsigned)__builtin_amdgcn_ballot_w64(w != 0u);  // one word per block
+  if (threadIdx.x == 0) sink[blockIdx.x] = any;
+}
+
 // Issue probe: how the matrix core and the vector ALU of one SIMD share a wave's and two
 // waves' instruction streams. MFMA waves run two alternating accumulator chains of
 // v_mfma_f32_32x32x16_bf16 and, after each MFMA, K independent v_fma_f32 and E independent
@@ -225,6 +245,21 @@ int fa_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   const int grid = (int)(want < (int64_t)cus * 16 ? want : (int64_t)cus * 16);
   hipLaunchKernelGGL(copy_probe, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const fa::u32x4*>(src), static_cast<fa::u32x4*>(dst), n16);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_probe_read(const void* src, int64_t bytes, unsigned* sink, int sink_words, void* stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 16 != 0 || (uintptr_t)src % 16 != 0) return FA_ERR_NULL;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return FA_ERR_DEVICE;
+  const int64_t n16 = bytes / 16;
+  const int64_t want = (n16 + 255) / 256;
+  const int grid = (int)(want < (int64_t)cus * 16 ? want : (int64_t)cus * 16);
+  if (sink_words < grid) return FA_ERR_SHAPE;
+  hipLaunchKernelGGL(read_probe, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const fa::u32x4*>(src), n16, sink);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

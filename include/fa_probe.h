@@ -30,6 +30,17 @@ extern "C" {
 int fa_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /*
+ * fa_probe_read — reads `bytes` bytes at src (device memory, 16-byte aligned, bytes a
+ * positive multiple of 16) with 16-byte loads, four in flight per lane, and writes one word
+ * per workgroup to sink (device memory, caller-owned, sink_words >= the grid: at most
+ * 16 * the CU count). With a buffer far larger than the last-level cache, bytes / time is
+ * the HBM read bandwidth, the B_max of kernels that mostly read (a decoding step, a bias
+ * stream). Returns FA_OK, FA_ERR_NULL, FA_ERR_SHAPE (sink too small), FA_ERR_DEVICE or
+ * FA_ERR_LAUNCH.
+ */
+int fa_probe_read(const void* src, int64_t bytes, unsigned* sink, int sink_words, void* stream);
+
+/*
  * fa_probe_mfma — `blocks` workgroups of four waves, each wave running `iters` rounds of
  * four independent v_mfma_f32_32x32x16_bf16 chains on register operands (two
  * workgroups per compute unit fit, as in the attention kernel); writes blocks * 256

@@ -114,3 +114,12 @@ def test_issue_probe_arguments_are_checked():
     assert L.fa_probe_issue(0, 0, 0, 0, 1, buf, buf, None) == capi.STATUS["FA_ERR_NULL"]
     assert L.fa_probe_issue(0, 3, 0, 1, 1, buf, buf, None) == capi.STATUS["FA_ERR_SHAPE"]
     assert L.fa_probe_issue(1, 4, 0, 1, 1, buf, buf, None) == capi.STATUS["FA_ERR_SHAPE"]
+
+
+def test_read_probe_arguments_are_checked():
+    L = capi.lib()
+    buf = ctypes.c_void_p(16)
+    assert L.fa_probe_read(None, 16, buf, 1, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_read(buf, 16, None, 1, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_read(buf, 24, buf, 1, None) == capi.STATUS["FA_ERR_NULL"]   # not a multiple of 16
+    assert L.fa_probe_read(ctypes.c_void_p(8), 16, buf, 1, None) == capi.STATUS["FA_ERR_NULL"]  # misaligned
