@@ -108,3 +108,18 @@ def test_issue_probe_times_every_working_wave(gpu_device):
     assert len(cyc) == 64 * 4 and all(w % 8 >= 4 for w in waves)
     cyc, rt, waves = capi.fa_probe_issue(1, 0, 0, 64, 200)
     assert len(cyc) == 64 * 8
+
+
+def test_read_probe_reads_and_checks_its_sink(gpu_device):
+    import torch
+
+    cus = torch.cuda.get_device_properties(gpu_device).multi_processor_count
+    src = torch.arange(1 << 22, dtype=torch.int32, device=gpu_device)   # 16 MiB, nonzero words
+    sink = torch.full((16 * cus,), -1, dtype=torch.int32, device=gpu_device)
+    capi.fa_probe_read(src, sink)
+    torch.cuda.synchronize()
+    grid = min((src.numel() // 4 + 255) // 256, 16 * cus)
+    assert (sink[:grid] != -1).all()        # every workgroup wrote its word
+    assert (sink[grid:] == -1).all()        # nothing past the grid
+    with pytest.raises(capi.FaError):
+        capi.fa_probe_read(src, sink[:1])   # a sink smaller than the grid is refused
