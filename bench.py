@@ -212,6 +212,47 @@ def issue_probe():
     return 0
 
 
+def loop_probe():
+    """The LDS probe and the tile-body probe of include/fa_probe.h on every CU, two
+    workgroups of four waves per CU as the attention kernel runs: bytes per clock per CU of
+    each LDS access kind, and shader cycles per tile for a SIMD's pair of waves running the
+    forward kernel's tile instruction mix, without and with the tile's K/V copies. A
+    launch's cycles are its duration (events around it, the second of two launches) times
+    the mean shader clock of its waves (s_memtime over s_memrealtime)."""
+    import torch
+
+    from exact_attention_35_amd import capi
+
+    dev = torch.device("cuda", torch.cuda.current_device())
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * cus
+
+    def cycles(res):
+        cyc, rt, ms = res
+        mhz = 100.0 * sum(cyc) / max(sum(rt), 1)
+        return ms * 1e3 * mhz, mhz
+
+    lds = []
+    iters = 2000
+    for mode, kind, width in ((0, "ds_read_b128", 16), (1, "ds_read_b64", 8), (2, "ds_read_b64_tr_b16", 8),
+                              (3, "ds_read_b32", 4), (4, "ds_write_b128", 16)):
+        capi.fa_probe_lds(mode, blocks, iters)
+        c, mhz = cycles(capi.fa_probe_lds(mode, blocks, iters))
+        total = blocks * 4 * iters * 8 * 64 * width
+        lds.append({"access": kind, "bytes_per_clk_per_cu": round(total / c / cus, 1), "MHz": round(mhz)})
+    src = torch.zeros(1 << 18, dtype=torch.uint8, device=dev)
+    tiles = 400
+    tile = []
+    for copies, valu in ((0, 0), (0, 117), (1, 0), (1, 117)):
+        capi.fa_probe_tile(copies, valu, blocks, tiles, src)
+        c, mhz = cycles(capi.fa_probe_tile(copies, valu, blocks, tiles, src))
+        tile.append({"copies": copies, "valu_ops": valu, "exps": 33, "cycles_per_tile_pair": round(c / tiles),
+                     "MHz": round(mhz)})
+    print(json.dumps({"probe": "loop", "device_cus": cus, "lds": lds, "tile": tile,
+                      "mfma_bound_cycles_per_tile_pair": 2 * 32 * 32}), flush=True)
+    return 0
+
+
 def measured_ceilings(dev, stream):
     """B_max from the library's streaming copy probe (2 GiB each way, far beyond the last-level
     cache) and from its read-only probe (the same 2 GiB read), and the bf16 matrix-core
@@ -372,6 +413,8 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--issue-probe", action="store_true",
                     help="how one SIMD shares MFMA and vector-ALU issue (fa_probe_issue); prints one JSON line")
+    ap.add_argument("--loop-probe", action="store_true",
+                    help="LDS throughput and the tile-body model (fa_probe_lds, fa_probe_tile); prints one JSON line")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the gradients of the workload")
     ap.add_argument("--tile-sweep", action="store_true",
@@ -388,6 +431,8 @@ def main() -> int:
 
     if args.issue_probe:
         return issue_probe()
+    if args.loop_probe:
+        return loop_probe()
     if args.copy_probe:
         copy_probe(args.steps)
         return 0

@@ -19,7 +19,7 @@ __all__ = [
     "FaPlanInfo", "EXPORTED", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "FaBwdStrides",
     "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size", "fa_plan_describe_qk", "fa_fwd_qk_noalloc",
     "fa_probe_copy", "fa_probe_mfma", "fa_probe_mfma_flops", "fa_probe_timer_arm", "fa_probe_timer_read",
-    "FA_PROBE_TIMER_MAX", "fa_probe_issue", "fa_probe_read",
+    "FA_PROBE_TIMER_MAX", "fa_probe_issue", "fa_probe_read", "fa_probe_lds", "fa_probe_tile",
 ]
 
 FA_OK = 0
@@ -40,7 +40,7 @@ EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_workspace_size", "fa_status_string",
             "fa_bwd_workspace_size", "fa_fwd_qk", "fa_fwd_qk_ex", "fa_fwd_qk_workspace_size",
             "fa_plan_describe_qk", "fa_fwd_qk_noalloc", "fa_probe_copy", "fa_probe_mfma",
             "fa_probe_mfma_flops", "fa_probe_timer_arm", "fa_probe_timer_read", "fa_probe_issue",
-            "fa_probe_read")
+            "fa_probe_read", "fa_probe_lds", "fa_probe_tile")
 FA_PROBE_TIMER_MAX = 4096
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -140,6 +140,10 @@ def lib():
     L.fa_probe_issue.restype = ctypes.c_int
     L.fa_probe_read.argtypes = [vp, i64, vp, ctypes.c_int, vp]
     L.fa_probe_read.restype = ctypes.c_int
+    L.fa_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    L.fa_probe_lds.restype = ctypes.c_int
+    L.fa_probe_tile.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp]
+    L.fa_probe_tile.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -488,6 +492,55 @@ def fa_probe_issue(role, valu_ops, exps, blocks, iters, stream=None):
     torch.cuda.synchronize(dev)
     t = ticks.view(-1, 2).cpu().tolist()
     return [a for a, b in t if a > 0], [b for a, b in t if a > 0], [w for w, (a, b) in enumerate(t) if a > 0]
+
+
+def _wave_ticks(ticks, dev):
+    import torch
+
+    torch.cuda.synchronize(dev)
+    t = ticks.view(-1, 2).cpu().tolist()
+    return [a for a, b in t], [b for a, b in t]
+
+
+def fa_probe_lds(mode, blocks, iters, stream=None):
+    """The LDS probe (include/fa_probe.h): per-wave (shader cycles, 100 MHz ticks) lists and
+    the launch's duration in ms from events recorded around it on the same stream."""
+    import torch
+
+    dev = torch.device("cuda", torch.cuda.current_device())
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    ticks = torch.zeros(2 * blocks * 4, dtype=torch.int64, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    _check(lib().fa_probe_lds(int(mode), int(blocks), int(iters), _ptr(out), _ptr(ticks), _stream_handle(st, dev)))
+    e1.record(st)
+    cyc, rt = _wave_ticks(ticks, dev)
+    return cyc, rt, e0.elapsed_time(e1)
+
+
+def fa_probe_tile(copies, valu_ops, blocks, tiles, src=None, stream=None):
+    """The tile-body probe (include/fa_probe.h): per-wave (shader cycles, 100 MHz ticks)
+    lists and the launch's duration in ms from events recorded around it on the same stream;
+    src: a device tensor of at least 256 KiB when copies = 1."""
+    import torch
+
+    dev = torch.device("cuda", torch.cuda.current_device())
+    if src is not None:
+        _same_device((("src", src),))
+        if src.device != dev:
+            raise FaError(STATUS["FA_ERR_NULL"], f"src is on {src.device}, expected {dev}")
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    nbytes = 0 if src is None else src.numel() * src.element_size()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    ticks = torch.zeros(2 * blocks * 4, dtype=torch.int64, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    _check(lib().fa_probe_tile(int(copies), int(valu_ops), int(blocks), int(tiles), _ptr(src), nbytes, _ptr(out),
+                               _ptr(ticks), _stream_handle(st, dev)))
+    e1.record(st)
+    cyc, rt = _wave_ticks(ticks, dev)
+    return cyc, rt, e0.elapsed_time(e1)
 
 
 def fa_probe_read(src, sink, stream=None):

@@ -175,6 +175,158 @@ __global__ __launch_bounds__(256, 2) void mfma_probe(float* __restrict__ out, in
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// LDS probe: every wave of 4-wave workgroups (64 KiB of LDS each, two per compute unit)
+// runs `iters` rounds of eight LDS accesses of one kind at consecutive per-lane addresses
+// (no bank conflicts) and folds what it reads into one word per thread. M: 0 ds_read_b128,
+// 1 ds_read_b64, 2 ds_read_b64_tr_b16, 3 ds_read_b32, 4 ds_write_b128 (a wait for the
+// writes ends each round). Each wave times its loop as the issue probe does.
+template <int M>
+__global__ __launch_bounds__(256, 2) void lds_probe(unsigned* __restrict__ out, long long* __restrict__ ticks,
+                                                    int iters) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[65536];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 65536 / 4; i += 256) reinterpret_cast<unsigned*>(lds)[i] = (unsigned)i * 2654435761u;
+  __syncthreads();
+  constexpr int W = M == 0 || M == 4 ? 16 : M == 3 ? 4 : 8;  // bytes per lane
+  // base < 32768; a round touches base ^ (0..240) + k * 2048 + W for k < 8: below 48 KiB
+  const int base = (wave * 8192 + lane * W) & 32767;
+  unsigned acc = 0;
+  fa::u32x4 v4 = {(unsigned)lane, (unsigned)wave, 3u, 4u};
+  const long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+    const int b = base ^ ((it & 15) << 4);
+    if constexpr (M == 0) {
+      fa::u32x4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const fa::u32x4*>(lds + b + k * 2048);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc ^= v[k][0] ^ v[k][3];
+    } else if constexpr (M == 1) {
+      fa::u32x2 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const fa::u32x2*>(lds + b + k * 2048);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc ^= v[k][0] ^ v[k][1];
+    } else if constexpr (M == 2) {
+      fa::i16x4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(fa::i16x4, lds + b + k * 2048));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc ^= __builtin_bit_cast(fa::u32x2, v[k])[0] ^ __builtin_bit_cast(fa::u32x2, v[k])[1];
+    } else if constexpr (M == 3) {
+      unsigned v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const unsigned*>(lds + b + k * 2048);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc ^= v[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) *reinterpret_cast<fa::u32x4*>(lds + b + k * 2048) = v4;
+      v4[2] += 1u;
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the round's writes are done
+    }
+  }
+  const long long t = __builtin_amdgcn_s_memtime() - t0, r = __builtin_amdgcn_s_memrealtime() - r0;
+  __syncthreads();
+  if constexpr (M == 4) acc = reinterpret_cast<const unsigned*>(lds)[threadIdx.x * 16];
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  out[gid] = acc;
+  if (lane == 0) {
+    ticks[2 * (gid / 64)] = t;
+    ticks[2 * (gid / 64) + 1] = r;
+  }
+}
+
+// Tile probe: a model of the forward kernel's steady-state tile body with the same
+// instruction mix and none of its data dependences. 4-wave workgroups (64 KiB of LDS, two
+// per compute unit); per tile and wave, 32 MFMA slots: slots 0-15 accumulate into four
+// chains (the P V half, A operand read by two ds_read_b64_tr_b16), slots 16-31 into two
+// chains restarted from zero each tile (the Q K^T half, A operand one ds_read_b128); the
+// operand reads run three slots ahead; NF independent v_fma_f32 and 33 independent
+// v_exp_f32 are spread over the slots; one workgroup barrier per tile. With CP, each
+// wave also issues the tile's K and V copies as the kernel does: after a wait for its
+// earlier copies and the barrier, eight 1 KiB LDS-DMA loads into the LDS half the reads do
+// not use, from a 256 KiB source that stays in the L2 cache.
+constexpr int kTileProbeSrcBytes = 256 * 1024;
+template <int NF, int CP>
+__global__ __launch_bounds__(256, 2) void tile_probe(const unsigned char* __restrict__ src, float* __restrict__ out,
+                                                     long long* __restrict__ ticks, int tiles) {
+  using fa::bf16x8;
+  using fa::floatx16;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[65536];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 65536 / 4; i += 256) reinterpret_cast<float*>(lds)[i] = 1e-3f * (float)(i & 255);
+  __syncthreads();
+  bf16x8 b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = (__bf16)(0.002f * (float)(lane - e));
+  floatx16 c[4] = {}, d[2] = {};
+  float x[12], y[4];
+#pragma unroll
+  for (int i = 0; i < 12; ++i) x[i] = 1.0f + 1e-3f * (float)(lane + i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = -1.0f - 1e-3f * (float)(lane + i);
+  const float m = 0.999f, sm = 1e-6f;
+  // operand reads: tb < 32768 and 16-byte aligned, slot offsets add at most 31 KiB + 512 + 16
+  const int base = (wave * 4096 + lane * 16) & 32767;
+  auto operand = [&](int tb, int s) {
+    const int off = tb + (s & 31) * 1024;
+    if (s % 32 >= 16) return *reinterpret_cast<const bf16x8*>(lds + off);
+    const fa::i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(fa::i16x4, lds + off));
+    const fa::i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(fa::i16x4, lds + off + 512));
+    const fa::bf16x4 l = __builtin_bit_cast(fa::bf16x4, lo), h = __builtin_bit_cast(fa::bf16x4, hi);
+    return bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+  };
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(src), 0, kTileProbeSrcBytes, fa::kBufferWord3);
+  const long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  bf16x8 q[4];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) q[i] = operand(base, i);
+  for (int t = 0; t < tiles; ++t) {
+    if constexpr (CP) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      // LDS destination (t mod 2) * 32 KiB + (wave * 8 + i) KiB; source offset below 256 KiB
+      unsigned char* stage = lds + 32768 * (t & 1);
+      const int so = ((blockIdx.x * 7 + t) & 7) * 32768 + wave * 8192 + lane * 16;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, stage + (wave * 8 + i) * 1024), 16, so + i * 1024, 0, 0, 0);
+    } else {
+      __syncthreads();
+    }
+    const int tb = base ^ ((t & 7) << 4);
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      q[(s + 3) & 3] = operand(tb, s + 3);
+      if (s < 16) c[s & 3] = fa::mfma32(q[s & 3], b, c[s & 3]);
+      else d[s & 1] = fa::mfma32(q[s & 3], b, s < 18 ? floatx16{} : d[s & 1]);
+#pragma unroll
+      for (int k = 0; k < NF / 32 + (s < NF % 32 ? 1 : 0); ++k)
+        asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[(s * 4 + k) % 12]) : "v"(m), "v"(sm));
+      asm volatile("v_exp_f32 %0, %0" : "+v"(y[s % 4]));
+      if (s == 0) asm volatile("v_exp_f32 %0, %0" : "+v"(y[1]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const long long t = __builtin_amdgcn_s_memtime() - t0, r = __builtin_amdgcn_s_memrealtime() - r0;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc += c[0][i] + c[1][i] + c[2][i] + c[3][i] + d[0][i] + d[1][i];
+#pragma unroll
+  for (int i = 0; i < 12; ++i) acc += x[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc += y[i] + (float)q[i][0];
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  out[gid] = acc;
+  if (lane == 0) {
+    ticks[2 * (gid / 64)] = t;
+    ticks[2 * (gid / 64) + 1] = r;
+  }
+}
+
 // The calling thread's launch timer: a grow-only pool of event pairs (created on the device
 // current when armed, kept until the process ends), how many are armed, and how many of
 // those the main-kernel launches have taken.
@@ -302,6 +454,39 @@ int fa_probe_issue(int role, int valu_ops, int exps, int blocks, int iters, floa
     }
   }
 #undef FA_ISSUE
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_probe_lds(int mode, int blocks, int iters, unsigned* out, long long* ticks, void* stream) {
+  if (!out || !ticks || blocks <= 0 || iters <= 0) return FA_ERR_NULL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(lds_probe<0>, dim3(blocks), dim3(256), 0, st, out, ticks, iters); break;
+    case 1: hipLaunchKernelGGL(lds_probe<1>, dim3(blocks), dim3(256), 0, st, out, ticks, iters); break;
+    case 2: hipLaunchKernelGGL(lds_probe<2>, dim3(blocks), dim3(256), 0, st, out, ticks, iters); break;
+    case 3: hipLaunchKernelGGL(lds_probe<3>, dim3(blocks), dim3(256), 0, st, out, ticks, iters); break;
+    case 4: hipLaunchKernelGGL(lds_probe<4>, dim3(blocks), dim3(256), 0, st, out, ticks, iters); break;
+    default: return FA_ERR_SHAPE;
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_probe_tile(int copies, int valu_ops, int blocks, int tiles, const void* src, int64_t src_bytes, float* out,
+                  long long* ticks, void* stream) {
+  if (!out || !ticks || blocks <= 0 || tiles <= 0) return FA_ERR_NULL;
+  if (copies && (!src || reinterpret_cast<uintptr_t>(src) % 16 != 0 || src_bytes < kTileProbeSrcBytes))
+    return copies && !src ? FA_ERR_NULL : FA_ERR_SHAPE;
+  if ((copies != 0 && copies != 1) || (valu_ops != 0 && valu_ops != 117)) return FA_ERR_SHAPE;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned char* g = static_cast<const unsigned char*>(src);
+  const dim3 grid(blocks), block(256);
+  if (valu_ops == 117) {
+    if (copies) hipLaunchKernelGGL((tile_probe<117, 1>), grid, block, 0, st, g, out, ticks, tiles);
+    else hipLaunchKernelGGL((tile_probe<117, 0>), grid, block, 0, st, g, out, ticks, tiles);
+  } else {
+    if (copies) hipLaunchKernelGGL((tile_probe<0, 1>), grid, block, 0, st, g, out, ticks, tiles);
+    else hipLaunchKernelGGL((tile_probe<0, 0>), grid, block, 0, st, g, out, ticks, tiles);
+  }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -75,6 +75,37 @@ double fa_probe_mfma_flops(int blocks, int iters);
 int fa_probe_issue(int role, int valu_ops, int exps, int blocks, int iters, float* out, long long* ticks,
                    void* stream);
 
+/*
+ * fa_probe_lds — LDS throughput of one access kind. `blocks` workgroups of four waves, 64 KiB
+ * of LDS each (two per compute unit); each wave runs `iters` rounds of eight accesses at
+ * consecutive per-lane addresses (free of bank conflicts). mode: 0 ds_read_b128 (16 bytes
+ * per lane), 1 ds_read_b64 (8), 2 ds_read_b64_tr_b16 (8, the transposing read of the V
+ * operand), 3 ds_read_b32 (4), 4 ds_write_b128 (16, each round ends with a wait for its
+ * writes). A wave moves iters * 8 * 64 * (bytes per lane) bytes. Writes blocks * 256 words
+ * to out and, per wave i, ticks[2i] = s_memtime cycles and ticks[2i+1] = s_memrealtime ticks
+ * (100 MHz) of its loop (device memory, caller-owned, 2 * blocks * 4 entries). Returns
+ * FA_OK, FA_ERR_NULL, FA_ERR_SHAPE (unknown mode) or FA_ERR_LAUNCH.
+ */
+int fa_probe_lds(int mode, int blocks, int iters, unsigned* out, long long* ticks, void* stream);
+
+/*
+ * fa_probe_tile — a model of the forward kernel's steady-state tile body (the loop that
+ * streams K and V tiles past a resident Q tile): its instruction mix without its data
+ * dependences. `blocks` workgroups of four waves, two per compute unit, 64 KiB of LDS
+ * each; per tile and wave, 32 MFMA slots (16 whose A operand takes two ds_read_b64_tr_b16,
+ * 16 whose A operand takes one ds_read_b128, the reads three slots ahead), valu_ops
+ * independent v_fma_f32 (0 or 117) and 33 independent v_exp_f32, and one workgroup barrier.
+ * copies = 1 adds the kernel's tile copies: per wave and tile, after a wait for its earlier
+ * copies and the barrier, eight 1 KiB LDS-DMA loads from the first 256 KiB at src (device
+ * memory, 16-byte aligned, src_bytes >= 262144; it stays in the L2 cache); copies = 0
+ * ignores src. Writes blocks * 256 floats to out and per-wave loop times to ticks as
+ * fa_probe_lds does; a wave's cycles / tiles is the cycles per tile of its SIMD's pair of
+ * waves. Returns FA_OK, FA_ERR_NULL, FA_ERR_SHAPE (copies not 0 or 1, valu_ops not 0 or
+ * 117, src too small or misaligned) or FA_ERR_LAUNCH.
+ */
+int fa_probe_tile(int copies, int valu_ops, int blocks, int tiles, const void* src, int64_t src_bytes, float* out,
+                  long long* ticks, void* stream);
+
 /* Most launches one fa_probe_timer_arm call can arm. */
 #define FA_PROBE_TIMER_MAX 4096
 

@@ -123,3 +123,28 @@ def test_read_probe_arguments_are_checked():
     assert L.fa_probe_read(buf, 16, None, 1, None) == capi.STATUS["FA_ERR_NULL"]
     assert L.fa_probe_read(buf, 24, buf, 1, None) == capi.STATUS["FA_ERR_NULL"]   # not a multiple of 16
     assert L.fa_probe_read(ctypes.c_void_p(8), 16, buf, 1, None) == capi.STATUS["FA_ERR_NULL"]  # misaligned
+
+
+def test_lds_probe_arguments_are_checked():
+    # refused before any launch: null buffers, empty grids or loops, unknown access kinds
+    L = capi.lib()
+    buf = ctypes.c_void_p(16)  # never dereferenced: every call below fails its checks first
+    assert L.fa_probe_lds(0, 1, 1, None, buf, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_lds(0, 1, 1, buf, None, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_lds(0, 0, 1, buf, buf, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_lds(0, 1, 0, buf, buf, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_lds(5, 1, 1, buf, buf, None) == capi.STATUS["FA_ERR_SHAPE"]
+    assert L.fa_probe_lds(-1, 1, 1, buf, buf, None) == capi.STATUS["FA_ERR_SHAPE"]
+
+
+def test_tile_probe_arguments_are_checked():
+    L = capi.lib()
+    buf = ctypes.c_void_p(256)  # never dereferenced: every call below fails its checks first
+    big = 1 << 18
+    assert L.fa_probe_tile(0, 117, 1, 1, None, 0, None, buf, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_tile(0, 117, 1, 0, None, 0, buf, buf, None) == capi.STATUS["FA_ERR_NULL"]
+    assert L.fa_probe_tile(1, 117, 1, 1, None, big, buf, buf, None) == capi.STATUS["FA_ERR_NULL"]   # copies need src
+    assert L.fa_probe_tile(1, 117, 1, 1, buf, big - 16, buf, buf, None) == capi.STATUS["FA_ERR_SHAPE"]  # too small
+    assert L.fa_probe_tile(1, 117, 1, 1, ctypes.c_void_p(264), big, buf, buf, None) == capi.STATUS["FA_ERR_SHAPE"]
+    assert L.fa_probe_tile(2, 117, 1, 1, buf, big, buf, buf, None) == capi.STATUS["FA_ERR_SHAPE"]
+    assert L.fa_probe_tile(0, 100, 1, 1, None, 0, buf, buf, None) == capi.STATUS["FA_ERR_SHAPE"]

@@ -1,7 +1,7 @@
 """The measurement probes of include/fa_probe.h on the GPU: the streaming copy copies, the
-matrix-core probe reports its FLOP count, and the launch timer stamps each armed main-kernel
+matrix-core probe reports its FLOP count, the launch timer stamps each armed main-kernel
 launch with an interval that lies inside the launch's own event bracket, without changing
-what the launch computes.
+what the launch computes, and the LDS and tile-body probes time every wave.
 """
 
 import numpy as np
@@ -123,3 +123,33 @@ def test_read_probe_reads_and_checks_its_sink(gpu_device):
     assert (sink[grid:] == -1).all()        # nothing past the grid
     with pytest.raises(capi.FaError):
         capi.fa_probe_read(src, sink[:1])   # a sink smaller than the grid is refused
+
+
+def test_lds_probe_times_every_wave(gpu_device):
+    import torch
+
+    cus = torch.cuda.get_device_properties(gpu_device).multi_processor_count
+    for mode in range(5):
+        cyc, rt, ms = capi.fa_probe_lds(mode, 2 * cus, 50)
+        assert len(cyc) == 2 * cus * 4 and all(c > 0 for c in cyc) and all(r > 0 for r in rt) and ms > 0
+        # eight waves per CU move 8 * 50 * 8 * 64 * width bytes; no LDS serves 1 KiB per clock
+        width = (16, 8, 8, 4, 16)[mode]
+        rate = 8 * 50 * 8 * 64 * width / (sum(cyc) / len(cyc))
+        assert 0 < rate < 1024, (mode, rate)
+
+
+def test_tile_probe_times_every_wave(gpu_device):
+    import torch
+
+    cus = torch.cuda.get_device_properties(gpu_device).multi_processor_count
+    src = torch.zeros(1 << 18, dtype=torch.uint8, device=gpu_device)
+    for copies in (0, 1):
+        cyc, rt, ms = capi.fa_probe_tile(copies, 117, 2 * cus, 20, src)
+        assert len(cyc) == 2 * cus * 4 and all(r > 0 for r in rt)
+        # a SIMD's two waves issue 64 MFMAs per tile pair, 32 cycles each at least: the
+        # launch lasts at least that long at the waves' clock
+        mhz = 100.0 * sum(cyc) / sum(rt)
+        per_pair = ms * 1e3 * mhz / 20
+        assert 2048 <= per_pair < 20000, (copies, per_pair)
+    with pytest.raises(capi.FaError):
+        capi.fa_probe_tile(1, 117, 1, 1, src[:1024])   # the copy source must hold 256 KiB
