@@ -510,7 +510,8 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
     // dS of the tile; tiles that cross the diagonal or the sequence end mask keys
     auto dscores = [&](auto MASKc) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        float ds_even = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, mcs));
@@ -518,8 +519,13 @@ __device__ void dq_block(const BwdParams& p, int blk, unsigned char* st0, unsign
             const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
             if (key >= N || (p.causal && key > qi)) pr = 0.f;
           }
-          dsk[kb * 2 + (r >> 3)][r & 7] = (E)(pr * (dpacc[kb][r] + ndrow));
+          const float ds = pr * (dpacc[kb][r] + ndrow);
+          if (r & 1)  // elements r - 1 and r as one packed word
+            set_pair(dsk[kb * 2 + (r >> 3)], (r & 7) >> 1, cvt_pk<E>(ds_even, ds));
+          else
+            ds_even = ds;
         }
+      }
     };
     if (kv0 + C::KS > N || (p.causal && kv0 + C::KS - 1 > wq0))
       dscores(std::true_type{});

@@ -589,8 +589,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma(Params p) {
         st.ps[f & 3] += st.pf[f];
         if constexpr (f & 1) {
           constexpr int r = f % 16;
-          pk[(f / 16) * 2 + r / 8][r % 8 - 1] = (E)st.pf[f - 1];
-          pk[(f / 16) * 2 + r / 8][r % 8] = (E)st.pf[f];
+          set_pair(pk[(f / 16) * 2 + r / 8], (r % 8) / 2, cvt_pk<E>(st.pf[f - 1], st.pf[f]));
         }
       }
     } else {

@@ -40,6 +40,33 @@ __device__ __forceinline__ floatx16 mfma32(halfx8 a, halfx8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Two fp32 values rounded to the nearest 16-bit float (ties to even), packed with the first
+// in the low half. Written as asm so that each conversion is issued where the code places
+// it: as plain conversions the compiler sinks all of a tile's conversions next to the first
+// use of the packed vectors, which keeps every fp32 value live until then (the forward
+// kernel with a bias and d = dv = 128 then spilled 91 registers).
+template <typename E>
+__device__ __forceinline__ unsigned cvt_pk(float a, float b);
+template <>
+__device__ __forceinline__ unsigned cvt_pk<__bf16>(float a, float b) {
+  unsigned r;
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+template <>
+__device__ __forceinline__ unsigned cvt_pk<_Float16>(float a, float b) {
+  unsigned r;
+  asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// Elements 2j and 2j+1 of an 8-element 16-bit vector set from a packed word.
+template <typename V8>
+__device__ __forceinline__ void set_pair(V8& v, int j, unsigned w) {
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+  u[j] = w;
+  v = __builtin_bit_cast(V8, u);
+}
+
 // Compile-time loop: f(integral_constant<int, I>) for I = I0 .. N-1.
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
