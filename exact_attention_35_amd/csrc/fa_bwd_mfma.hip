@@ -170,6 +170,8 @@ __global__ __launch_bounds__(256) void bwd_rowstat(BwdParams p) {
   const int bh = row / Np, i = row % Np;
   const int b = bh / p.H, h = bh % p.H;
   float acc = 0.f;
+  // the row's lse is loaded with O and dO (one memory round trip, not two)
+  const float lse = part == 0 && i < p.N ? p.lse[b * p.l_sb + h * p.l_sh + i] : 0.f;
   if (i < p.N) {
     const E* o = static_cast<const E*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_sn + part * EL;
     const E* g = static_cast<const E*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)i * p.do_sn + part * EL;
@@ -185,10 +187,7 @@ __global__ __launch_bounds__(256) void bwd_rowstat(BwdParams p) {
     // -lse * sqrt(d): the start value of a score accumulator, so that it ends holding
     // sqrt(d) * (S_ij - lse_i) without C; -inf where no probability may arise
     float m = -INFINITY;
-    if (i < p.N) {
-      const float l = p.lse[b * p.l_sb + h * p.l_sh + i];
-      m = l == -INFINITY ? -INFINITY : -l * p.sqrt_d;
-    }
+    if (i < p.N) m = lse == -INFINITY ? -INFINITY : -lse * p.sqrt_d;
     float* grp = p.rowstat + ((int64_t)bh * p.n_grp + i / 64) * 128;
     grp[i % 64] = m;
     grp[64 + i % 64] = i < p.N ? -acc : 0.f;  // -D: the start value of a dP accumulator
