@@ -485,10 +485,12 @@ def fa_probe_issue(role, valu_ops, exps, blocks, iters, stream=None):
 
     waves = blocks * (4 if role == 0 else 8)
     dev = torch.device("cuda", torch.cuda.current_device())
-    out = torch.empty(waves * 64, dtype=torch.float32, device=dev)
-    ticks = torch.zeros(2 * waves, dtype=torch.int64, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.stream(st):  # the zeroed tick buffer is ready on the probe's stream
+        out = torch.empty(waves * 64, dtype=torch.float32, device=dev)
+        ticks = torch.zeros(2 * waves, dtype=torch.int64, device=dev)
     _check(lib().fa_probe_issue(int(role), int(valu_ops), int(exps), int(blocks), int(iters), _ptr(out),
-                                _ptr(ticks), _stream_handle(stream, dev)))
+                                _ptr(ticks), _stream_handle(st, dev)))
     torch.cuda.synchronize(dev)
     t = ticks.view(-1, 2).cpu().tolist()
     return [a for a, b in t if a > 0], [b for a, b in t if a > 0], [w for w, (a, b) in enumerate(t) if a > 0]
@@ -509,8 +511,9 @@ def fa_probe_lds(mode, blocks, iters, stream=None):
 
     dev = torch.device("cuda", torch.cuda.current_device())
     st = stream if stream is not None else torch.cuda.current_stream(dev)
-    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
-    ticks = torch.zeros(2 * blocks * 4, dtype=torch.int64, device=dev)
+    with torch.cuda.stream(st):  # the zeroed tick buffer is ready on the probe's stream
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        ticks = torch.zeros(2 * blocks * 4, dtype=torch.int64, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
     _check(lib().fa_probe_lds(int(mode), int(blocks), int(iters), _ptr(out), _ptr(ticks), _stream_handle(st, dev)))
@@ -532,8 +535,9 @@ def fa_probe_tile(copies, valu_ops, blocks, tiles, src=None, stream=None):
             raise FaError(STATUS["FA_ERR_NULL"], f"src is on {src.device}, expected {dev}")
     st = stream if stream is not None else torch.cuda.current_stream(dev)
     nbytes = 0 if src is None else src.numel() * src.element_size()
-    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-    ticks = torch.zeros(2 * blocks * 4, dtype=torch.int64, device=dev)
+    with torch.cuda.stream(st):  # the zeroed tick buffer is ready on the probe's stream
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        ticks = torch.zeros(2 * blocks * 4, dtype=torch.int64, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
     _check(lib().fa_probe_tile(int(copies), int(valu_ops), int(blocks), int(tiles), _ptr(src), nbytes, _ptr(out),
