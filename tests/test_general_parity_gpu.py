@@ -32,6 +32,8 @@ CASES = [  # (dtype, d, dv, N, causal, bias)
     ("bf16", 96, 96, 300, True, False),
     ("bf16", 40, 72, 150, False, True),
     ("bf16", 256, 256, 130, True, False),
+    ("bf16", 128, 128, 700, False, True),    # bias at d = dv = 128: the most registers in use
+    ("bf16", 128, 128, 650, True, True),     # the same, causal, on a split plan
     ("f32", 1, 256, 64, True, False),
     ("f32", 256, 24, 100, False, True),
     ("f16", 17, 33, 97, True, True),
@@ -91,6 +93,8 @@ F16_MFMA = [  # (d, dv, N, causal, bias, B, H): the matrix-core kernel with fp16
     (64, 128, 555, False, True, 2, 3),       # bias with a sparse mask
     (128, 64, 777, True, False, 2, 4),
     (64, 64, 129, True, True, 1, 2),
+    (128, 128, 700, False, True, 1, 2),      # bias at d = dv = 128: the most registers in use
+    (128, 128, 650, True, True, 2, 1),       # the same with a causal mask and a split plan
 ]
 
 
