@@ -17,7 +17,7 @@ without a GPU:
     that emulation exceed its bar somewhere;
   * the forward bar rejects three plausible kernel bugs on the last query tile of the
     single causal head of length 8192 (a value tile read from its neighbour, O scaled
-    by 0.9, a 512-key range dropped), which the north_star bar alone does not see;
+    by 0.9, a 512-key range dropped), which the fixed 2e-2 + 1e-2|O| bar alone does not see;
   * closed forms: one allowed key gives scale |v_j|; uniform weights over n keys with
     values +-1 give 1/sqrt(n).
 
@@ -249,11 +249,11 @@ def test_forward_bar_rejects_planted_bugs_on_headline_tile(headline_last_tile):
     drop[0, 0, :, 1024:1536] = float("-inf")
     o_drop, _ = sdpa_reference_rows(q, k, v, drop, True, 0, 0, rows)
     for name, o_bad in (("value tile swap", o_swap), ("O x 0.9", o_scaled), ("dropped key range", o_drop)):
-        # the benchmark spec bar alone: how many elements it flags (reported, not asserted)
+        # the fixed 2e-2 + 1e-2|O| bar alone: how many elements it flags (reported, not asserted)
         ns_bad = int((np.abs(o_bad - o_ref) > 2e-2 + 1e-2 * np.abs(o_ref)).sum())
         with pytest.raises(AssertionError):
             check_out(o_bad, o_ref, "bf16", name, scale=sc)
-        print(f"{name}: north_star bar flags {ns_bad} of {o_ref.size} elements; error-scale bar rejects")
+        print(f"{name}: fixed bar flags {ns_bad} of {o_ref.size} elements; error-scale bar rejects")
 
 
 # ---------------------------------------------------------------- gradient scales
